@@ -1,0 +1,256 @@
+/*
+ * msa.h -- C ABI of the Memory Sparse Attention (MSA) hot path on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * MSA is described on these pages:
+ *   [neo]   news.neo-ai.one MSA article: 全体設計 › アーキテクチャ (Fig. 2),
+ *           推論パイプライン (Fig. 3)
+ *   [blog]  ruixiangma.github.io "Memory-Sparse-Attention": 方法 ›
+ *           稀疏注意力机制, 文档级RoPE, 三阶段推理流程, Memory Parallel
+ *   [aip]   ai-papers.net MSA summary: MSAの提案手法
+ *   [rev]   github-eval-reports review of MSA: 推理流程, 核心模块
+ *
+ * The calls follow the three-stage pipeline of [neo] 推論パイプライン and
+ * [blog] 三阶段推理流程:
+ *   1. offline global memory encoding  -> msa_encode_pool
+ *   2. online routing + context build  -> msa_route, msa_gather
+ *   3. sparse generation               -> msa_sparse_attn
+ *
+ * Conventions for every call
+ *   - All tensors are row-major and densely packed.  "device" pointers are
+ *     HIP device memory on the context's device; "host" pointers are CPU
+ *     memory.  bf16 tensors hold raw bfloat16 bit patterns (uint16).
+ *   - The caller allocates and owns every buffer and every stream; the
+ *     library allocates only the context's RoPE table.  Workspaces are
+ *     caller-provided device buffers of at least the size the matching
+ *     *_workspace_size() call returns, aligned to 256 bytes.
+ *   - Calls are asynchronous on the given stream unless stated otherwise.
+ *     Arguments are validated synchronously, before anything is enqueued;
+ *     on any error nothing is enqueued.  Launch failures map to
+ *     MSA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  No C++ exception crosses the ABI.
+ *   - msa_last_error() returns a message for the last failing call on the
+ *     calling thread (thread-local; valid until that thread's next call).
+ *   - Inputs are assumed finite (no NaN/Inf); this is not checked.
+ *   - Head dim d is 64 or 128 (fixed per context); Hq % Hkv == 0.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+#define MSA_MAX_TOPK 64
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_INVALID_ARG = 1,  /* a pointer, size or relation is wrong      */
+    MSA_ERR_UNSUPPORTED = 2,  /* valid request this build does not handle  */
+    MSA_ERR_HIP = 3,          /* a HIP runtime call or launch failed       */
+    MSA_ERR_WORKSPACE = 4     /* workspace null, misaligned or too small   */
+} msa_status;
+
+typedef enum msa_dtype {
+    MSA_F32 = 0,              /* IEEE binary32                             */
+    MSA_BF16 = 1              /* bfloat16 bits; fp32 accumulation inside   */
+} msa_dtype;
+
+typedef struct msa_ctx msa_ctx;
+
+/* ABI version compiled into the library (MSA_ABI_VERSION). */
+int msa_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* Static name of a status code. */
+const char* msa_status_string(msa_status s);
+
+/*
+ * msa_ctx_create -- bind the library to `device` and build the RoPE table.
+ *
+ * Rotary embedding in rotate-half form ([neo] アーキテクチャ: parallel /
+ * document-wise RoPE and global RoPE; the pages give no formula, the
+ * backbone's rotate-half form is used): element i pairs with i + d/2,
+ * angle(pos, i) = pos * rope_theta^(-2i/d).  The table cos/sin[max_pos][d/2]
+ * is computed on the host from float64 angles and stored as float32 on the
+ * device (owned by the context, freed by msa_ctx_destroy).  Every position a
+ * later call uses (document-local token index, top_k + local index) must be
+ * < max_pos.  Synchronous.
+ *   device     HIP device ordinal; must be a gfx950 device.
+ *   head_dim   64 or 128.
+ *   rope_theta > 1.
+ *   max_pos    1 .. 1<<22.
+ *   out        receives the context; untouched on error.
+ */
+msa_status msa_ctx_create(int device, int head_dim, double rope_theta, int max_pos,
+                          msa_ctx** out);
+
+/* Frees the context and its table.  Synchronises the device first.  NULL ok. */
+msa_status msa_ctx_destroy(msa_ctx* ctx);
+
+/*
+ * msa_chunk_offsets -- host helper, synchronous.  Chunk-row layout of a
+ * pooled bank ([neo] アーキテクチャ, [blog] 稀疏注意力机制: every document is
+ * split into fixed-length chunks): document d has ceil(len_d / chunk_len)
+ * chunks, stored at rows doc_chunk_off[d] .. doc_chunk_off[d+1]-1.
+ *   doc_tok_off      host int64[n_docs+1], doc_tok_off[0] == 0, strictly
+ *                    increasing (every document has >= 1 token).
+ *   doc_chunk_off    host int64[n_docs+1] output.
+ */
+msa_status msa_chunk_offsets(const int64_t* doc_tok_off, int64_t n_docs, int chunk_len,
+                             int64_t* doc_chunk_off);
+
+/*
+ * msa_encode_pool -- stage 1 (offline): document-wise RoPE + chunk mean.
+ * ([neo] アーキテクチャ and 推論パイプライン first stage; [blog] 稀疏注意力机制,
+ * 文档级RoPE; [aip] MSAの提案手法.)
+ * For document d with tokens [s, e) and its chunk j covering rows
+ * r in [s + j*c, min(s + (j+1)*c, e)):
+ *     K̄  = mean_r RoPE(K[r], r - s)     (positions restart at 0 per document)
+ *     V̄  = mean_r V[r]
+ *     K̄r = mean_r Kr[r]
+ * summed in fp32, divided by the actual row count, rounded once to `dt`.
+ *   K, V, Kr       device [T][Hkv][d] of dt, unrotated.
+ *   doc_tok_off    device int64[n_docs+1] token offsets (as for
+ *                  msa_chunk_offsets).
+ *   doc_chunk_off  device int64[n_docs+1], the msa_chunk_offsets result.
+ *   N              number of chunk rows = doc_chunk_off[n_docs].
+ *   KVbar          device [N][2][Hkv][d] of dt: row n holds K̄ then V̄, so a
+ *                  document's pooled content is one contiguous span.
+ *   Krbar          device [N][Hkv][d] of dt.
+ * Offsets are trusted to be consistent (use msa_chunk_offsets); if they are
+ * not, outputs are unspecified but every access stays inside [0, T) rows
+ * and [0, N) chunk rows.  Document-local positions must be < max_pos.
+ */
+msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt,
+                           const void* K, const void* V, const void* Kr,
+                           const int64_t* doc_tok_off, const int64_t* doc_chunk_off,
+                           int64_t n_docs, int64_t T, int64_t N, int Hkv, int chunk_len,
+                           void* KVbar, void* Krbar, hipStream_t stream);
+
+/*
+ * msa_route -- stage 2a (online): cosine routing + document top-k.
+ * ([neo] アーキテクチャ: cosine similarity, mean over heads, then max over
+ * tokens, top-k documents; [blog] 稀疏注意力机制; [rev] 核心模块.)
+ * B independent queries of Tq tokens each; one pass over Krbar serves all.
+ *     cos(q, k) = q.k / (max(|q|, 1e-8) * max(|k|, 1e-8))
+ *     s[b,t,n]  = (1/Hq) sum_h cos(Qr[b,t,h], Krbar[n, h / (Hq/Hkv)])
+ *     c[b,n]    = max_t s[b,t,n]                       (chunk score)
+ *     D[b,doc]  = max over the document's chunk rows of c[b,n]
+ *     out_ids[b] = the top_k documents by (D descending, id ascending),
+ *                  in that order (ties go to the lowest id).
+ *   Qr             device [B][Tq][Hq][d] of dt.
+ *   Krbar          device [N][Hkv][d] of dt, resident in HBM.
+ *   doc_chunk_off  device int64[n_docs+1], every document >= 1 chunk,
+ *                  doc_chunk_off[n_docs] == N (trusted; accesses clamped).
+ *   top_k          1 .. min(n_docs, MSA_MAX_TOPK).
+ *   out_ids        device int32[B][top_k].
+ *   out_scores     device float[B][top_k] (D of each selected id), or NULL.
+ *   out_chunk      device float[B][N] receives c, or NULL (then c lives in
+ *                  the workspace).
+ *   out_doc        device float[B][n_docs] receives D, or NULL.
+ *   workspace      device, >= msa_route_workspace_size(...) bytes.
+ * bf16 routing with B*Tq >= 8 contracts on the matrix cores with the
+ * head-group sum of the unit query vectors rounded to bf16 (see the
+ * design notes); other cases accumulate in fp32 on the vector units.
+ */
+size_t msa_route_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv,
+                                int64_t N, int64_t n_docs, int top_k);
+
+msa_status msa_route(msa_ctx* ctx, msa_dtype dt,
+                     const void* Qr, int64_t B, int Tq, int Hq,
+                     const void* Krbar, int64_t N, int Hkv,
+                     const int64_t* doc_chunk_off, int64_t n_docs, int top_k,
+                     int32_t* out_ids, float* out_scores,
+                     float* out_chunk, float* out_doc,
+                     void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * msa_gather -- stage 2b (online): fetch the selected documents' pooled
+ * K̄/V̄ rows from the host store.  ([neo] 推論パイプライン: only the selected
+ * K̄/V̄ are loaded, content K̄/V̄ live in host memory and are fetched
+ * asynchronously when selected; [blog] Memory Parallel: CPU-offloaded K̄/V̄
+ * fetched on demand.)
+ * For each query b the selected ids are taken in ascending id order and the
+ * rows doc_chunk_off[id] .. doc_chunk_off[id+1]-1 of host_KVbar are copied,
+ * back to back, to dst_KVmem starting at row mem_off[b]; mem_off[0] = 0 and
+ * mem_off[b+1] = mem_off[b] + (rows of query b).  Adjacent selected
+ * documents are merged into one copy.  Copies are hipMemcpyAsync on `side`;
+ * mem_off_dev (if not NULL) is filled from mem_off_host on `side` as well;
+ * `done` (if not NULL) is recorded on `side` after the last copy, so the
+ * consumer stream can hipStreamWaitEvent on it.
+ *   host_KVbar     host store, pinned (hipHostMalloc), rows of row_bytes
+ *                  (= 2*Hkv*d*sizeof(dt) for a [N][2][Hkv][d] bank).
+ *   n_rows_host    rows in host_KVbar.
+ *   doc_chunk_off  host int64[n_docs+1], non-decreasing from 0, last entry
+ *                  <= n_rows_host.
+ *   ids_host       host int32[B][top_k], ids in [0, n_docs), no duplicate
+ *                  within a query.  Read synchronously.
+ *   dst_KVmem      device buffer of cap_rows rows.
+ *   mem_off_host   host int64[B+1], written synchronously; it is the
+ *                  source of the mem_off_dev copy, so keep it unchanged
+ *                  until `done` has completed (pinned memory makes that
+ *                  copy asynchronous).
+ *   mem_off_dev    device int64[B+1] or NULL.
+ * Fails with MSA_ERR_INVALID_ARG (nothing enqueued) if the rows do not fit
+ * cap_rows or the host store is not pinned.
+ */
+msa_status msa_gather(const void* host_KVbar, size_t row_bytes, int64_t n_rows_host,
+                      const int64_t* doc_chunk_off, int64_t n_docs,
+                      const int32_t* ids_host, int64_t B, int top_k,
+                      void* dst_KVmem, int64_t cap_rows,
+                      int64_t* mem_off_host, int64_t* mem_off_dev,
+                      hipStream_t side, hipEvent_t done);
+
+/*
+ * msa_sparse_attn -- stage 3: GQA attention over [selected K̄/V̄ ; local K/V].
+ * ([neo] アーキテクチャ: the compressed K/V are concatenated with the query's
+ * local K/V for autoregressive decoding; global RoPE shifts the query start
+ * by k so the order is background -> query -> generation; 推論パイプライン
+ * third stage.)
+ * Positions: local key j (0 <= j < L) sits at q_offset + j; query token i
+ * (0 <= i < Tq, the last Tq tokens of the local context) at
+ * q_offset + (L - Tq) + i.  Q and K_local are given unrotated and rotated
+ * inside; memory keys K̄ are used as stored (they carry document-local RoPE
+ * from encoding).  Every memory row is visible to every query token; local
+ * key j is visible to query token i iff j <= (L - Tq) + i.  Query head h
+ * reads KV head h / (Hq/Hkv).
+ *     O[b,i,h] = softmax_j(scale * q~.k~_j) . v_j      (fp32 inside)
+ *   Q              device [B][Tq][Hq][d] of dt.
+ *   KVmem          device [mem_rows_cap][2][Hkv][d] of dt (msa_gather's
+ *                  dst: K̄ then V̄ per row).
+ *   mem_off        device int64[B+1]: query b uses rows
+ *                  mem_off[b] .. mem_off[b+1]-1 (clamped to
+ *                  [0, mem_rows_cap] and to max_rows_per_query rows).
+ *   max_rows_per_query  host upper bound of any query's memory rows (sizes
+ *                  the launch); 0 is allowed (no memory rows).
+ *   K_local, V_local    device [B][L][Hkv][d] of dt; Tq <= L.
+ *   q_offset       the global RoPE shift k (normally top_k).
+ *   scale          logit scale (normally 1/sqrt(d)).
+ *   O              device [B][Tq][Hq][d] of dt.
+ *   workspace      device, >= msa_sparse_attn_workspace_size(...) bytes.
+ * q_offset + L - 1 must be < max_pos.
+ */
+size_t msa_sparse_attn_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv,
+                                      int64_t max_rows_per_query, int L);
+
+msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt,
+                           const void* Q, int64_t B, int Tq, int Hq,
+                           const void* KVmem, const int64_t* mem_off,
+                           int64_t mem_rows_cap, int64_t max_rows_per_query,
+                           const void* K_local, const void* V_local, int L, int Hkv,
+                           int q_offset, float scale, void* O,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

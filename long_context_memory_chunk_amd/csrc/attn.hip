@@ -1,0 +1,272 @@
+// Stage 3: GQA attention over [selected K̄/V̄ ; local K/V] with global RoPE.
+//
+// Source: news.neo-ai.one MSA article, 全体設計 › アーキテクチャ (Fig. 2): the
+// compressed K/V of the selected documents are concatenated with the query's
+// local K/V for autoregressive decoding, and global RoPE shifts the query's
+// start index by k so the order is background -> query -> generation;
+// 推論パイプライン (Fig. 3), third stage (sparse generation).
+//
+// Key space of query (b, i): first the M_b memory rows of query b (visible to
+// every query token, used as stored), then the local keys j = 0 ..
+// (L - Tq) + i (causal), rotated here at position q_offset + j.  The query is
+// rotated at q_offset + (L - Tq) + i.
+//
+// attn_split (vector ALU, any Tq): a workgroup owns one (b, i, kv head g) and
+// the G = Hq/Hkv query heads that read g, so every key row loaded is used G
+// times.  Keys are taken 256 at a time (one per thread for the logits; the
+// (head, dim) outputs are spread over the threads for P.V), with an online
+// softmax across the 256-key splits the workgroup owns.  Splits are dealt to
+// P workgroups; attn_combine merges the P partial (m, l, o) exactly.
+#include "common.hpp"
+#include "launch.hpp"
+#include "attn_mfma.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kSplit = 256;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void attn_split_kernel(
+    const T* __restrict__ Q, int Tq, int Hq, int hkv, const T* __restrict__ KVmem,
+    const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows,
+    const T* __restrict__ Kl, const T* __restrict__ Vl, int L, int q_offset, float scale,
+    const float2* __restrict__ rope_cs, int max_pos, int P,
+    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    constexpr int VEC = Vec16<T>::kN;
+    constexpr int HALF = D / 2;
+    __shared__ float qs[G][D];
+    __shared__ float lg[G][kSplit];
+    __shared__ float s_corr[G];
+    __shared__ float s_m[G];
+    __shared__ float s_l[G];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int p = blockIdx.x;
+    const int g = blockIdx.y;
+    const int64_t bt = blockIdx.z;
+    const int64_t b = bt / Tq;
+    const int i = int(bt % Tq);
+
+    // rotate and scale the G query heads of this group
+    int pos_q = q_offset + (L - Tq) + i;
+    pos_q = pos_q < max_pos ? pos_q : max_pos - 1;
+    for (int idx = tid; idx < G * HALF; idx += 256) {
+        const int hh = idx / HALF, ii = idx % HALF;
+        const int64_t qb = ((bt * Hq) + g * G + hh) * D;
+        const float x1 = Elem<T>::load(Q, qb + ii), x2 = Elem<T>::load(Q, qb + ii + HALF);
+        const float2 cs = rope_cs[int64_t(pos_q) * HALF + ii];
+        qs[hh][ii] = (x1 * cs.x - x2 * cs.y) * scale;
+        qs[hh][ii + HALF] = (x2 * cs.x + x1 * cs.y) * scale;
+    }
+    if (tid < G) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
+
+    int64_t r0 = mem_off[b], r1 = mem_off[b + 1];
+    r0 = r0 < 0 ? 0 : (r0 > cap ? cap : r0);
+    r1 = r1 < r0 ? r0 : (r1 > cap ? cap : r1);
+    if (r1 - r0 > max_rows) r1 = r0 + max_rows;
+    const int64_t M = r1 - r0;
+    const int64_t n_vis = int64_t(L - Tq) + i + 1;
+    const int64_t total = M + n_vis;
+    const int64_t n_splits = (total + kSplit - 1) / kSplit;
+    const int64_t row_elems = int64_t(hkv) * D;
+
+    // output slots of this thread: dim dd, heads h0, h0 + HSTEP, ...
+    constexpr int HSTEP = 256 / D;
+    constexpr int NO = (G + HSTEP - 1) / HSTEP;
+    const int dd = tid % D, h0 = tid / D;
+    float o[NO];
+#pragma unroll
+    for (int k = 0; k < NO; ++k) o[k] = 0.f;
+    __syncthreads();
+
+    for (int64_t sp = p; sp < n_splits; sp += P) {
+        // ---- logits: one key per thread
+        const int64_t kk = sp * kSplit + tid;
+        float acc[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
+        if (kk < total) {
+            if (kk < M) {
+                const T* kr = KVmem + (r0 + kk) * 2 * row_elems + int64_t(g) * D;
+                for (int i0 = 0; i0 < D; i0 += VEC) {
+                    float x[VEC];
+                    Vec16<T>::load(kr + i0, x);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        float a = acc[hh];
+#pragma unroll
+                        for (int u = 0; u < VEC; ++u) a += x[u] * qs[hh][i0 + u];
+                        acc[hh] = a;
+                    }
+                }
+            } else {
+                const int64_t j = kk - M;
+                const T* kr = Kl + ((b * L + j) * hkv + g) * D;
+                int pos = q_offset + int(j);
+                pos = pos < max_pos ? pos : max_pos - 1;
+                const float2* cs = rope_cs + int64_t(pos) * HALF;
+                for (int i0 = 0; i0 < HALF; i0 += VEC) {
+                    float x1[VEC], x2[VEC], y1[VEC], y2[VEC];
+                    Vec16<T>::load(kr + i0, x1);
+                    Vec16<T>::load(kr + i0 + HALF, x2);
+#pragma unroll
+                    for (int u = 0; u < VEC; ++u) {
+                        const float2 c = cs[i0 + u];
+                        y1[u] = x1[u] * c.x - x2[u] * c.y;
+                        y2[u] = x2[u] * c.x + x1[u] * c.y;
+                    }
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        float a = acc[hh];
+#pragma unroll
+                        for (int u = 0; u < VEC; ++u)
+                            a += y1[u] * qs[hh][i0 + u] + y2[u] * qs[hh][i0 + HALF + u];
+                        acc[hh] = a;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) lg[hh][tid] = (kk < total) ? acc[hh] : -INFINITY;
+        __syncthreads();
+
+        // ---- softmax bookkeeping per head (wave w owns heads w, w+4, ...)
+        for (int hh = wave; hh < G; hh += 4) {
+            float mx = -INFINITY;
+            for (int t = lane; t < kSplit; t += kWave) mx = fmaxf(mx, lg[hh][t]);
+            mx = wave_max(mx);
+            const float m_old = s_m[hh];
+            const float m_new = fmaxf(m_old, mx);
+            float sum = 0.f;
+            for (int t = lane; t < kSplit; t += kWave) {
+                const float e = (lg[hh][t] == -INFINITY) ? 0.f : expf(lg[hh][t] - m_new);
+                lg[hh][t] = e;
+                sum += e;
+            }
+            sum = wave_sum(sum);
+            if (lane == 0) {
+                const float corr = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
+                s_corr[hh] = corr;
+                s_l[hh] = s_l[hh] * corr + sum;
+                s_m[hh] = m_new;
+            }
+        }
+        __syncthreads();
+
+        // ---- P.V for this split
+        const int64_t k_end = (sp + 1) * kSplit < total ? (sp + 1) * kSplit : total;
+        const int nk = int(k_end - sp * kSplit);
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+            const int hh = h0 + k * HSTEP;
+            if (hh < G) o[k] *= s_corr[hh];
+        }
+        for (int t = 0; t < nk; ++t) {
+            const int64_t key = sp * kSplit + t;
+            float v;
+            if (key < M) v = Elem<T>::load(KVmem, (r0 + key) * 2 * row_elems + row_elems + int64_t(g) * D + dd);
+            else v = Elem<T>::load(Vl, ((b * L + (key - M)) * hkv + g) * D + dd);
+#pragma unroll
+            for (int k = 0; k < NO; ++k) {
+                const int hh = h0 + k * HSTEP;
+                if (hh < G) o[k] += lg[hh][t] * v;
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- partial results of this workgroup
+#pragma unroll
+    for (int k = 0; k < NO; ++k) {
+        const int hh = h0 + k * HSTEP;
+        if (hh < G) part_o[((bt * Hq + g * G + hh) * P + p) * D + dd] = o[k];
+    }
+    if (tid < G) part_ml[(bt * Hq + g * G + tid) * P + p] = make_float2(s_m[tid], s_l[tid]);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                         const float2* __restrict__ part_ml, int P,
+                                                         T* __restrict__ O) {
+    const int64_t row = blockIdx.x;   // (b, i, h)
+    const int dd = threadIdx.x;
+    float m = -INFINITY;
+    for (int p = 0; p < P; ++p) m = fmaxf(m, part_ml[row * P + p].x);
+    float l = 0.f, acc = 0.f;
+    for (int p = 0; p < P; ++p) {
+        const float2 ml = part_ml[row * P + p];
+        const float w = (ml.x == -INFINITY) ? 0.f : expf(ml.x - m);
+        l += w * ml.y;
+        acc += w * part_o[(row * P + p) * D + dd];
+    }
+    Elem<T>::store(O, row * D + dd, acc / l);
+}
+
+int attn_parts(int64_t B, int Tq, int Hkv, int64_t max_rows, int L, int num_cus) {
+    const int64_t units = B * Tq * Hkv;
+    const int64_t max_splits = ceil_div(max_rows + L, kSplit);
+    int64_t P = ceil_div(int64_t(2) * num_cus, units);
+    if (P > max_splits) P = max_splits;
+    if (P < 1) P = 1;
+    return int(P);
+}
+
+template <typename T, int D, int G>
+hipError_t launch_split_g(const AttnArgs& a, float* part_o, float2* part_ml, int P, hipStream_t st) {
+    hipLaunchKernelGGL((attn_split_kernel<T, D, G>), dim3(unsigned(P), unsigned(a.Hkv), unsigned(a.B * a.Tq)),
+                       dim3(256), 0, st, static_cast<const T*>(a.Q), a.Tq, a.Hq, a.Hkv,
+                       static_cast<const T*>(a.KVmem), a.mem_off, a.mem_rows_cap, a.max_rows,
+                       static_cast<const T*>(a.K_local), static_cast<const T*>(a.V_local), a.L,
+                       a.q_offset, a.scale, a.rope_cs, a.max_pos, P, part_o, part_ml);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(D), 0, st,
+                       part_o, part_ml, P, static_cast<T*>(a.O));
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_split(const AttnArgs& a, float* part_o, float2* part_ml, int P, hipStream_t st) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return launch_split_g<T, D, 1>(a, part_o, part_ml, P, st);
+        case 2: return launch_split_g<T, D, 2>(a, part_o, part_ml, P, st);
+        case 4: return launch_split_g<T, D, 4>(a, part_o, part_ml, P, st);
+        case 8: return launch_split_g<T, D, 8>(a, part_o, part_ml, P, st);
+        case 16: return launch_split_g<T, D, 16>(a, part_o, part_ml, P, st);
+        default: return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+bool attn_supported_group(int Hq, int Hkv) {
+    const int G = Hq / Hkv;
+    return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+}
+
+size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t max_rows,
+                      int L, int num_cus) {
+    const int P = attn_parts(B, Tq, Hkv, max_rows, L, num_cus);
+    const size_t rows = size_t(B) * Tq * Hq * P;
+    size_t split = align256(rows * D * sizeof(float)) + align256(rows * sizeof(float2));
+    size_t mf = attn_mfma_workspace(dt, B, Tq, Hq, Hkv, D, max_rows, L);
+    return split > mf ? split : mf;
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+    if (a.B == 0 || a.Tq == 0) return hipSuccess;
+    if (attn_mfma_applicable(a)) return launch_attn_mfma(a, st);
+    const int P = attn_parts(a.B, a.Tq, a.Hkv, a.max_rows, a.L, a.num_cus);
+    const size_t rows = size_t(a.B) * a.Tq * a.Hq * P;
+    float* part_o = static_cast<float*>(a.ws);
+    float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align256(rows * a.D * sizeof(float)));
+    if (a.dt == MSA_BF16)
+        return a.D == 128 ? launch_split<bf16_t, 128>(a, part_o, part_ml, P, st)
+                          : launch_split<bf16_t, 64>(a, part_o, part_ml, P, st);
+    return a.D == 128 ? launch_split<float, 128>(a, part_o, part_ml, P, st)
+                      : launch_split<float, 64>(a, part_o, part_ml, P, st);
+}
+
+}  // namespace msa

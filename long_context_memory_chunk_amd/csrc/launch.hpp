@@ -1,0 +1,61 @@
+// Internal launchers (not part of the C ABI).  Each returns the HIP error of
+// its launches; argument validation happens in api.hip before these run.
+#pragma once
+
+#include "common.hpp"
+
+namespace msa {
+
+hipError_t launch_encode(const msa_ctx* ctx, msa_dtype dt, const void* K, const void* V,
+                         const void* Kr, const int64_t* tok_off, const int64_t* chunk_off,
+                         int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
+                         void* KVbar, void* Krbar, hipStream_t st);
+
+struct RouteArgs {
+    msa_dtype dt;
+    const void* Qr;
+    int64_t B;
+    int Tq, Hq, Hkv, D;
+    const void* Krbar;
+    int64_t N;
+    const int64_t* chunk_off;
+    int64_t n_docs;
+    int top_k;
+    int32_t* out_ids;
+    float* out_scores;
+    float* out_chunk;
+    float* out_doc;
+    void* ws;
+    size_t ws_bytes;
+    int num_cus;
+};
+
+size_t route_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,
+                       int64_t n_docs, int top_k, int num_cus);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct AttnArgs {
+    msa_dtype dt;
+    const void* Q;
+    int64_t B;
+    int Tq, Hq, Hkv, D, L;
+    const void* KVmem;
+    const int64_t* mem_off;
+    int64_t mem_rows_cap, max_rows;
+    const void* K_local;
+    const void* V_local;
+    int q_offset;
+    float scale;
+    void* O;
+    void* ws;
+    size_t ws_bytes;
+    const float2* rope_cs;
+    int max_pos;
+    int num_cus;
+};
+
+size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
+                      int64_t max_rows, int L, int num_cus);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace msa

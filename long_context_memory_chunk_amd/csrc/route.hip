@@ -1,0 +1,425 @@
+// Stage 2a (online): cosine routing score, per-document max, top-k.
+//
+// Source: news.neo-ai.one MSA article, 全体設計 › アーキテクチャ (Fig. 2):
+// relevance is the cosine similarity of Qr with K̄r, averaged over heads and
+// then maximised over tokens, and the top-k documents are selected;
+// 推論パイプライン (Fig. 3): K̄r is matched online.  ruixiangma.github.io blog,
+// 方法 › 稀疏注意力机制 (top-k documents by cosine).  github-eval-reports
+// review, 核心模块 (head mean first, then token max).
+//
+// Group fold used by every kernel here (exact in real arithmetic):
+//   sum_h cos(q_h, k_{g(h)}) = sum_g (sum_{h in g} q_h/|q_h|) . k_g / |k_g|
+// so route_prep builds U[q][g] = sum_{h in g} q_h / max(|q_h|, eps) once per
+// call, and each (query, chunk) costs Hkv*d multiply-adds plus one norm per
+// chunk head.
+//
+// Kernels
+//   route_prep            U (fp32) from Qr.
+//   route_scan_bf16_d128  decode scan for B*Tq <= 4: streams K̄r with 16-byte
+//                         coalesced loads (a 1 KiB wave load per 4 heads), dot
+//                         and norm partials per lane, DPP reduction over the
+//                         16 lanes of a head, cross-group sum by readlane.
+//                         HBM-bound (1 flop per byte at B*Tq = 1).
+//   route_scan_generic    any dtype/shape: one thread per (query, chunk).
+//   topk_partial          per-wave document max + running top-k in registers.
+//   topk_final            merges the per-wave candidates.
+// The top-k key is 64 bits: order-preserving bits of the fp32 document
+// score above (0xFFFFFFFF - doc id), so a larger key is a better document
+// and equal scores order by lower id, a total order.
+#include "common.hpp"
+#include "launch.hpp"
+#include "route_mfma.hpp"
+
+namespace msa {
+namespace {
+
+constexpr float kEps = 1e-8f;
+
+// ---------------------------------------------------------------- prep
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void route_prep_kernel(const T* __restrict__ Qr, int Hq, int hkv,
+                                                        float* __restrict__ U) {
+    constexpr int PER = D / kWave;
+    const int64_t q = blockIdx.x / hkv;
+    const int g = blockIdx.x % hkv;
+    const int G = Hq / hkv;
+    const int lane = threadIdx.x;
+    float u[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) u[p] = 0.f;
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+        const int64_t base = (q * Hq + h) * D + lane * PER;
+        float x[PER], s = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) { x[p] = Elem<T>::load(Qr, base + p); s += x[p] * x[p]; }
+        s = wave_sum(s);
+        const float inv = 1.f / fmaxf(sqrtf(s), kEps);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) u[p] += x[p] * inv;
+    }
+    const int64_t ob = (q * hkv + g) * D + lane * PER;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) U[ob + p] = u[p];
+}
+
+// ---------------------------------------------------------------- decode scan
+
+// Row n of K̄r is hkv*128 bf16 = LPR KiB; wave load j of a row covers heads
+// 4j .. 4j+3, 16 lanes per head, 8 elements per lane.
+template <int LPR, int NQ>
+__global__ __launch_bounds__(256) void route_scan_bf16_d128(
+    const u32x4* __restrict__ Kr, int64_t N, const float* __restrict__ U, int B, int Tq,
+    float inv_hq, float* __restrict__ cout) {
+    constexpr int UNROLL = 4;
+    const int lane = threadIdx.x % kWave;
+    const int64_t wave_id = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;
+    const int64_t n_waves = int64_t(gridDim.x) * 4;
+    const int sub = lane / 16;          // head within the wave load
+    const int e0 = (lane % 16) * 8;     // first element within the head
+    constexpr int HKV = LPR * 4;
+
+    float u[NQ][LPR][8];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int j = 0; j < LPR; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[q][j][e] = U[(int64_t(q) * HKV + j * 4 + sub) * 128 + e0 + e];
+
+    const int64_t n_groups = (N + 63) / 64;
+    for (int64_t grp = wave_id; grp < n_groups; grp += n_waves) {
+        const int64_t r_base = grp * 64;
+        const int rows = int((N - r_base) < 64 ? (N - r_base) : 64);
+        float mine[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) mine[q] = 0.f;
+        for (int rr = 0; rr < rows; rr += UNROLL) {
+            u32x4 x[UNROLL][LPR];
+#pragma unroll
+            for (int k = 0; k < UNROLL; ++k) {
+                const int r = (rr + k < rows) ? rr + k : rows - 1;   // stay in bounds
+                const u32x4* p = Kr + (r_base + r) * (LPR * 64) + lane;
+#pragma unroll
+                for (int j = 0; j < LPR; ++j) x[k][j] = __builtin_nontemporal_load(p + j * 64);
+            }
+#pragma unroll
+            for (int k = 0; k < UNROLL; ++k) {
+                float acc[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
+#pragma unroll
+                for (int j = 0; j < LPR; ++j) {
+                    float f[8];
+                    f[0] = bf16_lo(x[k][j].x); f[1] = bf16_hi(x[k][j].x);
+                    f[2] = bf16_lo(x[k][j].y); f[3] = bf16_hi(x[k][j].y);
+                    f[4] = bf16_lo(x[k][j].z); f[5] = bf16_hi(x[k][j].z);
+                    f[6] = bf16_lo(x[k][j].w); f[7] = bf16_hi(x[k][j].w);
+                    float n2 = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) n2 += f[e] * f[e];
+                    n2 = group_sum<16>(n2);
+                    // 1 / max(|k|, eps) as one reciprocal square root (1 ulp)
+                    const float rn = __builtin_amdgcn_rsqf(fmaxf(n2, kEps * kEps));
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        float dq = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) dq += u[q][j][e] * f[e];
+                        dq = group_sum<16>(dq);
+                        acc[q] += dq * rn;
+                    }
+                }
+                float sc[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[q]), 0));
+                    t += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[q]), 16));
+                    t += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[q]), 32));
+                    t += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[q]), 48));
+                    sc[q] = t * inv_hq;
+                }
+                if (lane == rr + k) {
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) mine[q] = sc[q];
+                }
+            }
+        }
+        if (lane < rows) {
+            for (int b = 0; b < B; ++b) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if (q / Tq == b) m = fmaxf(m, mine[q]);
+                cout[int64_t(b) * N + r_base + lane] = m;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- generic scan
+
+constexpr int kMaxHkvGeneric = 32;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void route_scan_generic(
+    const T* __restrict__ Kr, int64_t N, int hkv, const float* __restrict__ U, int64_t B, int Tq,
+    float inv_hq, float* __restrict__ cout) {
+    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= B * N) return;
+    const int64_t b = idx / N, n = idx % N;
+    const T* row = Kr + n * hkv * D;
+    float rn[kMaxHkvGeneric];
+    for (int g = 0; g < hkv; ++g) {
+        float s = 0.f;
+        for (int i = 0; i < D; ++i) { const float x = Elem<T>::load(row, g * D + i); s += x * x; }
+        rn[g] = 1.f / fmaxf(sqrtf(s), kEps);
+    }
+    float best = -INFINITY;
+    for (int t = 0; t < Tq; ++t) {
+        const float* uq = U + (b * Tq + t) * hkv * D;
+        float tot = 0.f;
+        for (int g = 0; g < hkv; ++g) {
+            float dq = 0.f;
+            for (int i = 0; i < D; ++i) dq += uq[g * D + i] * Elem<T>::load(row, g * D + i);
+            tot += dq * rn[g];
+        }
+        best = fmaxf(best, tot * inv_hq);
+    }
+    cout[b * N + n] = best;
+}
+
+// ---------------------------------------------------------------- top-k
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
+    s = s + 0.0f;                                   // -0 -> +0
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - id);
+}
+
+__device__ __forceinline__ float key_score(uint64_t k) {
+    const uint32_t o = uint32_t(k >> 32);
+    const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(v)), m));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(v >> 32)), m));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+    const uint32_t lo = uint32_t(__shfl(int(uint32_t(v)), src));
+    const uint32_t hi = uint32_t(__shfl(int(uint32_t(v >> 32)), src));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+// Bitonic sort of one key per lane, descending across lanes 0..63.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int lane) {
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t y = shfl_xor64(x, j);
+            const bool desc_block = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            const uint64_t mx = x > y ? x : y, mn = x > y ? y : x;
+            x = (lower == desc_block) ? mx : mn;
+        }
+    }
+    return x;
+}
+
+// best and x sorted descending across lanes; returns the top 64 of both.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t best, uint64_t x, int lane) {
+    const uint64_t xr = shfl64(x, 63 - lane);
+    uint64_t c = best > xr ? best : xr;             // bitonic
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) {
+        const uint64_t y = shfl_xor64(c, j);
+        const bool lower = (lane & j) == 0;
+        const uint64_t mx = c > y ? c : y, mn = c > y ? y : c;
+        c = lower ? mx : mn;
+    }
+    return c;
+}
+
+__device__ __forceinline__ uint64_t wave_offer(uint64_t best, uint64_t key, int K, int lane) {
+    const uint64_t kth = shfl64(best, K - 1);
+    if (__any(key > kth)) best = wave_merge_desc(best, wave_sort_desc(key, lane), lane);
+    return best;
+}
+
+__global__ __launch_bounds__(256) void topk_partial_kernel(
+    const float* __restrict__ c, int64_t N, const int64_t* __restrict__ off, int64_t n_docs, int K,
+    int64_t docs_per_wave, int waves_per_b, uint64_t* __restrict__ cand, float* __restrict__ out_doc) {
+    const int lane = threadIdx.x % kWave;
+    const int w = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (w >= waves_per_b) return;
+    const int64_t b = blockIdx.y;
+    const int64_t d0 = int64_t(w) * docs_per_wave;
+    const int64_t d1 = (d0 + docs_per_wave < n_docs) ? d0 + docs_per_wave : n_docs;
+    const float* cb = c + b * N;
+    uint64_t best = 0;
+    for (int64_t base = d0; base < d1; base += kWave) {
+        const int64_t d = base + lane;
+        uint64_t key = 0;
+        if (d < d1) {
+            int64_t a = off[d], e = off[d + 1];
+            a = a < 0 ? 0 : (a > N ? N : a);
+            e = e < a ? a : (e > N ? N : e);
+            float m = -INFINITY;
+            for (int64_t n = a; n < e; ++n) m = fmaxf(m, cb[n]);
+            if (out_doc) out_doc[b * n_docs + d] = m;
+            if (e > a) key = make_key(m, uint32_t(d));
+        }
+        best = wave_offer(best, key, K, lane);
+    }
+    if (lane < K) cand[(b * waves_per_b + w) * K + lane] = best;
+}
+
+__global__ __launch_bounds__(64) void topk_final_kernel(const uint64_t* __restrict__ cand,
+                                                        int64_t n_cand, int K,
+                                                        int32_t* __restrict__ ids,
+                                                        float* __restrict__ scores) {
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const uint64_t* cb = cand + b * n_cand;
+    uint64_t best = 0;
+    for (int64_t base = 0; base < n_cand; base += kWave) {
+        const uint64_t key = (base + lane < n_cand) ? cb[base + lane] : 0;
+        best = wave_offer(best, key, K, lane);
+    }
+    if (lane < K) {
+        ids[b * K + lane] = int32_t(0xFFFFFFFFu - uint32_t(best));
+        if (scores) scores[b * K + lane] = key_score(best);
+    }
+}
+
+int topk_waves(int64_t n_docs) {
+    int64_t w = ceil_div(n_docs, 256);
+    if (w < 1) w = 1;
+    if (w > 2048) w = 2048;
+    return int(w);
+}
+
+struct RouteWs {
+    size_t u_off, c_off, cand_off, mfma_off, total;
+};
+
+RouteWs route_ws_layout(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,
+                        int64_t n_docs, int top_k, int num_cus) {
+    RouteWs w;
+    const int64_t nq = B * Tq;
+    size_t o = 0;
+    w.u_off = o;   o += align256(size_t(nq) * Hkv * D * sizeof(float));
+    w.c_off = o;   o += align256(size_t(B) * N * sizeof(float));
+    w.cand_off = o; o += align256(size_t(B) * topk_waves(n_docs) * top_k * sizeof(uint64_t));
+    w.mfma_off = o; o += align256(route_mfma_workspace(dt, B, Tq, Hq, Hkv, D, N, num_cus));
+    w.total = o;
+    return w;
+}
+
+template <typename T, int D>
+hipError_t launch_scan_generic(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
+    const int64_t total = a.B * a.N;
+    hipLaunchKernelGGL((route_scan_generic<T, D>), dim3(unsigned(ceil_div(total, 256))), dim3(256),
+                       0, st, static_cast<const T*>(a.Krbar), a.N, a.Hkv, U, a.B, a.Tq,
+                       1.f / float(a.Hq), c);
+    return hipGetLastError();
+}
+
+template <int LPR, int NQ>
+hipError_t launch_scan_fast(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
+    const int64_t groups = ceil_div(a.N, 64);
+    int64_t blocks = ceil_div(groups, 4);
+    const int64_t cap = int64_t(a.num_cus) * 8;   // 32 waves per CU
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((route_scan_bf16_d128<LPR, NQ>), dim3(unsigned(blocks)), dim3(256), 0, st,
+                       static_cast<const u32x4*>(a.Krbar), a.N, U, int(a.B), a.Tq,
+                       1.f / float(a.Hq), c);
+    return hipGetLastError();
+}
+
+template <int LPR>
+hipError_t dispatch_nq(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
+    switch (a.B * a.Tq) {
+        case 1: return launch_scan_fast<LPR, 1>(a, U, c, st);
+        case 2: return launch_scan_fast<LPR, 2>(a, U, c, st);
+        case 3: return launch_scan_fast<LPR, 3>(a, U, c, st);
+        default: return launch_scan_fast<LPR, 4>(a, U, c, st);
+    }
+}
+
+}  // namespace
+
+size_t route_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,
+                       int64_t n_docs, int top_k, int num_cus) {
+    return route_ws_layout(dt, B, Tq, Hq, Hkv, D, N, n_docs, top_k, num_cus).total;
+}
+
+bool route_generic_supported(int Hkv) { return Hkv <= kMaxHkvGeneric; }
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+    const RouteWs w = route_ws_layout(a.dt, a.B, a.Tq, a.Hq, a.Hkv, a.D, a.N, a.n_docs, a.top_k,
+                                      a.num_cus);
+    char* ws = static_cast<char*>(a.ws);
+    float* U = reinterpret_cast<float*>(ws + w.u_off);
+    float* c = a.out_chunk ? a.out_chunk : reinterpret_cast<float*>(ws + w.c_off);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + w.cand_off);
+    const int64_t nq = a.B * a.Tq;
+    hipError_t err;
+
+    // 1. unit-query group sums
+    if (a.dt == MSA_BF16) {
+        if (a.D == 128)
+            hipLaunchKernelGGL((route_prep_kernel<bf16_t, 128>), dim3(unsigned(nq * a.Hkv)), dim3(64),
+                               0, st, static_cast<const bf16_t*>(a.Qr), a.Hq, a.Hkv, U);
+        else
+            hipLaunchKernelGGL((route_prep_kernel<bf16_t, 64>), dim3(unsigned(nq * a.Hkv)), dim3(64),
+                               0, st, static_cast<const bf16_t*>(a.Qr), a.Hq, a.Hkv, U);
+    } else {
+        if (a.D == 128)
+            hipLaunchKernelGGL((route_prep_kernel<float, 128>), dim3(unsigned(nq * a.Hkv)), dim3(64),
+                               0, st, static_cast<const float*>(a.Qr), a.Hq, a.Hkv, U);
+        else
+            hipLaunchKernelGGL((route_prep_kernel<float, 64>), dim3(unsigned(nq * a.Hkv)), dim3(64),
+                               0, st, static_cast<const float*>(a.Qr), a.Hq, a.Hkv, U);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    // 2. chunk scores c[B][N]
+    if (a.N > 0) {
+        const bool fast = a.dt == MSA_BF16 && a.D == 128 && nq <= 4 &&
+                          (a.Hkv == 4 || a.Hkv == 8 || a.Hkv == 16);
+        const bool mfma = route_mfma_applicable(a.dt, a.B, a.Tq, a.Hkv, a.D);
+        if (fast) {
+            if (a.Hkv == 4) err = dispatch_nq<1>(a, U, c, st);
+            else if (a.Hkv == 8) err = dispatch_nq<2>(a, U, c, st);
+            else err = dispatch_nq<4>(a, U, c, st);
+        } else if (mfma) {
+            err = launch_route_mfma(a, U, c, ws + w.mfma_off, st);
+        } else if (a.dt == MSA_BF16) {
+            err = (a.D == 128) ? launch_scan_generic<bf16_t, 128>(a, U, c, st)
+                               : launch_scan_generic<bf16_t, 64>(a, U, c, st);
+        } else {
+            err = (a.D == 128) ? launch_scan_generic<float, 128>(a, U, c, st)
+                               : launch_scan_generic<float, 64>(a, U, c, st);
+        }
+        if (err != hipSuccess) return err;
+    }
+
+    // 3. document max + top-k
+    const int wpb = topk_waves(a.n_docs);
+    const int64_t dpw = ceil_div(a.n_docs, wpb);
+    hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
+                       0, st, c, a.N, a.chunk_off, a.n_docs, a.top_k, dpw, wpb, cand, a.out_doc);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(64), 0, st, cand,
+                       int64_t(wpb) * a.top_k, a.top_k, a.out_ids, a.out_scores);
+    return hipGetLastError();
+}
+
+}  // namespace msa

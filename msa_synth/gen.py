@@ -35,8 +35,9 @@ def normal_f32(seed, stream, shape):
 
 
 def normal_bf16(seed, stream, shape):
-    """Standard normals rounded to float32, then to bf16 bits (uint16)."""
-    return f32_to_bf16_bits(normal_f32(seed, stream, shape))
+    """Standard normals drawn in float32 (PCG64 keyed by (seed, stream)),
+    rounded to bf16 bits (uint16)."""
+    return f32_to_bf16_bits(_rng(seed, stream).standard_normal(shape, dtype=np.float32))
 
 
 # ---------------------------------------------------------------- counter-based

@@ -25,7 +25,7 @@ takes it.  Parity status of each function is stated in its module docstring.
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, f32_to_f64
 from .rope import inv_freq, rope_angles, rope
-from .encode import chunk_counts, chunk_offsets, encode_pool, encode_pool_loops
+from .encode import chunk_counts, chunk_offsets, chunk_mean, encode_pool, encode_pool_loops
 from .route import (cosine, chunk_scores, chunk_scores_loops, doc_scores,
                     topk_docs, route, EPS)
 from .gather import gather_rows
@@ -34,7 +34,7 @@ from .attention import sparse_attn, sparse_attn_loops
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_to_f64",
     "inv_freq", "rope_angles", "rope",
-    "chunk_counts", "chunk_offsets", "encode_pool", "encode_pool_loops",
+    "chunk_counts", "chunk_offsets", "chunk_mean", "encode_pool", "encode_pool_loops",
     "cosine", "chunk_scores", "chunk_scores_loops", "doc_scores", "topk_docs",
     "route", "EPS",
     "gather_rows",

@@ -47,6 +47,24 @@ def chunk_offsets(doc_tok_off, chunk_len):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
 
 
+def chunk_mean(X, doc_tok_off, chunk_len):
+    """Plain chunk means of X[T, ...] (the V̄ and K̄r part of encode_pool)."""
+    X = np.asarray(X, dtype=np.float64)
+    doc_tok_off = np.asarray(doc_tok_off, dtype=np.int64)
+    lens = np.diff(doc_tok_off)
+    if np.any(lens < 1):
+        raise ValueError("every document needs at least one token")
+    off = chunk_offsets(doc_tok_off, chunk_len)
+    out = np.empty((int(off[-1]),) + X.shape[1:])
+    for doc in range(len(lens)):
+        s, e = int(doc_tok_off[doc]), int(doc_tok_off[doc + 1])
+        starts = np.arange(0, e - s, chunk_len)
+        cnt = np.minimum(starts + chunk_len, e - s) - starts
+        shape = (-1,) + (1,) * (X.ndim - 1)
+        out[off[doc]:off[doc + 1]] = np.add.reduceat(X[s:e], starts, axis=0) / cnt.reshape(shape)
+    return out
+
+
 def encode_pool(K, V, Kr, doc_tok_off, chunk_len, theta):
     """K, V, Kr: float64 [T, Hkv, d].  Returns (Kbar, Vbar, Krbar), each
     float64 [N, Hkv, d] with N = sum_d ceil(len_d / chunk_len)."""

@@ -1,0 +1,368 @@
+"""HIP path vs the oracle, element by element, through the C ABI (GPU only).
+
+Tolerances (stated where used):
+  pooled rows      fp32 1e-5, bf16 2e-2, relative per (chunk, head) row:
+                   |got - ref| <= rtol * (|ref| + rms(ref row))
+  attention output fp32 1e-3, bf16 2e-2, max-abs of the normalised output
+  chunk/doc scores 1e-4 absolute on the fp32-accumulating vector paths
+                   (1024-term fp32 sums of terms bounded by the head-group
+                   size; see the design notes for the derivation)
+  top-k            document id sets bit-exact on planted-margin inputs; on
+                   unplanted inputs every selected id is a valid top-k under
+                   the score tolerance and the order is (score desc, id asc)
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import msa_synth
+import oracle
+from tests import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SCORE_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_mod(gpu):
+    import torch
+    return torch
+
+
+@pytest.fixture(scope="module")
+def msa(gpu):
+    import long_context_memory_chunk_amd as m
+    m.lib()   # raises if the library is missing: no fallback
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx128(msa):
+    c = msa.msa_ctx_create(0, 128, 1e6, 16384)
+    yield c
+    c.close()
+
+
+@pytest.fixture(scope="module")
+def ctx64(msa):
+    c = msa.msa_ctx_create(0, 64, 1e4, 4096)
+    yield c
+    c.close()
+
+
+def _ctx(d, ctx64, ctx128):
+    return ctx128 if d == 128 else ctx64
+
+
+# ---------------------------------------------------------------- generator
+
+def test_device_counter_fill_matches_numpy(torch_mod, msa):
+    from msa_synth import device
+    torch = torch_mod
+    for seed, stream, start, count in [(0, 1, 0, 4096), (7, 3, 12345, 1000), (3, 1001, 2**33 + 8, 77)]:
+        t = torch.empty(count, dtype=torch.bfloat16, device="cuda")
+        device.fill_counter_bf16(t, seed, stream, start)
+        torch.cuda.synchronize()
+        assert np.array_equal(W.host_bits(t), msa_synth.counter_bf16(seed, stream, start, count))
+
+
+# ---------------------------------------------------------------- stage 1
+
+ENCODE_CASES = [
+    # dtype, d, Hkv, chunk, lengths
+    ("f32", 64, 2, 16, [256] * 6),
+    ("f32", 128, 3, 5, [1, 7, 12, 3, 40]),
+    ("bf16", 128, 8, 64, [128, 1024, 64, 65, 300, 999, 1]),
+    ("bf16", 64, 4, 1, [3, 9, 1, 17]),
+    ("bf16", 128, 8, 7, [50, 7, 8, 6, 2000]),
+    ("bf16", 128, 1, 64, [4100]),
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hkv,c,lens", ENCODE_CASES)
+def test_encode_pool_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, c, lens):
+    torch = torch_mod
+    ctx = _ctx(d, ctx64, ctx128)
+    lens = np.array(lens, dtype=np.int64)
+    tok = msa_synth.prefix_offsets(lens)
+    coff = msa.msa_chunk_offsets(tok, c)
+    assert np.array_equal(coff, oracle.chunk_offsets(tok, c))
+    T, N = int(tok[-1]), int(coff[-1])
+    K, V, Kr = (W.draw(21, s, (T, Hkv, d), dtype) for s in (1, 2, 3))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    KVbar = torch.full((N, 2, Hkv, d), float("nan"), dtype=tdt, device="cuda")
+    Krbar = torch.full((N, Hkv, d), float("nan"), dtype=tdt, device="cuda")
+    msa.msa_encode_pool(ctx, W.dev(K, dtype), W.dev(V, dtype), W.dev(Kr, dtype),
+                        torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda(), KVbar, Krbar, c)
+    torch.cuda.synchronize()
+    Kb, Vb, Rb = oracle.encode_pool(W.widen(K, dtype), W.widen(V, dtype), W.widen(Kr, dtype), tok, c,
+                                    ctx.rope_theta)
+    kv = W.widen(W.host_bits(KVbar), dtype)
+    kr = W.widen(W.host_bits(Krbar), dtype)
+    rtol = 2e-2 if dtype == "bf16" else 1e-5
+    assert W.rel_row_err(kv[:, 0], Kb) <= rtol
+    assert W.rel_row_err(kv[:, 1], Vb) <= rtol
+    assert W.rel_row_err(kr, Rb) <= rtol
+    if dtype == "bf16":
+        # tighter self-check: one rounding of an fp32 accumulation is within half a
+        # bf16 ulp (<= 2^-8 relative) plus fp32 summation error
+        for got, ref in ((kv[:, 0], Kb), (kv[:, 1], Vb), (kr, Rb)):
+            assert W.rel_row_err(got, ref) <= 2 ** -8 + 1e-5
+
+
+# ---------------------------------------------------------------- stage 2a
+
+def _bank(dtype, N, Hkv, d, seed):
+    if dtype == "bf16":
+        return msa_synth.counter_bf16(seed, 77, 0, N * Hkv * d).reshape(N, Hkv, d)
+    return msa_synth.normal_f32(seed, 77, (N, Hkv, d))
+
+
+def _run_route(torch, msa, ctx, Qr_h, Kb_h, coff, top_k, dtype, Tq_override=None):
+    B, Tq, Hq, d = Qr_h.shape
+    N, Hkv, _ = Kb_h.shape
+    n_docs = len(coff) - 1
+    ws = msa.workspace(msa.msa_route_workspace_size(1 if dtype == "bf16" else 0, B, Tq, Hq, Hkv, N,
+                                                    n_docs, top_k))
+    ids = torch.empty((B, top_k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, top_k), dtype=torch.float32, device="cuda")
+    ch = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    dc = torch.empty((B, n_docs), dtype=torch.float32, device="cuda")
+    msa.msa_route(ctx, W.dev(Qr_h, dtype), W.dev(Kb_h, dtype), torch.from_numpy(coff).cuda(), top_k,
+                  ids, ws, out_scores=sc, out_chunk=ch, out_doc=dc)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), sc.cpu().numpy(), ch.cpu().numpy(), dc.cpu().numpy()
+
+
+def _check_valid_topk(ids, sc, D_ref, tol):
+    """ids/sc of one query against oracle doc scores: scores match, order is
+    (score desc, id asc) on the returned scores, and no unselected document
+    beats a selected one by more than the tolerance."""
+    k = len(ids)
+    assert len(set(ids.tolist())) == k
+    np.testing.assert_allclose(sc, D_ref[ids], atol=tol, rtol=0)
+    for a in range(k - 1):
+        assert sc[a] > sc[a + 1] or (sc[a] == sc[a + 1] and ids[a] < ids[a + 1])
+    kth = D_ref[ids].min()
+    others = np.delete(D_ref, ids)
+    if others.size:
+        assert others.max() <= kth + 2 * tol
+
+
+ROUTE_CASES = [
+    # dtype, d, Hq, Hkv, B, Tq, n_docs, max chunks per doc, top_k
+    ("bf16", 128, 32, 8, 1, 1, 300, 12, 16),     # decode scan, Qwen shape
+    ("bf16", 128, 32, 8, 2, 2, 200, 9, 8),       # decode scan, 4 queries
+    ("bf16", 128, 16, 4, 3, 1, 150, 5, 5),       # decode scan, 4 KV heads
+    ("bf16", 128, 16, 16, 1, 1, 64, 3, 64),      # decode scan, 16 KV heads, k = 64
+    ("bf16", 128, 32, 8, 1, 3, 100, 4, 7),       # 3 tokens of one query
+    ("f32", 64, 4, 2, 1, 32, 64, 16, 4),         # tiny fp32 shape, generic scan
+    ("bf16", 64, 8, 2, 2, 5, 90, 6, 10),         # generic scan
+    ("bf16", 128, 32, 8, 3, 3, 120, 7, 9),       # 9 queries
+    ("f32", 128, 8, 8, 1, 1, 10, 1, 10),         # k = n_docs
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,n_docs,maxc,k", ROUTE_CASES)
+def test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, n_docs, maxc, k):
+    ctx = _ctx(d, ctx64, ctx128)
+    rng = np.random.default_rng(n_docs + Hq)
+    counts = rng.integers(1, maxc + 1, size=n_docs)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank(dtype, N, Hkv, d, 31)
+    Qr = W.draw(32, 4, (B, Tq, Hq, d), dtype)
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx, Qr, Kb, coff, k, dtype)
+    c_ref = oracle.chunk_scores(W.widen(Qr, dtype), W.widen(Kb, dtype))
+    D_ref = oracle.doc_scores(c_ref, coff)
+    assert np.max(np.abs(ch - c_ref)) <= SCORE_TOL
+    assert np.max(np.abs(dc - D_ref)) <= SCORE_TOL
+    for b in range(B):
+        _check_valid_topk(ids[b], sc[b], D_ref[b], SCORE_TOL)
+
+
+@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16)])
+def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
+    Hq, Hkv, d, n_docs, k = 32, 8, 128, 500, 16
+    counts = np.random.default_rng(3).integers(1, 10, size=n_docs)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank("bf16", N, Hkv, d, 41)
+    Qr = msa_synth.normal_bf16(42, 4, (B, Tq, Hq, d))
+    qf = msa_synth.bf16_bits_to_f32(Qr)
+    planted = []
+    for b in range(B):
+        pl = msa_synth.pick_planted(43 + b, 50, n_docs, k, exclude=[p for q in planted for p in q])
+        planted.append(pl)
+        toks = np.random.default_rng(44 + b).integers(0, Tq, size=k)
+        for j, doc in enumerate(pl):
+            Kb[coff[doc]:coff[doc + 1]] = msa_synth.planted_rows(45 + b, j, qf[b, toks[j]], Hkv,
+                                                                 int(counts[doc]))
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, k, "bf16")
+    ids_ref, sc_ref, c_ref, D_ref = oracle.route(W.widen(Qr, "bf16"), W.widen(Kb, "bf16"), coff, k)
+    for b in range(B):
+        assert sorted(ids[b].tolist()) == sorted(planted[b].tolist())      # recovered
+        assert sorted(ids[b].tolist()) == sorted(ids_ref[b].tolist())      # bit-exact set
+        margin = sc_ref[b].min() - np.delete(D_ref[b], ids_ref[b]).max()
+        assert margin >= 0.05
+    assert np.max(np.abs(ch - c_ref)) <= SCORE_TOL
+
+
+def test_route_ties_go_to_lowest_id(torch_mod, msa, ctx128):
+    Hq, Hkv, d = 32, 8, 128
+    counts = np.array([2, 3, 1, 2, 3, 2, 1, 4])
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank("bf16", N, Hkv, d, 51)
+    # every chunk of docs 1, 4 and 6 is a copy of one row, and the query points at it
+    row = Kb[coff[1]].copy()
+    Qr = np.stack([row[h // (Hq // Hkv)] for h in range(Hq)])[None, None]
+    for doc in (1, 4, 6):
+        Kb[coff[doc]:coff[doc + 1]] = row
+    ids, sc, _, dc = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, 3, "bf16")
+    assert dc[0, 1] == dc[0, 4] == dc[0, 6]
+    assert ids[0].tolist() == [1, 4, 6]
+
+
+def test_route_is_deterministic(torch_mod, msa, ctx128):
+    counts = np.random.default_rng(5).integers(1, 9, size=400)
+    coff = msa_synth.prefix_offsets(counts)
+    Kb = _bank("bf16", int(coff[-1]), 8, 128, 61)
+    Qr = msa_synth.normal_bf16(62, 4, (1, 1, 32, 128))
+    a = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, 16, "bf16")
+    b = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, 16, "bf16")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- stage 2b
+
+def test_gather_matches_oracle_indexing(torch_mod, msa):
+    torch = torch_mod
+    Hkv, d, n_docs = 8, 128, 50
+    counts = np.random.default_rng(7).integers(1, 12, size=n_docs)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    bank = msa_synth.counter_bf16(3, 5, 0, N * 2 * Hkv * d).reshape(N, 2, Hkv, d)
+    host = torch.empty((N, 2, Hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = np.array([[7, 3, 8, 9, 40], [0, 49, 12, 13, 1]], dtype=np.int32)   # adjacent runs merge
+    cap = 200
+    dst = torch.zeros((cap, 2, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    mo_host = torch.zeros(3, dtype=torch.int64, pin_memory=True)
+    mo_dev = torch.zeros(3, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    msa.msa_gather(host, 2 * Hkv * d * 2, N, coff, ids, 5, dst, cap, mo_host, mo_dev, side=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mo = mo_host.numpy()
+    assert np.array_equal(mo_dev.cpu().numpy(), mo)
+    got = W.host_bits(dst)
+    for b in range(2):
+        ref, m = oracle.gather_rows(bank, coff, ids[b])
+        assert mo[b + 1] - mo[b] == m
+        assert np.array_equal(got[mo[b]:mo[b + 1]], ref)
+
+
+def test_gather_rejects_overflow_and_duplicates(torch_mod, msa):
+    torch = torch_mod
+    coff = np.array([0, 4, 8, 12], dtype=np.int64)
+    host = torch.zeros((12, 64), dtype=torch.uint8, pin_memory=True)
+    dst = torch.zeros((12, 64), dtype=torch.uint8, device="cuda")
+    mo = torch.zeros(2, dtype=torch.int64, pin_memory=True)
+    with pytest.raises(msa.MsaError, match="cap_rows"):
+        msa.msa_gather(host, 64, 12, coff, np.array([[0, 2]], np.int32), 2, dst, 7, mo)
+    with pytest.raises(msa.MsaError, match="twice"):
+        msa.msa_gather(host, 64, 12, coff, np.array([[1, 1]], np.int32), 2, dst, 12, mo)
+    with pytest.raises(msa.MsaError, match="outside"):
+        msa.msa_gather(host, 64, 12, coff, np.array([[1, 3]], np.int32), 2, dst, 12, mo)
+
+
+# ---------------------------------------------------------------- stage 3
+
+ATTN_CASES = [
+    # dtype, d, Hq, Hkv, B, Tq, L, rows per query, q_offset
+    ("f32", 64, 4, 2, 1, 32, 32, [64], 4),            # tiny fp32 shape
+    ("bf16", 128, 32, 8, 1, 1, 257, [152], 16),       # decode, Qwen shape
+    ("bf16", 128, 32, 8, 1, 1, 2048, [125], 16),      # decode, 2K local
+    ("bf16", 128, 32, 8, 3, 4, 300, [30, 0, 700], 16),  # ragged memory, one empty
+    ("bf16", 64, 8, 8, 2, 5, 5, [3, 9], 2),           # G = 1, Tq = L
+    ("f32", 128, 16, 1, 1, 7, 19, [260], 33),         # G = 16, several splits
+    ("bf16", 128, 32, 8, 1, 64, 600, [250], 32),      # short prefill
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,L,rows,qoff", ATTN_CASES)
+def test_sparse_attn_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, L, rows, qoff):
+    torch = torch_mod
+    ctx = _ctx(d, ctx64, ctx128)
+    mem_off = msa_synth.prefix_offsets(rows)
+    M = int(mem_off[-1])
+    Q = W.draw(71, 1, (B, Tq, Hq, d), dtype)
+    KV = W.draw(71, 2, (max(M, 1), 2, Hkv, d), dtype)
+    Kl = W.draw(71, 3, (B, L, Hkv, d), dtype)
+    Vl = W.draw(71, 4, (B, L, Hkv, d), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    O = torch.full((B, Tq, Hq, d), float("nan"), dtype=tdt, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1 if dtype == "bf16" else 0, B, Tq, Hq, Hkv,
+                                                          max(rows), L))
+    msa.msa_sparse_attn(ctx, W.dev(Q, dtype), W.dev(KV, dtype), torch.from_numpy(mem_off).cuda(),
+                        max(rows), W.dev(Kl, dtype), W.dev(Vl, dtype), qoff, W.scale_of(d), O, ws)
+    torch.cuda.synchronize()
+    kv = W.widen(KV, dtype)
+    ref = oracle.sparse_attn(W.widen(Q, dtype), kv[:, 0], kv[:, 1], mem_off, W.widen(Kl, dtype),
+                             W.widen(Vl, dtype), qoff, W.scale_of(d), ctx.rope_theta)
+    got = W.widen(W.host_bits(O), dtype)
+    tol = 2e-2 if dtype == "bf16" else 1e-3
+    assert np.max(np.abs(got - ref)) <= tol
+
+
+def test_sparse_attn_is_deterministic(torch_mod, msa, ctx128):
+    torch = torch_mod
+    Q = W.dev_bf16(msa_synth.normal_bf16(81, 1, (1, 1, 32, 128)))
+    KV = W.dev_bf16(msa_synth.normal_bf16(81, 2, (300, 2, 8, 128)))
+    Kl = W.dev_bf16(msa_synth.normal_bf16(81, 3, (1, 1000, 8, 128)))
+    Vl = W.dev_bf16(msa_synth.normal_bf16(81, 4, (1, 1000, 8, 128)))
+    mo = torch.tensor([0, 300], dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, 1, 32, 8, 300, 1000))
+    outs = []
+    for _ in range(2):
+        O = torch.empty((1, 1, 32, 128), dtype=torch.bfloat16, device="cuda")
+        msa.msa_sparse_attn(ctx128, Q, KV, mo, 300, Kl, Vl, 16, W.scale_of(128), O, ws)
+        outs.append(W.host_bits(O))
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------- validation with a context
+
+def test_validation_errors_enqueue_nothing(torch_mod, msa, ctx128):
+    torch = torch_mod
+    Qr = torch.zeros((1, 1, 30, 128), dtype=torch.bfloat16, device="cuda")
+    Kb = torch.zeros((10, 8, 128), dtype=torch.bfloat16, device="cuda")
+    coff = torch.arange(11, dtype=torch.int64, device="cuda")
+    ids = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    ws = msa.workspace(1 << 20)
+    with pytest.raises(msa.MsaError) as e:                       # Hq % Hkv
+        msa.msa_route(ctx128, Qr, Kb, coff, 4, ids, ws)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    Qr = torch.zeros((1, 1, 32, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(msa.MsaError):                            # top_k > n_docs
+        msa.msa_route(ctx128, Qr, Kb, coff, 11, torch.zeros((1, 11), dtype=torch.int32, device="cuda"), ws)
+    with pytest.raises(msa.MsaError) as e:                       # small workspace
+        msa.msa_route(ctx128, Qr, Kb, coff, 4, ids, msa.workspace(256)[:16])
+    assert e.value.status == msa.MSA_ERR_WORKSPACE
+    Q = torch.zeros((1, 1, 24, 128), dtype=torch.bfloat16, device="cuda")
+    Kl = torch.zeros((1, 8, 8, 128), dtype=torch.bfloat16, device="cuda")
+    O = torch.zeros_like(Q)
+    with pytest.raises(msa.MsaError) as e:                       # G = 3 unsupported
+        msa.msa_sparse_attn(ctx128, Q, None, torch.zeros(2, dtype=torch.int64, device="cuda"), 0,
+                            Kl, Kl, 0, 0.1, O, ws)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG or e.value.status == msa.MSA_ERR_UNSUPPORTED
+    Q = torch.zeros((1, 1, 32, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(msa.MsaError, match="max_pos"):           # positions beyond the table
+        msa.msa_sparse_attn(ctx128, Q, None, torch.zeros(2, dtype=torch.int64, device="cuda"), 0,
+                            Kl, Kl, 16380, 0.1, torch.zeros_like(Q), ws)
+    torch.cuda.synchronize()

@@ -104,3 +104,12 @@ def test_rejects_empty_documents():
     K, V, Kr = _inputs(4, 1, 4)
     with pytest.raises(ValueError):
         oracle.encode_pool(K, V, Kr, np.array([0, 2, 2, 4]), 2, 1e4)
+
+
+def test_chunk_mean_equals_pooled_v():
+    lens = [70, 1, 130]
+    off = _docs(lens)
+    K, V, Kr = _inputs(int(off[-1]), 2, 8, seed=8)
+    _, Vb, Rb = oracle.encode_pool(K, V, Kr, off, 64, 1e4)
+    assert np.array_equal(oracle.chunk_mean(V, off, 64), Vb)
+    assert np.array_equal(oracle.chunk_mean(Kr, off, 64), Rb)
