@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Routed-decode benchmark of the MSA hot path on one MI355X.
+
+Workload (the 100M-token memory): documents with log-normal lengths
+(median 400 tokens, log-sd 0.67, clipped to [64, 8192], multiples of 64)
+summing to 100M tokens, pooled with chunk 64 into N = 1,562,500 rows per
+layer; 18 routing layers of K̄r [N][8][128] bf16 (57.6 GB) resident in HBM;
+pooled K̄/V̄ [N][2][8][128] bf16 of the routing layers (115.2 GB) in pinned
+host memory; 16 planted documents (the same in every layer, planted against
+each layer's own query); top-k 16; a 1-token decode query with 2,048 local
+tokens.  One step = for each of the 18 layers: route (scan K̄r, document
+max, top-16) -> ids to the host -> gather the 16 documents' K̄/V̄ rows from
+the host store (hipMemcpyAsync on a side stream) -> sparse GQA attention
+over [gathered rows ; local K/V].  All inputs are synthetic and seeded.
+
+Prints one JSON line.  `value` is K̄r bytes routed per second of whole
+routed-decode step (18 layers x N x 2 KiB per step / step time).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "K̄r routing scan GB/s (% HBM peak) + sparse-decode tokens/s, 100M-token bank"
+HBM_PEAK_GBPS = 8000.0
+Hq, Hkv, D, CHUNK = 32, 8, 128, 64
+ROW_KR = Hkv * D * 2          # bytes of one pooled routing-key row
+ROW_KV = 2 * Hkv * D * 2      # bytes of one pooled K̄/V̄ row
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--tokens", type=int, default=100_000_000)
+    p.add_argument("--layers", type=int, default=18)
+    p.add_argument("--host-layers", type=int, default=None,
+                   help="layers held in the pinned host store (default: the routing layers)")
+    p.add_argument("--local", type=int, default=2048)
+    p.add_argument("--top-k", type=int, default=16)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+class PinnedHost:
+    """Page-locked host memory from hipHostMalloc (exact size; freed at exit)."""
+
+    def __init__(self, nbytes):
+        import ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        p = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), ctypes.c_size_t(nbytes), 0)
+        if rc != 0 or not p.value:
+            self._hip.hipGetLastError()    # do not leave the failure for the next HIP call to report
+            raise RuntimeError(f"hipHostMalloc({nbytes}) failed with HIP error {rc}")
+        self.addr, self.nbytes = p.value, nbytes
+
+    def free(self):
+        if self.addr:
+            self._hip.hipHostFree(self.addr)
+            self.addr = 0
+
+
+def build_workload(args, torch, msa, msa_synth, device_fill, W):
+    seed, L, k = args.seed, args.layers, args.top_k
+    lens = msa_synth.lognormal_lengths(seed, args.tokens)
+    coff = msa_synth.ceil_chunk_offsets(lens, CHUNK)
+    n_docs, N = len(lens), int(coff[-1])
+    log(f"{args.tokens} tokens -> {n_docs} documents, {N} chunk rows per layer")
+    dev = torch.device("cuda:0")
+    Krbar = torch.empty((L, N, Hkv, D), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        device_fill.fill_counter_bf16(Krbar[l], seed, W.krbar_stream(l), 0)
+    planted = msa_synth.pick_planted(seed, 50, n_docs, k)
+    Qr_h = [msa_synth.normal_bf16(seed, 100 + l, (1, 1, Hq, D)) for l in range(L)]
+    for l in range(L):
+        q = msa_synth.bf16_bits_to_f32(Qr_h[l])[0, 0]
+        for j, d in enumerate(planted):
+            rows = W.planted_pooled(seed, l, q, Hkv, int(coff[d + 1] - coff[d]), tag=j)
+            Krbar[l, coff[d]:coff[d + 1]].copy_(W.dev_bf16(rows))
+    torch.cuda.synchronize()
+    log(f"K̄r resident: {Krbar.numel() * 2 / 1e9:.1f} GB")
+    wl = dict(lens=lens, coff=coff, n_docs=n_docs, N=N, Krbar=Krbar, planted=planted, Qr_h=Qr_h, L=L)
+    wl["Qr"] = [W.dev_bf16(q) for q in Qr_h]
+    wl["Q_h"] = [msa_synth.normal_bf16(seed, 200 + l, (1, 1, Hq, D)) for l in range(L)]
+    wl["Kl_h"] = [msa_synth.normal_bf16(seed, 300 + l, (1, args.local, Hkv, D)) for l in range(L)]
+    wl["Vl_h"] = [msa_synth.normal_bf16(seed, 400 + l, (1, args.local, Hkv, D)) for l in range(L)]
+    wl["Q"] = [W.dev_bf16(x) for x in wl["Q_h"]]
+    wl["Kl"] = [W.dev_bf16(x) for x in wl["Kl_h"]]
+    wl["Vl"] = [W.dev_bf16(x) for x in wl["Vl_h"]]
+    return wl
+
+
+def build_host_store(args, torch, device_fill, W, wl):
+    """Pinned host store of pooled K̄/V̄, one page-locked block per layer, as
+    many blocks as the host lets this process lock (one block is given back
+    as headroom for the runtime); routing layer l reads block l % (blocks)."""
+    seed, L, N = args.seed, wl["L"], wl["N"]
+    want = args.host_layers or L
+    t0 = time.time()
+    layer_bytes = N * ROW_KV
+    host = []
+    for l in range(want):
+        try:
+            host.append(PinnedHost(layer_bytes))
+        except RuntimeError as e:
+            log(f"page-locked memory exhausted after {l} layer blocks ({l * layer_bytes / 1e9:.1f} GB): {e}")
+            if len(host) > 1:
+                host.pop().free()
+            break
+        device_fill.fill_counter_bf16((host[l].addr, layer_bytes // 2), seed, W.kvbar_stream(l), 0)
+        torch.cuda.synchronize()
+        log(f"pinned host layer {l}: {layer_bytes / 1e9:.2f} GB allocated and filled "
+            f"({time.time() - t0:.1f} s)")
+    HL = len(host)
+    if HL == 0:
+        raise RuntimeError("could not page-lock one layer of the host store")
+    if HL < L:
+        log(f"host store holds {HL} distinct layer blocks; routing layer l gathers from block l % {HL}")
+    wl.update(host=host, host_layer=[h.addr for h in host], HL=HL)
+
+
+class Runner:
+    """Per-layer buffers and one routed decode step."""
+
+    def __init__(self, args, torch, msa, wl):
+        self.torch, self.msa, self.wl, self.k = torch, msa, wl, args.top_k
+        dev = torch.device("cuda:0")
+        L, N, n_docs, k = wl["L"], wl["N"], wl["n_docs"], args.top_k
+        self.ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+        self.coff_dev = torch.from_numpy(wl["coff"]).to(dev)
+        self.coff_np = np.ascontiguousarray(wl["coff"])
+        counts = np.diff(wl["coff"])
+        self.cap = int(np.sort(counts)[-k:].sum())          # rows of the k largest documents
+        self.ws_route = msa.workspace(msa.msa_route_workspace_size(1, 1, 1, Hq, Hkv, N, n_docs, k))
+        self.ws_attn = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, 1, Hq, Hkv, self.cap,
+                                                                        args.local))
+        self.ids_dev = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
+        self.ids_host = torch.empty((L, 1, k), dtype=torch.int32, pin_memory=True)
+        self.ids_np = [self.ids_host[l].numpy() for l in range(L)]
+        self.KVmem = torch.empty((L, self.cap, 2, Hkv, D), dtype=torch.bfloat16, device=dev)
+        self.mo_host = torch.zeros((L, 2), dtype=torch.int64, pin_memory=True)
+        self.mo_dev = torch.zeros((L, 2), dtype=torch.int64, device=dev)
+        self.O = torch.empty((L, 1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+        self.side = torch.cuda.Stream()
+        self.ev_ids = torch.cuda.Event()
+        self.scale = 1.0 / math.sqrt(D)
+        self.timers = None
+        self.timing = False
+
+    def arm_timers(self, n):
+        ev = lambda: self.torch.cuda.Event(enable_timing=True)
+        self.timers = [(ev(), ev()) for _ in range(n)]
+        self.attn_timers = [(ev(), ev()) for _ in range(n)]
+        for a, b in self.timers + self.attn_timers:      # create the underlying events
+            a.record()
+            b.record()
+        self.t_i = 0
+
+    def step(self):
+        torch, msa, wl, k = self.torch, self.msa, self.wl, self.k
+        main = torch.cuda.current_stream()
+        for l in range(wl["L"]):
+            if self.timing:
+                msa.msa_route_time_next(self.ctx, *self.timers[self.t_i])
+            msa.msa_route(self.ctx, wl["Qr"][l], wl["Krbar"][l], self.coff_dev, k, self.ids_dev[l],
+                          self.ws_route)
+            self.ids_host[l].copy_(self.ids_dev[l], non_blocking=True)
+            self.ev_ids.record(main)
+            self.ev_ids.synchronize()
+            msa.msa_gather(wl["host_layer"][l % wl["HL"]], ROW_KV, wl["N"], self.coff_np, self.ids_np[l], k, self.KVmem[l],
+                           self.cap, self.mo_host[l], self.mo_dev[l], side=self.side)
+            main.wait_stream(self.side)
+            if self.timing:
+                self.attn_timers[self.t_i][0].record(main)
+            msa.msa_sparse_attn(self.ctx, wl["Q"][l], self.KVmem[l], self.mo_dev[l], self.cap, wl["Kl"][l],
+                                wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
+            if self.timing:
+                self.attn_timers[self.t_i][1].record(main)
+                self.t_i += 1
+
+
+def cpu_baseline(args, wl, W, msa_synth):
+    """The oracle, untuned, on a bounded sample of the same workload: layer
+    0's routing over the first S chunk rows (regenerated on the host; only
+    the oracle calls are timed) plus layer 0's full attention; scaled to one
+    18-layer step."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    seed, k = args.seed, args.top_k
+    coff, N = wl["coff"], wl["N"]
+    S = min(args.cpu_sample_chunks, N)
+    n_docs_s = int(np.searchsorted(coff, S, side="right")) - 1      # documents fully inside
+    S = int(coff[n_docs_s])
+    Kb = W.counter_bf16_threads(seed, W.krbar_stream(0), 0, S * Hkv * D).reshape(S, Hkv, D)
+    q0 = msa_synth.bf16_bits_to_f32(wl["Qr_h"][0])[0, 0]
+    for j, d in enumerate(wl["planted"]):
+        if coff[d + 1] <= S:
+            Kb[coff[d]:coff[d + 1]] = W.planted_pooled(seed, 0, q0, Hkv, int(coff[d + 1] - coff[d]), tag=j)
+    Qr64, Kb64 = W.widen(wl["Qr_h"][0], "bf16"), W.widen(Kb, "bf16")
+    t0 = time.perf_counter()
+    _ids, _, _, _ = oracle.route(Qr64, Kb64, coff[: n_docs_s + 1], min(k, n_docs_s))
+    t_route = time.perf_counter() - t0
+    # attention of layer 0 over the planted documents' pooled rows + local context
+    sel = sorted(int(d) for d in wl["planted"])
+    rows = [msa_synth.counter_bf16(seed, W.kvbar_stream(0), int(coff[d]) * 2 * Hkv * D,
+                                   int(coff[d + 1] - coff[d]) * 2 * Hkv * D).reshape(-1, 2, Hkv, D) for d in sel]
+    kv = W.widen(np.concatenate(rows), "bf16")
+    Qa, Kl, Vl = (W.widen(wl[n][0], "bf16") for n in ("Q_h", "Kl_h", "Vl_h"))
+    t0 = time.perf_counter()
+    oracle.sparse_attn(Qa, kv[:, 0], kv[:, 1], [0, len(kv)], Kl, Vl, k, 1 / math.sqrt(D), 1e6)
+    t_attn = time.perf_counter() - t0
+    t_step = wl["L"] * (t_route * N / S + t_attn)
+    gb = wl["L"] * N * ROW_KR / 1e9
+    return {"value": gb / t_step, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 routing over {S} of {N} chunk rows ({n_docs_s} documents) "
+                      f"+ layer 0 attention ({len(kv)} memory rows + {args.local} local), "
+                      f"scaled x{N / S:.2f} (rows) and x{wl['L']} (layers); "
+                      f"{t_route + t_attn:.1f} s measured; {1 / t_step:.4f} tokens/s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the routed-decode path here has no multi-GPU "
+              "(Memory Parallel) implementation, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_memory_chunk_amd as msa
+    import msa_synth
+    from msa_synth import device as device_fill
+    from tests import workloads as W
+
+    msa.lib()
+    wl = build_workload(args, torch, msa, msa_synth, device_fill, W)
+    run = Runner(args, torch, msa, wl)
+    run.arm_timers(args.steps * wl["L"])
+    build_host_store(args, torch, device_fill, W, wl)
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    run.t_i, run.timing = 0, True
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    scan_ms = [a.elapsed_time(b) for a, b in run.timers]
+    attn_ms = [a.elapsed_time(b) for a, b in run.attn_timers]
+    scan_avg_s = float(np.mean(scan_ms)) / 1e3
+
+    # the planted documents are recovered in every layer of the last step
+    got = [sorted(run.ids_np[l][0].tolist()) for l in range(wl["L"])]
+    recovered = all(g == sorted(int(d) for d in wl["planted"]) for g in got)
+
+    N, L = wl["N"], wl["L"]
+    kr_bytes_step = L * N * ROW_KR
+    scan_bytes = N * (ROW_KR + 4)            # K̄r read + one fp32 chunk score written
+    achieved = scan_bytes / scan_avg_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(kr_bytes_step / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "100M-token bank, 18 routing layers, 1-token routed decode "
+                               "(route + top-16 + host gather + sparse attention per layer)",
+                   "tokens": args.tokens, "n_docs": wl["n_docs"], "chunk_rows": N, "chunk": CHUNK,
+                   "layers": L, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "top_k": args.top_k,
+                   "local": args.local, "Krbar_GB": round(kr_bytes_step / 1e9, 2),
+                   "host_store_layers": wl["HL"], "host_store_GB": round(wl["HL"] * N * ROW_KV / 1e9, 1)},
+        "decode_tokens_per_s": round(1.0 / step_s, 3),
+        "docs_routed_per_s": round(wl["n_docs"] * L / step_s, 1),
+        "scan_kernel_ms": round(scan_avg_s * 1e3, 4),
+        "attn_call_ms": round(float(np.mean(attn_ms)), 4),
+        "planted_recovered_all_layers": recovered,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "route_scan_bf16_d128", "bytes_per_launch": scan_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(args, wl, W, msa_synth)
+    print(json.dumps(out), flush=True)
+    torch.cuda.synchronize()
+    for h in wl["host"]:
+        h.free()
+    if not recovered:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,6 +173,16 @@ msa_status msa_route(msa_ctx* ctx, msa_dtype dt,
                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * msa_route_time_next -- profiling aid, synchronous.  The next msa_route call
+ * on this context records `start` on its stream immediately before its
+ * chunk-score kernel and `stop` immediately after it, then forgets both, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  Both must be
+ * events created on the context's device (or both NULL, which clears).  Not
+ * for concurrent use of one context from several threads.
+ */
+msa_status msa_route_time_next(msa_ctx* ctx, hipEvent_t start, hipEvent_t stop);
+
+/*
  * msa_gather -- stage 2b (online): fetch the selected documents' pooled
  * K̄/V̄ rows from the host store.  ([neo] 推論パイプライン: only the selected
  * K̄/V̄ are loaded, content K̄/V̄ live in host memory and are fetched

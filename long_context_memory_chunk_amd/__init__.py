@@ -24,7 +24,7 @@ MSA_MAX_TOPK = 64
 EXPORTS = [
     "msa_abi_version", "msa_last_error", "msa_status_string",
     "msa_ctx_create", "msa_ctx_destroy", "msa_chunk_offsets",
-    "msa_encode_pool", "msa_route_workspace_size", "msa_route",
+    "msa_encode_pool", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
     "msa_gather", "msa_sparse_attn_workspace_size", "msa_sparse_attn",
 ]
 
@@ -53,6 +53,7 @@ _SIGS = {
     "msa_encode_pool": (I32, [P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, P, P]),
     "msa_route_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I64, I32]),
     "msa_route": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, I32, P, P, P, P, P, SZ, P]),
+    "msa_route_time_next": (I32, [P, P, P]),
     "msa_gather": (I32, [P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, P, P]),
     "msa_sparse_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
@@ -194,6 +195,13 @@ def msa_route(ctx, Qr, Krbar, doc_chunk_off, top_k, out_ids, workspace, out_scor
                            _ptr(doc_chunk_off), doc_chunk_off.numel() - 1, top_k, _ptr(out_ids),
                            _ptr(out_scores), _ptr(out_chunk), _ptr(out_doc), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def msa_route_time_next(ctx, start=None, stop=None):
+    """start/stop: torch.cuda.Event(enable_timing=True) already recorded once
+    (so the underlying event exists), or None to clear."""
+    h = lambda e: None if e is None else e.cuda_event
+    _check(lib().msa_route_time_next(ctx.handle, h(start), h(stop)))
 
 
 def msa_gather(host_KVbar, row_bytes, n_rows_host, doc_chunk_off_host, ids_host, top_k,

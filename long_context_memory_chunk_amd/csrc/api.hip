@@ -48,11 +48,15 @@ bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) 
 size_t dtype_bytes(msa_dtype dt) { return dt == MSA_BF16 ? 2 : 4; }
 bool dtype_ok(msa_dtype dt) { return dt == MSA_F32 || dt == MSA_BF16; }
 
-// Makes the context's device current for the duration of a call.
+// Makes the context's device current for the duration of a call.  It also
+// clears a stale, non-sticky error left by an unrelated earlier HIP call (a
+// failed allocation, say), so the launch checks of this call report only
+// errors of this call.
 struct DeviceGuard {
     int prev = -1;
     hipError_t err = hipSuccess;
     explicit DeviceGuard(int dev) {
+        (void)hipGetLastError();
         err = hipGetDevice(&prev);
         if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
     }
@@ -138,6 +142,8 @@ msa_status msa_ctx_create(int device, int head_dim, double rope_theta, int max_p
     c->max_pos = max_pos;
     c->num_cus = prop.multiProcessorCount;
     c->rope_cs = d_table;
+    c->prof_start = nullptr;
+    c->prof_stop = nullptr;
     *out = c;
     return ok();
 }
@@ -241,11 +247,22 @@ msa_status msa_route(msa_ctx* ctx, msa_dtype dt, const void* Qr, int64_t B, int 
         return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
                     ws_bytes);
     msa::RouteArgs a{dt, Qr, B, Tq, Hq, Hkv, ctx->head_dim, Krbar, N, doc_chunk_off, n_docs, top_k,
-                     out_ids, out_scores, out_chunk, out_doc, workspace, ws_bytes, ctx->num_cus};
+                     out_ids, out_scores, out_chunk, out_doc, workspace, ws_bytes, ctx->num_cus,
+                     ctx->prof_start, ctx->prof_stop};
+    ctx->prof_start = ctx->prof_stop = nullptr;
     DeviceGuard dg(ctx->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_route: hipSetDevice");
     hipError_t e = msa::launch_route(a, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_route: launch");
+    return ok();
+}
+
+msa_status msa_route_time_next(msa_ctx* ctx, hipEvent_t start, hipEvent_t stop) {
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "msa_route_time_next: ctx is NULL");
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(MSA_ERR_INVALID_ARG, "msa_route_time_next: give both events or neither");
+    ctx->prof_start = start;
+    ctx->prof_stop = stop;
     return ok();
 }
 

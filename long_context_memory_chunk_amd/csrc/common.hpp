@@ -128,4 +128,6 @@ struct msa_ctx {
     int max_pos;
     int num_cus;
     float2* rope_cs;   // device [max_pos][head_dim/2] (cos, sin)
+    hipEvent_t prof_start;   // msa_route_time_next: consumed by the next msa_route
+    hipEvent_t prof_stop;
 };

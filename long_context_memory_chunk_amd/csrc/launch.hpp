@@ -28,6 +28,7 @@ struct RouteArgs {
     void* ws;
     size_t ws_bytes;
     int num_cus;
+    hipEvent_t prof_start, prof_stop;   // recorded around the chunk-score kernel if set
 };
 
 size_t route_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,

@@ -391,6 +391,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     // 2. chunk scores c[B][N]
+    if (a.prof_start && (err = hipEventRecord(a.prof_start, st)) != hipSuccess) return err;
     if (a.N > 0) {
         const bool fast = a.dt == MSA_BF16 && a.D == 128 && nq <= 4 &&
                           (a.Hkv == 4 || a.Hkv == 8 || a.Hkv == 16);
@@ -410,6 +411,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
         }
         if (err != hipSuccess) return err;
     }
+    if (a.prof_stop && (err = hipEventRecord(a.prof_stop, st)) != hipSuccess) return err;
 
     // 3. document max + top-k
     const int wpb = topk_waves(a.n_docs);

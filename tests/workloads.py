@@ -139,6 +139,21 @@ def qwen_bf16_layer(seed=0, n_docs=2000, lo=128, hi=1024, Tq=256, top_k=16, n_pl
     return w
 
 
+def counter_bf16_threads(seed, stream, start, count, threads=16, block=1 << 23):
+    """msa_synth.counter_bf16 over [start, start+count), evaluated on slices by
+    a thread pool (NumPy releases the GIL inside its ufuncs)."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(count, dtype=np.uint16)
+
+    def job(o):
+        n = min(block, count - o)
+        out[o:o + n] = msa_synth.counter_bf16(seed, stream, start + o, n)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(job, range(0, count, block)))
+    return out
+
+
 def counter_rows(seed, stream, row0, row1, Hkv, d):
     """Rows row0..row1-1 of a counter-filled [T, Hkv, d] bf16 tensor."""
     n = Hkv * d
