@@ -151,7 +151,9 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt,
  *   doc_chunk_off  device int64[n_docs+1], every document >= 1 chunk,
  *                  doc_chunk_off[n_docs] == N (trusted; accesses clamped).
  *   top_k          1 .. min(n_docs, MSA_MAX_TOPK).
- *   out_ids        device int32[B][top_k].
+ *   out_ids        int32[B][top_k], device memory or pinned host memory
+ *                  (hipHostMalloc): a pinned buffer lets the host read the
+ *                  ids right after the stream reaches the end of the call.
  *   out_scores     device float[B][top_k] (D of each selected id), or NULL.
  *   out_chunk      device float[B][N] receives c, or NULL (then c lives in
  *                  the workspace).
@@ -192,8 +194,11 @@ msa_status msa_route_time_next(msa_ctx* ctx, hipEvent_t start, hipEvent_t stop);
  * rows doc_chunk_off[id] .. doc_chunk_off[id+1]-1 of host_KVbar are copied,
  * back to back, to dst_KVmem starting at row mem_off[b]; mem_off[0] = 0 and
  * mem_off[b+1] = mem_off[b] + (rows of query b).  Adjacent selected
- * documents are merged into one copy.  Copies are hipMemcpyAsync on `side`;
- * mem_off_dev (if not NULL) is filled from mem_off_host on `side` as well;
+ * documents are merged into one copy.  Copies are asynchronous host->device
+ * memcpys on `side`: one hipMemcpyAsync per copy, or one hipMemcpyBatchAsync
+ * for all of them when the HIP runtime in the process provides that call
+ * (and the environment does not set MSA_GATHER_BATCH=0); mem_off_dev (if not
+ * NULL) is filled from mem_off_host by the same submission;
  * `done` (if not NULL) is recorded on `side` after the last copy, so the
  * consumer stream can hipStreamWaitEvent on it.
  *   host_KVbar     host store, pinned (hipHostMalloc), rows of row_bytes
@@ -218,6 +223,33 @@ msa_status msa_gather(const void* host_KVbar, size_t row_bytes, int64_t n_rows_h
                       void* dst_KVmem, int64_t cap_rows,
                       int64_t* mem_off_host, int64_t* mem_off_dev,
                       hipStream_t side, hipEvent_t done);
+
+/*
+ * msa_gather_device -- stage 2b without a host round trip.  Same result and
+ * layout as msa_gather (each query's ids in ascending order, rows back to
+ * back, mem_off prefix sums), but the ids stay on the device and a kernel on
+ * `stream` reads the selected rows straight from the pinned host store
+ * (page-locked host memory is addressable by the GPU) and writes them to
+ * dst_KVmem.  ([neo] 推論パイプライン: only the selected K̄/V̄ are loaded from
+ * host memory; [blog] Memory Parallel: CPU-offloaded K̄/V̄ fetched on demand.)
+ *   host_KVbar     pinned host store (hipHostMalloc), 16-byte aligned, rows
+ *                  of row_bytes (a multiple of 16), n_rows_host rows.
+ *   doc_chunk_off  device int64[n_docs+1].
+ *   ids            device int32[B][top_k] (e.g. msa_route's out_ids).
+ *   mem_off        device int64[B+1] output.
+ *   workspace      device, >= msa_gather_device_workspace_size(B, top_k).
+ * B in [1, 1024].  Device-side data are not validated synchronously: an id
+ * outside [0, n_docs), or a document whose rows fall outside the host
+ * store, contributes no rows; rows beyond cap_rows are dropped (mem_off is
+ * clamped to cap_rows).  Every access stays in bounds.
+ */
+size_t msa_gather_device_workspace_size(int64_t B, int top_k);
+
+msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_bytes,
+                             int64_t n_rows_host, const int64_t* doc_chunk_off, int64_t n_docs,
+                             const int32_t* ids, int64_t B, int top_k, void* dst_KVmem,
+                             int64_t cap_rows, int64_t* mem_off,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * msa_sparse_attn -- stage 3: GQA attention over [selected K̄/V̄ ; local K/V].

@@ -25,7 +25,8 @@ EXPORTS = [
     "msa_abi_version", "msa_last_error", "msa_status_string",
     "msa_ctx_create", "msa_ctx_destroy", "msa_chunk_offsets",
     "msa_encode_pool", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
-    "msa_gather", "msa_sparse_attn_workspace_size", "msa_sparse_attn",
+    "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
+    "msa_sparse_attn_workspace_size", "msa_sparse_attn",
 ]
 
 
@@ -55,6 +56,8 @@ _SIGS = {
     "msa_route": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, I32, P, P, P, P, P, SZ, P]),
     "msa_route_time_next": (I32, [P, P, P]),
     "msa_gather": (I32, [P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, P, P]),
+    "msa_gather_device_workspace_size": (SZ, [I64, I32]),
+    "msa_gather_device": (I32, [P, P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, SZ, P]),
     "msa_sparse_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
                               P, SZ, P]),
@@ -216,6 +219,21 @@ def msa_gather(host_KVbar, row_bytes, n_rows_host, doc_chunk_off_host, ids_host,
     _check(lib().msa_gather(_ptr(host_KVbar), row_bytes, n_rows_host, _ptr(off), n_docs,
                             _ptr(ids_host), B, top_k, _ptr(dst_KVmem), cap_rows, _ptr(mem_off_host),
                             _ptr(mem_off_dev), _stream(side), done))
+
+
+def msa_gather_device_workspace_size(B, top_k):
+    return lib().msa_gather_device_workspace_size(B, top_k)
+
+
+def msa_gather_device(ctx, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, ids, dst_KVmem, cap_rows,
+                      mem_off, workspace, stream=None):
+    """host_KVbar: pinned host tensor or address; doc_chunk_off int64 device
+    [n_docs+1]; ids int32 device [B, top_k]; mem_off int64 device [B+1]."""
+    B, top_k = ids.shape
+    _check(lib().msa_gather_device(ctx.handle, _ptr(host_KVbar), row_bytes, n_rows_host, _ptr(doc_chunk_off),
+                                   doc_chunk_off.numel() - 1, _ptr(ids), B, top_k, _ptr(dst_KVmem), cap_rows,
+                                   _ptr(mem_off), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 # ---------------------------------------------------------------- stage 3

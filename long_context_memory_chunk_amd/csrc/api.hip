@@ -2,10 +2,13 @@
 // host-store gather.  Every entry point validates its arguments before it
 // enqueues anything and reports errors through msa_status plus a
 // thread-local message; no exception leaves this file.
+#include <dlfcn.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -22,6 +25,24 @@ bool attn_supported_group(int Hq, int Hkv);
 namespace {
 
 thread_local std::string g_err;
+
+// msa_gather submits its copies with hipMemcpyBatchAsync when the HIP runtime
+// loaded in the process provides it (looked up at run time: an older runtime
+// in the same process, e.g. one bundled with a framework, may lack it) and
+// MSA_GATHER_BATCH=0 is not set; otherwise one hipMemcpyAsync per copy.
+const bool g_gather_batch = [] {
+    const char* v = std::getenv("MSA_GATHER_BATCH");
+    return !(v && v[0] == '0');
+}();
+
+using BatchCopyFn = hipError_t (*)(void**, void**, size_t*, size_t, hipMemcpyAttributes*, size_t*,
+                                   size_t, size_t*, hipStream_t);
+
+BatchCopyFn batch_copy_fn() {
+    static const BatchCopyFn fn =
+        reinterpret_cast<BatchCopyFn>(dlsym(RTLD_DEFAULT, "hipMemcpyBatchAsync"));
+    return fn;
+}
 
 msa_status fail(msa_status s, const char* fmt, ...) {
     char buf[512];
@@ -316,22 +337,84 @@ msa_status msa_gather(const void* host_KVbar, size_t row_bytes, int64_t n_rows_h
         }
         mem_off_host[b + 1] = cur;
     }
+    // one batched submission of every host->device copy (the runs, then
+    // mem_off); a runtime that rejects the batch gets the copies one by one
     const char* src = static_cast<const char*>(host_KVbar);
     char* dst = static_cast<char*>(dst_KVmem);
+    std::vector<void*> dsts, srcs;
+    std::vector<size_t> sizes;
+    dsts.reserve(runs.size() + 1);
+    srcs.reserve(runs.size() + 1);
+    sizes.reserve(runs.size() + 1);
     for (const Run& r : runs) {
-        e = hipMemcpyAsync(dst + size_t(r.dst_row) * row_bytes, src + size_t(r.src_row) * row_bytes,
-                           size_t(r.rows) * row_bytes, hipMemcpyHostToDevice, side);
-        if (e != hipSuccess) return hip_fail(e, "msa_gather: hipMemcpyAsync");
+        dsts.push_back(dst + size_t(r.dst_row) * row_bytes);
+        srcs.push_back(const_cast<char*>(src) + size_t(r.src_row) * row_bytes);
+        sizes.push_back(size_t(r.rows) * row_bytes);
     }
     if (mem_off_dev) {
-        e = hipMemcpyAsync(mem_off_dev, mem_off_host, size_t(B + 1) * sizeof(int64_t),
-                           hipMemcpyHostToDevice, side);
-        if (e != hipSuccess) return hip_fail(e, "msa_gather: hipMemcpyAsync of mem_off");
+        dsts.push_back(mem_off_dev);
+        srcs.push_back(mem_off_host);
+        sizes.push_back(size_t(B + 1) * sizeof(int64_t));
+    }
+    bool batched = false;
+    if (dsts.size() > 1 && g_gather_batch) {
+        if (BatchCopyFn fn = batch_copy_fn()) {
+            size_t fail_idx = 0;
+            e = fn(dsts.data(), srcs.data(), sizes.data(), dsts.size(), nullptr, nullptr, 0, &fail_idx, side);
+            if (e == hipSuccess) batched = true;
+            else (void)hipGetLastError();
+        }
+    }
+    if (!batched) {
+        for (size_t i = 0; i < dsts.size(); ++i) {
+            e = hipMemcpyAsync(dsts[i], srcs[i], sizes[i], hipMemcpyHostToDevice, side);
+            if (e != hipSuccess) return hip_fail(e, "msa_gather: hipMemcpyAsync");
+        }
     }
     if (done) {
         e = hipEventRecord(done, side);
         if (e != hipSuccess) return hip_fail(e, "msa_gather: hipEventRecord");
     }
+    return ok();
+}
+
+size_t msa_gather_device_workspace_size(int64_t B, int top_k) {
+    if (B < 1 || top_k < 1) return 0;
+    return msa::gather_device_workspace(B);
+}
+
+msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_bytes, int64_t n_rows_host,
+                             const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids, int64_t B,
+                             int top_k, void* dst_KVmem, int64_t cap_rows, int64_t* mem_off,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "msa_gather_device";
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+    if (!host_KVbar || !doc_chunk_off || !ids || !dst_KVmem || !mem_off)
+        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (row_bytes == 0 || row_bytes % 16 || n_rows_host < 0 || n_docs < 1 || cap_rows < 0)
+        return fail(MSA_ERR_INVALID_ARG, "%s: bad size (row_bytes must be a multiple of 16)", fn);
+    if (B < 1 || B > msa::kMaxGatherB)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: B must be in [1, %d]", fn, msa::kMaxGatherB);
+    if (top_k < 1 || top_k > MSA_MAX_TOPK || top_k > n_docs)
+        return fail(MSA_ERR_INVALID_ARG, "%s: top_k %d outside [1, min(n_docs, %d)]", fn, top_k, MSA_MAX_TOPK);
+    if (!aligned16(host_KVbar) || !aligned16(dst_KVmem))
+        return fail(MSA_ERR_INVALID_ARG, "%s: host store and destination must be 16-byte aligned", fn);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, host_KVbar);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(MSA_ERR_INVALID_ARG, "%s: host store is not pinned host memory (use hipHostMalloc)", fn);
+    }
+    const size_t need = msa::gather_device_workspace(B);
+    if (!workspace || !aligned256(workspace) || ws_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
+                    ws_bytes);
+    DeviceGuard dg(ctx->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_gather_device: hipSetDevice");
+    e = msa::launch_gather_device(host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, B, top_k,
+                                  dst_KVmem, cap_rows, mem_off, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e, "msa_gather_device: launch");
     return ok();
 }
 

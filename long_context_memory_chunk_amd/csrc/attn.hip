@@ -13,10 +13,13 @@
 //
 // attn_split (vector ALU, any Tq): a workgroup owns one (b, i, kv head g) and
 // the G = Hq/Hkv query heads that read g, so every key row loaded is used G
-// times.  Keys are taken 256 at a time (one per thread for the logits; the
-// (head, dim) outputs are spread over the threads for P.V), with an online
-// softmax across the 256-key splits the workgroup owns.  Splits are dealt to
-// P workgroups; attn_combine merges the P partial (m, l, o) exactly.
+// times.  Keys are taken 256 at a time: one key per thread for the logits,
+// then for P.V each wave walks 64 of the keys, loading each V row as one
+// coalesced wave access (D/64 elements per lane) and accumulating all G
+// heads in registers; an online softmax runs across the 256-key splits the
+// workgroup owns, and the four waves' partial sums meet in LDS at the end.
+// Splits are dealt to P workgroups; attn_combine merges the P partial
+// (m, l, o) exactly.
 #include "common.hpp"
 #include "launch.hpp"
 #include "attn_mfma.hpp"
@@ -25,6 +28,27 @@ namespace msa {
 namespace {
 
 constexpr int kSplit = 256;
+
+// DPL consecutive elements of one row as floats (DPL = D / 64 per lane).
+template <typename T, int DPL> struct LanePart;
+template <> struct LanePart<bf16_t, 2> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float* v) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+        v[0] = bf16_lo(w); v[1] = bf16_hi(w);
+    }
+};
+template <> struct LanePart<bf16_t, 1> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float* v) { v[0] = bf16_to_f32(p->bits); }
+};
+template <> struct LanePart<float, 2> {
+    __device__ __forceinline__ static void load(const float* p, float* v) {
+        const float2 w = *reinterpret_cast<const float2*>(p);
+        v[0] = w.x; v[1] = w.y;
+    }
+};
+template <> struct LanePart<float, 1> {
+    __device__ __forceinline__ static void load(const float* p, float* v) { v[0] = *p; }
+};
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void attn_split_kernel(
@@ -35,11 +59,13 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
     constexpr int VEC = Vec16<T>::kN;
     constexpr int HALF = D / 2;
+    constexpr int DPL = D / kWave;
     __shared__ float qs[G][D];
     __shared__ float lg[G][kSplit];
     __shared__ float s_corr[G];
     __shared__ float s_m[G];
     __shared__ float s_l[G];
+    __shared__ float red[4][G][D];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
@@ -72,13 +98,12 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     const int64_t n_splits = (total + kSplit - 1) / kSplit;
     const int64_t row_elems = int64_t(hkv) * D;
 
-    // output slots of this thread: dim dd, heads h0, h0 + HSTEP, ...
-    constexpr int HSTEP = 256 / D;
-    constexpr int NO = (G + HSTEP - 1) / HSTEP;
-    const int dd = tid % D, h0 = tid / D;
-    float o[NO];
+    // P.V accumulators of this wave: its 64-key share of every split, DPL dims per lane
+    float o[G][DPL];
 #pragma unroll
-    for (int k = 0; k < NO; ++k) o[k] = 0.f;
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[hh][e] = 0.f;
     __syncthreads();
 
     for (int64_t sp = p; sp < n_splits; sp += P) {
@@ -90,6 +115,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         if (kk < total) {
             if (kk < M) {
                 const T* kr = KVmem + (r0 + kk) * 2 * row_elems + int64_t(g) * D;
+#pragma unroll
                 for (int i0 = 0; i0 < D; i0 += VEC) {
                     float x[VEC];
                     Vec16<T>::load(kr + i0, x);
@@ -107,6 +133,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
                 int pos = q_offset + int(j);
                 pos = pos < max_pos ? pos : max_pos - 1;
                 const float2* cs = rope_cs + int64_t(pos) * HALF;
+#pragma unroll
                 for (int i0 = 0; i0 < HALF; i0 += VEC) {
                     float x1[VEC], x2[VEC], y1[VEC], y2[VEC];
                     Vec16<T>::load(kr + i0, x1);
@@ -155,33 +182,43 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         }
         __syncthreads();
 
-        // ---- P.V for this split
-        const int64_t k_end = (sp + 1) * kSplit < total ? (sp + 1) * kSplit : total;
-        const int nk = int(k_end - sp * kSplit);
+        // ---- P.V: wave w takes keys w*64 .. w*64+63 of the split, one V row per step
 #pragma unroll
-        for (int k = 0; k < NO; ++k) {
-            const int hh = h0 + k * HSTEP;
-            if (hh < G) o[k] *= s_corr[hh];
+        for (int hh = 0; hh < G; ++hh) {
+            const float c = s_corr[hh];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[hh][e] *= c;
         }
+        const int64_t k_begin = sp * kSplit + wave * kWave;
+        int nk = int((total - k_begin) < kWave ? (total - k_begin) : kWave);
+        nk = nk < 0 ? 0 : nk;
+#pragma unroll 4
         for (int t = 0; t < nk; ++t) {
-            const int64_t key = sp * kSplit + t;
-            float v;
-            if (key < M) v = Elem<T>::load(KVmem, (r0 + key) * 2 * row_elems + row_elems + int64_t(g) * D + dd);
-            else v = Elem<T>::load(Vl, ((b * L + (key - M)) * hkv + g) * D + dd);
+            const int64_t key = k_begin + t;
+            const T* vr = (key < M) ? KVmem + (r0 + key) * 2 * row_elems + row_elems + int64_t(g) * D
+                                    : Vl + ((b * L + (key - M)) * hkv + g) * D;
+            float v[DPL];
+            LanePart<T, DPL>::load(vr + lane * DPL, v);
 #pragma unroll
-            for (int k = 0; k < NO; ++k) {
-                const int hh = h0 + k * HSTEP;
-                if (hh < G) o[k] += lg[hh][t] * v;
+            for (int hh = 0; hh < G; ++hh) {
+                const float pw = lg[hh][wave * kWave + t];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) o[hh][e] += pw * v[e];
             }
         }
         __syncthreads();
     }
 
-    // ---- partial results of this workgroup
+    // ---- sum the four waves' partial P.V and write this workgroup's partial
 #pragma unroll
-    for (int k = 0; k < NO; ++k) {
-        const int hh = h0 + k * HSTEP;
-        if (hh < G) part_o[((bt * Hq + g * G + hh) * P + p) * D + dd] = o[k];
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) red[wave][hh][lane * DPL + e] = o[hh][e];
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int hh = idx / D, dd = idx % D;
+        const float v = (red[0][hh][dd] + red[1][hh][dd]) + (red[2][hh][dd] + red[3][hh][dd]);
+        part_o[((bt * Hq + g * G + hh) * P + p) * D + dd] = v;
     }
     if (tid < G) part_ml[(bt * Hq + g * G + tid) * P + p] = make_float2(s_m[tid], s_l[tid]);
 }

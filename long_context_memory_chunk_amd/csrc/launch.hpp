@@ -55,6 +55,12 @@ struct AttnArgs {
     int num_cus;
 };
 
+constexpr int kMaxGatherB = 1024;
+size_t gather_device_workspace(int64_t B);
+hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
+                                int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
+                                int64_t cap_rows, int64_t* mem_off, void* ws, hipStream_t st);
+
 size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
                       int64_t max_rows, int L, int num_cus);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

@@ -280,18 +280,31 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(
     if (lane < K) cand[(b * waves_per_b + w) * K + lane] = best;
 }
 
-__global__ __launch_bounds__(64) void topk_final_kernel(const uint64_t* __restrict__ cand,
-                                                        int64_t n_cand, int K,
-                                                        int32_t* __restrict__ ids,
-                                                        float* __restrict__ scores) {
-    const int lane = threadIdx.x;
+// 16 waves each reduce a slice of the candidates to their top K, then wave 0
+// merges the 16 lists held in LDS.
+constexpr int kFinalWaves = 16;
+
+__global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
+    const uint64_t* __restrict__ cand, int64_t n_cand, int K, int32_t* __restrict__ ids,
+    float* __restrict__ scores) {
+    __shared__ uint64_t lists[kFinalWaves][64];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
     const int64_t b = blockIdx.x;
     const uint64_t* cb = cand + b * n_cand;
+    const int64_t per = ((n_cand + kFinalWaves - 1) / kFinalWaves + kWave - 1) / kWave * kWave;
+    const int64_t c0 = wave * per;
+    const int64_t c1 = (c0 + per < n_cand) ? c0 + per : n_cand;
     uint64_t best = 0;
-    for (int64_t base = 0; base < n_cand; base += kWave) {
-        const uint64_t key = (base + lane < n_cand) ? cb[base + lane] : 0;
+    for (int64_t base = c0; base < c1; base += kWave) {
+        const uint64_t key = (base + lane < c1) ? cb[base + lane] : 0;
         best = wave_offer(best, key, K, lane);
     }
+    lists[wave][lane] = (lane < K) ? best : 0;
+    __syncthreads();
+    if (wave != 0) return;
+    best = 0;
+    for (int w = 0; w < kFinalWaves; ++w) best = wave_offer(best, lists[w][lane], K, lane);
     if (lane < K) {
         ids[b * K + lane] = int32_t(0xFFFFFFFFu - uint32_t(best));
         if (scores) scores[b * K + lane] = key_score(best);
@@ -419,7 +432,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
                        0, st, c, a.N, a.chunk_off, a.n_docs, a.top_k, dpw, wpb, cand, a.out_doc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(64), 0, st, cand,
+    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalWaves * 64), 0, st, cand,
                        int64_t(wpb) * a.top_k, a.top_k, a.out_ids, a.out_scores);
     return hipGetLastError();
 }

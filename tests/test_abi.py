@@ -108,3 +108,20 @@ def test_gather_rejects_pageable_host_store():
     rc = L.msa_gather(host.ctypes.data, 64, 4, off.ctypes.data, 2, ids.ctypes.data, 1, 1, 1, 8,
                       mo.ctypes.data, None, None, None)
     assert rc == msa.MSA_ERR_INVALID_ARG and "pinned" in msa.msa_last_error()
+
+
+def test_library_loads_next_to_torchs_hip_runtime():
+    """torch brings its own libamdhip64; libmsa.so must not need a HIP
+    symbol that runtime lacks (optional newer calls are looked up at run time)."""
+    import subprocess
+    import sys
+    code = ("import torch, ctypes; ctypes.CDLL(%r); print('loaded')" % msa.LIB_PATH)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "loaded" in r.stdout, r.stderr[-2000:]
+
+
+def test_gather_device_validates_before_launch():
+    L = msa.lib()
+    assert L.msa_gather_device(None, 1, 64, 4, 1, 2, 1, 1, 1, 1, 8, 1, 1, 256, None) == 1   # ctx NULL
+    assert msa.msa_gather_device_workspace_size(0, 4) == 0
+    assert msa.msa_gather_device_workspace_size(3, 16) >= 3 * 64 * 3 * 8

@@ -366,3 +366,58 @@ def test_validation_errors_enqueue_nothing(torch_mod, msa, ctx128):
         msa.msa_sparse_attn(ctx128, Q, None, torch.zeros(2, dtype=torch.int64, device="cuda"), 0,
                             Kl, Kl, 16380, 0.1, torch.zeros_like(Q), ws)
     torch.cuda.synchronize()
+
+
+def test_gather_device_matches_oracle_and_host_gather(torch_mod, msa, ctx128):
+    torch = torch_mod
+    Hkv, d, n_docs = 8, 128, 60
+    counts = np.random.default_rng(17).integers(1, 12, size=n_docs)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    bank = msa_synth.counter_bf16(4, 6, 0, N * 2 * Hkv * d).reshape(N, 2, Hkv, d)
+    host = torch.empty((N, 2, Hkv, d), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = np.array([[7, 3, 8, 9, 40], [0, 59, 12, 13, 1], [30, 31, 32, 33, 34]], dtype=np.int32)
+    B, k = ids.shape
+    cap = int(sum(np.diff(coff)[ids[b]].sum() for b in range(B)))
+    row_bytes = 2 * Hkv * d * 2
+    coff_dev = torch.from_numpy(coff).cuda()
+    dst = torch.zeros((cap, 2, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    msa.msa_gather_device(ctx128, host, row_bytes, N, coff_dev, torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
+    # the host-side gather of the same ids gives the same bytes and offsets
+    dst2 = torch.zeros_like(dst)
+    mo_h = torch.zeros(B + 1, dtype=torch.int64, pin_memory=True)
+    side = torch.cuda.Stream()
+    msa.msa_gather(host, row_bytes, N, coff, ids, k, dst2, cap, mo_h, side=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mo_np = mo.cpu().numpy()
+    assert np.array_equal(mo_np, mo_h.numpy())
+    got = W.host_bits(dst)
+    assert np.array_equal(got, W.host_bits(dst2))
+    for b in range(B):
+        ref, m = oracle.gather_rows(bank, coff, ids[b])
+        assert mo_np[b + 1] - mo_np[b] == m
+        assert np.array_equal(got[mo_np[b]:mo_np[b + 1]], ref)
+
+
+def test_gather_device_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, ctx128):
+    torch = torch_mod
+    coff = np.array([0, 3, 5, 9, 10], dtype=np.int64)
+    bank = msa_synth.counter_bf16(5, 7, 0, 10 * 64).reshape(10, 64)
+    host = torch.empty((10, 64), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = torch.tensor([[2, -5, 0], [99, 3, 1]], dtype=torch.int32, device="cuda")
+    cap = 8
+    dst = torch.zeros((cap, 64), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(2, 3))
+    msa.msa_gather_device(ctx128, host, 128, 10, torch.from_numpy(coff).cuda(), ids, dst, cap, mo, ws)
+    torch.cuda.synchronize()
+    # query 0: docs 0 (3 rows) and 2 (4 rows) -> 7 rows; query 1: docs 1, 3 -> clamped to 1 row
+    assert mo.cpu().tolist() == [0, 7, 8]
+    got = W.host_bits(dst)
+    assert np.array_equal(got[:3], bank[0:3]) and np.array_equal(got[3:7], bank[5:9])
+    assert np.array_equal(got[7:8], bank[3:4])
