@@ -21,8 +21,9 @@
 //                         16 lanes of a head, cross-group sum by readlane.
 //                         HBM-bound (1 flop per byte at B*Tq = 1).
 //   route_scan_generic    any dtype/shape: one thread per (query, chunk).
-//   topk_partial          per-wave document max + running top-k in registers.
-//   topk_final            merges the per-wave candidates.
+//   topk_partial          per-wave document max (LDS segmented max over
+//                         coalesced chunk-score loads) + running top-k.
+//   topk_final            merges the per-wave candidates (16 waves, then one).
 // The top-k key is 64 bits: order-preserving bits of the fp32 document
 // score above (0xFFFFFFFF - doc id), so a larger key is a better document
 // and equal scores order by lower id, a total order.
@@ -246,38 +247,100 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t best, uint64_t x, i
     return c;
 }
 
+// Offers one key per lane to the running top-K list `best` (sorted
+// descending across lanes, distinct keys, zeros as padding).  A few winners
+// are inserted one at a time (one ballot and two shuffles each); many are
+// sorted and merged.
 __device__ __forceinline__ uint64_t wave_offer(uint64_t best, uint64_t key, int K, int lane) {
     const uint64_t kth = shfl64(best, K - 1);
-    if (__any(key > kth)) best = wave_merge_desc(best, wave_sort_desc(key, lane), lane);
+    uint64_t mask = __ballot(key > kth);
+    if (mask == 0) return best;
+    if (__popcll(mask) > 8) return wave_merge_desc(best, wave_sort_desc(key, lane), lane);
+    while (mask) {
+        const int src = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        const uint64_t x = shfl64(key, src);
+        if (x <= shfl64(best, K - 1)) continue;          // beaten by an earlier insertion
+        const int pos = __popcll(__ballot(best > x));
+        const uint64_t prev = shfl64(best, lane > 0 ? lane - 1 : 0);
+        best = (lane < pos) ? best : (lane == pos ? x : prev);
+    }
     return best;
 }
 
+__device__ __forceinline__ uint32_t order32(float s) {
+    s = s + 0.0f;                                   // -0 -> +0
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unorder32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Wave w of query b owns documents [256 w, 256 w + 256).  It stages their
+// chunk offsets in LDS, streams the chunk scores of their span with
+// coalesced loads, finds each chunk's document by binary search in LDS and
+// takes an LDS atomic max on the order-preserving bits (max is exact and
+// order-independent, so the result is deterministic), then offers the
+// document scores to its running top-K.
+constexpr int kDocsPerWave = 256;
+
 __global__ __launch_bounds__(256) void topk_partial_kernel(
     const float* __restrict__ c, int64_t N, const int64_t* __restrict__ off, int64_t n_docs, int K,
-    int64_t docs_per_wave, int waves_per_b, uint64_t* __restrict__ cand, float* __restrict__ out_doc) {
-    const int lane = threadIdx.x % kWave;
-    const int w = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (w >= waves_per_b) return;
+    int waves_per_b, uint64_t* __restrict__ cand, float* __restrict__ out_doc) {
+    __shared__ int64_t s_off[4][kDocsPerWave + 1];
+    __shared__ uint32_t s_max[4][kDocsPerWave];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    const int w = blockIdx.x * 4 + wv;
+    const bool active = w < waves_per_b;
     const int64_t b = blockIdx.y;
-    const int64_t d0 = int64_t(w) * docs_per_wave;
-    const int64_t d1 = (d0 + docs_per_wave < n_docs) ? d0 + docs_per_wave : n_docs;
-    const float* cb = c + b * N;
+    const int64_t d0 = int64_t(w) * kDocsPerWave;
+    int nd = 0;
+    if (active) {
+        const int64_t rem = n_docs - d0;
+        nd = int(rem < kDocsPerWave ? rem : kDocsPerWave);
+    }
+    for (int j = lane; j <= kDocsPerWave; j += kWave) {
+        int64_t o = 0;
+        if (j <= nd) {
+            o = off[d0 + j];
+            o = o < 0 ? 0 : (o > N ? N : o);
+        }
+        s_off[wv][j] = o;
+    }
+    for (int j = lane; j < kDocsPerWave; j += kWave) s_max[wv][j] = 0u;
+    __syncthreads();
+    if (nd > 0) {
+        int64_t lo_bound = s_off[wv][0];
+        const int64_t c1 = s_off[wv][nd];
+        const float* cb = c + b * N;
+        for (int64_t n0 = lo_bound; n0 < c1; n0 += kWave) {
+            const int64_t n = n0 + lane;
+            if (n < c1) {
+                const float v = cb[n];
+                int lo = 0, hi = nd;                 // largest j with s_off[j] <= n
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_off[wv][mid] <= n) lo = mid; else hi = mid;
+                }
+                atomicMax(&s_max[wv][lo], order32(v));
+            }
+        }
+    }
+    __syncthreads();
     uint64_t best = 0;
-    for (int64_t base = d0; base < d1; base += kWave) {
-        const int64_t d = base + lane;
+    for (int base = 0; base < nd; base += kWave) {
+        const int j = base + lane;
         uint64_t key = 0;
-        if (d < d1) {
-            int64_t a = off[d], e = off[d + 1];
-            a = a < 0 ? 0 : (a > N ? N : a);
-            e = e < a ? a : (e > N ? N : e);
-            float m = -INFINITY;
-            for (int64_t n = a; n < e; ++n) m = fmaxf(m, cb[n]);
-            if (out_doc) out_doc[b * n_docs + d] = m;
-            if (e > a) key = make_key(m, uint32_t(d));
+        if (j < nd && s_off[wv][j + 1] > s_off[wv][j]) {
+            const float m = unorder32(s_max[wv][j]);
+            if (out_doc) out_doc[b * n_docs + d0 + j] = m;
+            key = make_key(m, uint32_t(d0 + j));
         }
         best = wave_offer(best, key, K, lane);
     }
-    if (lane < K) cand[(b * waves_per_b + w) * K + lane] = best;
+    if (active && lane < K) cand[(b * waves_per_b + w) * K + lane] = best;
 }
 
 // 16 waves each reduce a slice of the candidates to their top K, then wave 0
@@ -304,7 +367,12 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
     __syncthreads();
     if (wave != 0) return;
     best = 0;
-    for (int w = 0; w < kFinalWaves; ++w) best = wave_offer(best, lists[w][lane], K, lane);
+    const int per_batch = kWave / K;                  // lists packed into one 64-key offer
+    for (int w0 = 0; w0 < kFinalWaves; w0 += per_batch) {
+        const int w = w0 + lane / K, e = lane % K;
+        const uint64_t key = (lane < per_batch * K && w < kFinalWaves) ? lists[w][e] : 0;
+        best = wave_offer(best, key, K, lane);
+    }
     if (lane < K) {
         ids[b * K + lane] = int32_t(0xFFFFFFFFu - uint32_t(best));
         if (scores) scores[b * K + lane] = key_score(best);
@@ -312,10 +380,8 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
 }
 
 int topk_waves(int64_t n_docs) {
-    int64_t w = ceil_div(n_docs, 256);
-    if (w < 1) w = 1;
-    if (w > 2048) w = 2048;
-    return int(w);
+    const int64_t w = ceil_div(n_docs, kDocsPerWave);
+    return int(w < 1 ? 1 : w);
 }
 
 struct RouteWs {
@@ -428,9 +494,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 
     // 3. document max + top-k
     const int wpb = topk_waves(a.n_docs);
-    const int64_t dpw = ceil_div(a.n_docs, wpb);
     hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
-                       0, st, c, a.N, a.chunk_off, a.n_docs, a.top_k, dpw, wpb, cand, a.out_doc);
+                       0, st, c, a.N, a.chunk_off, a.n_docs, a.top_k, wpb, cand, a.out_doc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalWaves * 64), 0, st, cand,
                        int64_t(wpb) * a.top_k, a.top_k, a.out_ids, a.out_scores);
