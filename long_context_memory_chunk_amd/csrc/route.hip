@@ -72,7 +72,8 @@ template <int LPR, int NQ>
 __global__ __launch_bounds__(256) void route_scan_bf16_d128(
     const u32x4* __restrict__ Kr, int64_t N, const float* __restrict__ U, int B, int Tq,
     float inv_hq, float* __restrict__ cout) {
-    constexpr int UNROLL = 4;
+    // rows in flight per wave: 8 (16 KiB) when registers allow, else 4
+    constexpr int UNROLL = (LPR * NQ <= 2) ? 8 : 4;
     const int lane = threadIdx.x % kWave;
     const int64_t wave_id = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;
     const int64_t n_waves = int64_t(gridDim.x) * 4;
@@ -414,7 +415,7 @@ template <int LPR, int NQ>
 hipError_t launch_scan_fast(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
     const int64_t groups = ceil_div(a.N, 64);
     int64_t blocks = ceil_div(groups, 4);
-    const int64_t cap = int64_t(a.num_cus) * 8;   // 32 waves per CU
+    const int64_t cap = int64_t(a.num_cus) * 4;   // 16 waves per CU, grid-strided over 64-row groups
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL((route_scan_bf16_d128<LPR, NQ>), dim3(unsigned(blocks)), dim3(256), 0, st,
                        static_cast<const u32x4*>(a.Krbar), a.N, U, int(a.B), a.Tq,

@@ -1,12 +1,232 @@
-// Matrix-core routing path: not enabled yet; every shape takes the vector path.
+// Stage 2a on the matrix cores: routing scores as a dense contraction, for
+// batched decode (B*Tq > 4, Tq = 1) and multi-token query prefill (Tq a
+// multiple of 128).
+//
+// Source: news.neo-ai.one MSA article, 全体設計 › アーキテクチャ (Fig. 2):
+// cosine similarity of Qr with K̄r, averaged over heads, maximised over
+// tokens.  With U[q][g] = sum_{h in g} q_h / max(|q_h|, eps) (route_prep), the
+// score of query token q and chunk n is
+//     s[q][n] = (1/Hq) sum_g rn[n][g] * (U[q][g] . K̄r[n][g]),
+//     rn[n][g] = 1 / max(|K̄r[n][g]|, eps),
+// i.e. a [Q x (Hkv*128)] x [(Hkv*128) x N] product whose 128-wide slices are
+// scaled per (chunk, head group) before they are summed.
+//
+// route_mfma_kernel<BM, BN>: a workgroup (4 waves) owns a BM x BN tile of
+// (query tokens) x (chunks).  For each head group g it stages the bf16 U and
+// K̄r slices (128 wide) in LDS with 16-byte loads, computes the chunks' rn from
+// the same loads (16-lane DPP sums of squares), runs 8 k-steps of
+// v_mfma_f32_32x32x16_bf16 into a per-group accumulator, and adds rn times
+// that accumulator to the running total.  K̄r enters the MFMA exactly; U is
+// rounded once to bf16 (relative error 2^-9 per element; see the design
+// notes for the score tolerance this implies).
+// Epilogue: Tq = 1 -> each row is its own query, scores are written; Tq a
+// multiple of BM -> the tile's column maxima over its BM tokens are written
+// to a partial array and route_mfma_tokmax takes the max over a query's tiles.
 #include "route_mfma.hpp"
 
 namespace msa {
+namespace {
 
-bool route_mfma_applicable(msa_dtype, int64_t, int, int, int) { return false; }
-size_t route_mfma_workspace(msa_dtype, int64_t, int, int, int, int, int64_t, int) { return 0; }
-hipError_t launch_route_mfma(const RouteArgs&, const float*, float*, void*, hipStream_t) {
-    return hipErrorNotSupported;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kStride = 128 + 8;   // LDS row stride in bf16 (16-byte pad: 4-bank skew per row)
+constexpr float kEps = 1e-8f;
+
+__global__ __launch_bounds__(256) void u_to_bf16_kernel(const float* __restrict__ U, int64_t n_real,
+                                                        int64_t n_pad, uint16_t* __restrict__ Ub) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n_pad) return;
+    Ub[i] = (i < n_real) ? f32_to_bf16(U[i]) : uint16_t(0);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void route_mfma_kernel(
+    const uint16_t* __restrict__ Ub, int64_t Q, const uint16_t* __restrict__ Kr, int64_t N, int hkv,
+    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial) {
+    constexpr int WM = (BM >= 64) ? 2 : 1;        // waves along queries
+    constexpr int WN = 4 / WM;                    // waves along chunks
+    constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
+    constexpr int MI = TM / 32, NI = TN / 32;     // 32x32 MFMA tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t sU[BM * kStride];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * kStride];
+    __shared__ float sRn[BN];
+    __shared__ float sMax[WM][BN];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t n0 = int64_t(blockIdx.x) * BN;
+    const int64_t q0 = int64_t(blockIdx.y) * BM;
+    const int64_t row_elems = int64_t(hkv) * 128;
+
+    f32x16 tot[MI][NI], acc[MI][NI];
+#pragma unroll
+    for (int a = 0; a < MI; ++a)
+#pragma unroll
+        for (int b = 0; b < NI; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { tot[a][b][i] = 0.f; acc[a][b][i] = 0.f; }
+
+    for (int g = 0; g < hkv; ++g) {
+        // ---- stage U and K̄r slices of head group g; norms of the K̄r slices
+        for (int r = tid / 16; r < BM; r += 16) {
+            const int c = tid % 16;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(Ub + (q0 + r) * row_elems + g * 128 + c * 8);
+            *reinterpret_cast<u32x4*>(sU + r * kStride + c * 8) = v;
+        }
+        for (int r = tid / 16; r < BN; r += 16) {
+            const int c = tid % 16;
+            int64_t n = n0 + r;
+            n = n < N ? n : N - 1;                       // tail rows: computed, never stored
+            const u32x4 v = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(Kr + n * row_elems + g * 128 + c * 8));
+            *reinterpret_cast<u32x4*>(sK + r * kStride + c * 8) = v;
+            float s = 0.f, f;
+            f = bf16_lo(v.x); s += f * f; f = bf16_hi(v.x); s += f * f;
+            f = bf16_lo(v.y); s += f * f; f = bf16_hi(v.y); s += f * f;
+            f = bf16_lo(v.z); s += f * f; f = bf16_hi(v.z); s += f * f;
+            f = bf16_lo(v.w); s += f * f; f = bf16_hi(v.w); s += f * f;
+            s = group_sum<16>(s);
+            if (c == 0) sRn[r] = __builtin_amdgcn_rsqf(fmaxf(s, kEps * kEps));
+        }
+        __syncthreads();
+
+        // ---- 128-deep contraction of this group on the matrix cores
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int col = ks * 16 + (lane / 32) * 8;
+            bf16x8 af[MI], bfr[NI];
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+                af[a] = *reinterpret_cast<const bf16x8*>(sU + (wm * TM + a * 32 + lane % 32) * kStride + col);
+#pragma unroll
+            for (int b = 0; b < NI; ++b)
+                bfr[b] = *reinterpret_cast<const bf16x8*>(sK + (wn * TN + b * 32 + lane % 32) * kStride + col);
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int b = 0; b < NI; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+        }
+        // ---- scale by 1/|K̄r[n][g]| (one chunk column per lane) and accumulate
+#pragma unroll
+        for (int b = 0; b < NI; ++b) {
+            const float rn = sRn[wn * TN + b * 32 + lane % 32];
+#pragma unroll
+            for (int a = 0; a < MI; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    tot[a][b][i] += rn * acc[a][b][i];
+                    acc[a][b][i] = 0.f;
+                }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue
+    if (Tq == 1) {
+#pragma unroll
+        for (int a = 0; a < MI; ++a)
+#pragma unroll
+            for (int b = 0; b < NI; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t q = q0 + wm * TM + a * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+                    const int64_t n = n0 + wn * TN + b * 32 + lane % 32;
+                    if (q < Q && n < N) cout[q * N + n] = tot[a][b][i] * inv_hq;
+                }
+        return;
+    }
+#pragma unroll
+    for (int b = 0; b < NI; ++b) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < MI; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, tot[a][b][i]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 32) sMax[wm][wn * TN + b * 32 + lane] = m;
+    }
+    __syncthreads();
+    for (int t = tid; t < BN; t += 256) {
+        float m = sMax[0][t];
+#pragma unroll
+        for (int w = 1; w < WM; ++w) m = fmaxf(m, sMax[w][t]);
+        const int64_t n = n0 + t;
+        if (n < N) partial[int64_t(blockIdx.y) * N + n] = m * inv_hq;
+    }
+}
+
+// c[b][n] = max over the query's tiles of partial[tile][n]
+__global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict__ partial, int64_t N,
+                                                         int tiles_per_query, int64_t B, float* __restrict__ cout) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= B * N) return;
+    const int64_t b = i / N, n = i % N;
+    float m = -INFINITY;
+    for (int t = 0; t < tiles_per_query; ++t) m = fmaxf(m, partial[(b * tiles_per_query + t) * N + n]);
+    cout[i] = m;
+}
+
+struct Plan {
+    int bm, bn;
+    int64_t q_pad, q_tiles;
+    size_t ub_bytes, partial_bytes;
+};
+
+Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
+    Plan p;
+    const int64_t Q = B * Tq;
+    p.bm = (Tq == 1 && Q <= 32) ? 32 : 128;
+    p.bn = 128;
+    p.q_pad = ceil_div(Q, p.bm) * p.bm;
+    p.q_tiles = p.q_pad / p.bm;
+    p.ub_bytes = align256(size_t(p.q_pad) * Hkv * 128 * 2);
+    p.partial_bytes = (Tq == 1) ? 0 : align256(size_t(p.q_tiles) * N * 4);
+    return p;
+}
+
+}  // namespace
+
+bool route_mfma_applicable(msa_dtype dt, int64_t B, int Tq, int Hkv, int D) {
+    if (dt != MSA_BF16 || D != 128 || Hkv < 1) return false;
+    if (B * Tq <= 4) return false;                 // the streaming scan handles decode
+    return Tq == 1 || Tq % 128 == 0;
+}
+
+size_t route_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int) {
+    (void)Hq;
+    if (!route_mfma_applicable(dt, B, Tq, Hkv, D)) return 0;
+    const Plan p = plan_for(B, Tq, Hkv, N);
+    return p.ub_bytes + p.partial_bytes;
+}
+
+hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void* ws, hipStream_t st) {
+    const Plan p = plan_for(a.B, a.Tq, a.Hkv, a.N);
+    const int64_t Q = a.B * a.Tq;
+    uint16_t* Ub = static_cast<uint16_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
+    const int64_t n_real = Q * a.Hkv * 128, n_pad = p.q_pad * a.Hkv * 128;
+    hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, n_real,
+                       n_pad, Ub);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid(unsigned(ceil_div(a.N, p.bn)), unsigned(p.q_tiles));
+    const float inv_hq = 1.f / float(a.Hq);
+    const uint16_t* Kr = static_cast<const uint16_t*>(a.Krbar);
+    if (p.bm == 32)
+        hipLaunchKernelGGL((route_mfma_kernel<32, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
+                           inv_hq, c, partial);
+    else
+        hipLaunchKernelGGL((route_mfma_kernel<128, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
+                           inv_hq, c, partial);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.Tq > 1) {
+        hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
+                           a.N, int(a.Tq / p.bm), a.B, c);
+        err = hipGetLastError();
+    }
+    return err;
 }
 
 }  // namespace msa

@@ -24,6 +24,14 @@ from tests import workloads as W
 pytestmark = pytest.mark.gpu
 
 SCORE_TOL = 1e-4
+# Matrix-core routing rounds the query group sums U to bf16 (relative 2^-9 per
+# element); by Cauchy-Schwarz |delta s| <= (1/Hq) sum_g 2^-9 |U_g| <= 2^-9.
+MFMA_SCORE_TOL = 3e-3
+
+
+def _score_tol(dtype, d, B, Tq):
+    mfma = dtype == "bf16" and d == 128 and B * Tq > 4 and (Tq == 1 or Tq % 128 == 0)
+    return MFMA_SCORE_TOL if mfma else SCORE_TOL
 
 
 @pytest.fixture(scope="module")
@@ -163,6 +171,11 @@ ROUTE_CASES = [
     ("bf16", 64, 8, 2, 2, 5, 90, 6, 10),         # generic scan
     ("bf16", 128, 32, 8, 3, 3, 120, 7, 9),       # 9 queries
     ("f32", 128, 8, 8, 1, 1, 10, 1, 10),         # k = n_docs
+    ("bf16", 128, 32, 8, 32, 1, 300, 9, 16),     # matrix cores: 32 decode queries
+    ("bf16", 128, 32, 8, 40, 1, 200, 5, 8),      # matrix cores: 40 queries, padded tile
+    ("bf16", 128, 32, 8, 1, 256, 250, 8, 16),    # matrix cores: 256-token query, token max
+    ("bf16", 128, 16, 4, 2, 128, 100, 12, 5),    # matrix cores: 4 KV heads, 2 queries
+    ("bf16", 128, 16, 16, 6, 1, 90, 4, 7),       # matrix cores: 16 KV heads
 ]
 
 
@@ -178,15 +191,17 @@ def test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B
     ids, sc, ch, dc = _run_route(torch_mod, msa, ctx, Qr, Kb, coff, k, dtype)
     c_ref = oracle.chunk_scores(W.widen(Qr, dtype), W.widen(Kb, dtype))
     D_ref = oracle.doc_scores(c_ref, coff)
-    assert np.max(np.abs(ch - c_ref)) <= SCORE_TOL
-    assert np.max(np.abs(dc - D_ref)) <= SCORE_TOL
+    tol = _score_tol(dtype, d, B, Tq)
+    assert np.max(np.abs(ch - c_ref)) <= tol
+    assert np.max(np.abs(dc - D_ref)) <= tol
     for b in range(B):
-        _check_valid_topk(ids[b], sc[b], D_ref[b], SCORE_TOL)
+        _check_valid_topk(ids[b], sc[b], D_ref[b], tol)
 
 
-@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16)])
+@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16), (32, 1), (1, 256)])
 def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
-    Hq, Hkv, d, n_docs, k = 32, 8, 128, 500, 16
+    Hq, Hkv, d, k = 32, 8, 128, 16
+    n_docs = max(500, 20 * B * k)
     counts = np.random.default_rng(3).integers(1, 10, size=n_docs)
     coff = msa_synth.prefix_offsets(counts)
     N = int(coff[-1])
@@ -208,7 +223,7 @@ def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
         assert sorted(ids[b].tolist()) == sorted(ids_ref[b].tolist())      # bit-exact set
         margin = sc_ref[b].min() - np.delete(D_ref[b], ids_ref[b]).max()
         assert margin >= 0.05
-    assert np.max(np.abs(ch - c_ref)) <= SCORE_TOL
+    assert np.max(np.abs(ch - c_ref)) <= _score_tol("bf16", d, B, Tq)
 
 
 def test_route_ties_go_to_lowest_id(torch_mod, msa, ctx128):
