@@ -306,7 +306,11 @@ ATTN_CASES = [
     ("bf16", 128, 32, 8, 3, 4, 300, [30, 0, 700], 16),  # ragged memory, one empty
     ("bf16", 64, 8, 8, 2, 5, 5, [3, 9], 2),           # G = 1, Tq = L
     ("f32", 128, 16, 1, 1, 7, 19, [260], 33),         # G = 16, several splits
-    ("bf16", 128, 32, 8, 1, 64, 600, [250], 32),      # short prefill
+    ("bf16", 128, 32, 8, 1, 64, 600, [250], 32),      # short prefill (matrix cores)
+    ("bf16", 128, 32, 8, 1, 256, 256, [152], 16),     # prefill, Tq = L (matrix cores)
+    ("bf16", 128, 32, 8, 2, 200, 500, [0, 300], 16),  # partial query tile, one query without memory
+    ("bf16", 128, 8, 8, 1, 130, 130, [70], 8),        # G = 1, ragged tile
+    ("bf16", 128, 16, 1, 1, 96, 1000, [64], 16),      # G = 16
 ]
 
 
