@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
+    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32"], default="decode100m",
+                   help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
+                        "prefill8k / batch32: extra measurements on the 10M-token bank")
     p.add_argument("--gather", choices=["batch", "loop"], default="batch",
                    help="msa_gather submission: one hipMemcpyBatchAsync, or one hipMemcpyAsync per copy")
     return p.parse_args()
@@ -257,6 +260,192 @@ def cpu_baseline(args, wl, W, msa_synth):
                       f"{t_route + t_attn:.1f} s measured; {1 / t_step:.4f} tokens/s"}
 
 
+# ---------------------------------------------------------------- extra workloads
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bank_10m(args, torch, msa_synth, device_fill, W, layers):
+    lens = msa_synth.lognormal_lengths(args.seed, 10_000_000)
+    coff = msa_synth.ceil_chunk_offsets(lens, CHUNK)
+    N = int(coff[-1])
+    Krbar = torch.empty((layers, N, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    for l in range(layers):
+        device_fill.fill_counter_bf16(Krbar[l], args.seed, W.krbar_stream(l), 0)
+    return lens, coff, N, Krbar
+
+
+def run_prefill8k(args, torch, msa, msa_synth, device_fill, W):
+    """One routing layer of the 10M-token bank: an 8,192-token query routed on
+    the matrix cores (32 planted documents, top-32), the 32 documents gathered
+    from pinned host memory, then causal prefill attention over [gathered rows
+    ; 8,192 local tokens]."""
+    seed, k, T = args.seed, 32, 8192
+    lens, coff, N, Krbar = bank_10m(args, torch, msa_synth, device_fill, W, 1)
+    n_docs = len(lens)
+    Qr_h = msa_synth.normal_bf16(seed, 700, (1, T, Hq, D))
+    planted = msa_synth.pick_planted(seed, 51, n_docs, k)
+    toks = np.random.default_rng(seed + 52).integers(0, T, size=k)
+    qf = msa_synth.bf16_bits_to_f32(Qr_h)
+    for j, d in enumerate(planted):
+        rows = W.planted_pooled(seed, 0, qf[0, toks[j]], Hkv, int(coff[d + 1] - coff[d]), tag=j)
+        Krbar[0, coff[d]:coff[d + 1]].copy_(W.dev_bf16(rows))
+    Qr = W.dev_bf16(Qr_h)
+    Q = torch.empty((1, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    Kl = torch.empty((1, T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    Vl = torch.empty_like(Kl)
+    for t_, st in ((Q, 710), (Kl, 711), (Vl, 712)):
+        device_fill.fill_counter_bf16(t_, seed, st, 0)
+    ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+    coff_dev = torch.from_numpy(coff).cuda()
+    ids = torch.empty((1, k), dtype=torch.int32, pin_memory=True)
+    ws_r = msa.workspace(msa.msa_route_workspace_size(1, 1, T, Hq, Hkv, N, n_docs, k))
+    cap = int(np.sort(np.diff(coff))[-k:].sum())
+    KVmem = torch.empty((cap, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    mo_h = torch.zeros(2, dtype=torch.int64, pin_memory=True)
+    mo_d = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ws_a = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, T, Hq, Hkv, cap, T))
+    O = torch.empty_like(Q)
+    host = PinnedHost(N * ROW_KV)
+    device_fill.fill_counter_bf16((host.addr, N * ROW_KV // 2), seed, W.kvbar_stream(0), 0)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rs, re_, a_s, a_e = ev(), ev(), ev(), ev()
+    for e_ in (rs, re_):
+        e_.record()
+    t_route, t_attn, t_step = [], [], []
+    for it in range(args.warmup + args.steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        msa.msa_route_time_next(ctx, rs, re_)
+        msa.msa_route(ctx, Qr, Krbar[0], coff_dev, k, ids, ws_r)
+        main.synchronize()
+        msa.msa_gather(host.addr, ROW_KV, N, coff, ids.numpy(), k, KVmem, cap, mo_h, mo_d, side=side)
+        main.wait_stream(side)
+        a_s.record(main)
+        msa.msa_sparse_attn(ctx, Q, KVmem, mo_d, cap, Kl, Vl, k, 1.0 / math.sqrt(D), O, ws_a)
+        a_e.record(main)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            t_step.append(time.perf_counter() - t0)
+            t_route.append(rs.elapsed_time(re_) / 1e3)
+            t_attn.append(a_s.elapsed_time(a_e) / 1e3)
+    recovered = sorted(ids.numpy()[0].tolist()) == sorted(int(d) for d in planted)
+    route_flop = 2.0 * T * N * Hkv * D                     # group-folded contraction
+    M = int(mo_h[1])
+    attn_flop = 4.0 * D * Hq * (M * T + T * (T + 1) / 2)
+    tr, ta, ts = float(np.mean(t_route)), float(np.mean(t_attn)), float(np.mean(t_step))
+    host.free()
+    return {
+        "metric": "prefill routing + attention on the matrix cores (8,192-token query, 10M-token bank, one layer)",
+        "value": round(route_flop / tr / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ts * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "8,192-token query routed against 156,250 pooled chunks (10M tokens), top-32, "
+                               "then causal prefill over [gathered rows ; 8,192 local]",
+                   "n_docs": n_docs, "chunk_rows": N, "top_k": k, "memory_rows": M},
+        "route_ms": round(tr * 1e3, 4), "route_TFLOPs": round(route_flop / tr / 1e12, 1),
+        "route_mfma_util": round(route_flop / tr / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attn_ms": round(ta * 1e3, 4), "attn_TFLOPs": round(attn_flop / ta / 1e12, 1),
+        "attn_mfma_util": round(attn_flop / ta / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "planted_recovered": recovered,
+        "roofline": {"bound": "mfma", "achieved": round(route_flop / tr / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(route_flop / tr / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "route_mfma_kernel<128,128>", "flop_per_launch": route_flop},
+    }
+
+
+def run_batch32(args, torch, msa, msa_synth, device_fill, W):
+    """32 independent single-token decode queries against the 10M-token bank,
+    18 routing layers, top-16 each: per layer one shared routing pass (matrix
+    cores), a device-side gather of 32 x 16 documents from pinned host memory,
+    and 32 decode attentions over [gathered rows ; 2,048 local tokens]."""
+    seed, k, B, Lr, L = args.seed, 16, 32, args.layers, args.local
+    lens, coff, N, Krbar = bank_10m(args, torch, msa_synth, device_fill, W, Lr)
+    n_docs = len(lens)
+    planted = [msa_synth.pick_planted(seed + 100 + b, 50, n_docs, k) for b in range(B)]
+    taken = set()
+    for b in range(B):      # disjoint planted sets per query
+        if set(planted[b].tolist()) & taken:
+            planted[b] = msa_synth.pick_planted(seed + 100 + b, 50, n_docs, k, exclude=taken)
+        taken |= set(planted[b].tolist())
+    Qr, Q, Kl, Vl = [], [], [], []
+    for l in range(Lr):
+        qh = msa_synth.normal_bf16(seed, 800 + l, (B, 1, Hq, D))
+        qf = msa_synth.bf16_bits_to_f32(qh)
+        for b in range(B):
+            for j, d in enumerate(planted[b]):
+                rows = W.planted_pooled(seed, l, qf[b, 0], Hkv, int(coff[d + 1] - coff[d]), tag=1000 + b * k + j)
+                Krbar[l, coff[d]:coff[d + 1]].copy_(W.dev_bf16(rows))
+        Qr.append(W.dev_bf16(qh))
+        Q.append(W.dev_bf16(msa_synth.normal_bf16(seed, 900 + l, (B, 1, Hq, D))))
+        kl = torch.empty((B, L, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        vl = torch.empty_like(kl)
+        device_fill.fill_counter_bf16(kl, seed, 1200 + l, 0)
+        device_fill.fill_counter_bf16(vl, seed, 1300 + l, 0)
+        Kl.append(kl)
+        Vl.append(vl)
+    ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+    coff_dev = torch.from_numpy(coff).cuda()
+    ids = torch.empty((Lr, B, k), dtype=torch.int32, device="cuda")
+    ws_r = msa.workspace(msa.msa_route_workspace_size(1, B, 1, Hq, Hkv, N, n_docs, k))
+    cap = B * int(np.sort(np.diff(coff))[-k:].sum())
+    max_rows = int(np.sort(np.diff(coff))[-k:].sum())
+    KVmem = torch.empty((cap, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros((Lr, B + 1), dtype=torch.int64, device="cuda")
+    ws_g = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    ws_a = msa.workspace(msa.msa_sparse_attn_workspace_size(1, B, 1, Hq, Hkv, max_rows, L))
+    O = torch.empty((Lr, B, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
+    host = [PinnedHost(N * ROW_KV) for _ in range(Lr)]
+    for l in range(Lr):
+        device_fill.fill_counter_bf16((host[l].addr, N * ROW_KV // 2), seed, W.kvbar_stream(l), 0)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    timers = [(ev(), ev()) for _ in range(Lr * args.steps)]
+    for a, b_ in timers:
+        a.record()
+        b_.record()
+
+    def step(ti=None):
+        for l in range(Lr):
+            if ti is not None:
+                msa.msa_route_time_next(ctx, *timers[ti + l])
+            msa.msa_route(ctx, Qr[l], Krbar[l], coff_dev, k, ids[l], ws_r)
+            msa.msa_gather_device(ctx, host[l].addr, ROW_KV, N, coff_dev, ids[l], KVmem, cap, mo[l], ws_g)
+            msa.msa_sparse_attn(ctx, Q[l], KVmem, mo[l], max_rows, Kl[l], Vl[l], k, 1.0 / math.sqrt(D), O[l], ws_a)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(s_ * Lr)
+    torch.cuda.synchronize()
+    st = (time.perf_counter() - t0) / args.steps
+    scan = float(np.mean([a.elapsed_time(b_) for a, b_ in timers])) / 1e3
+    got = ids.cpu().numpy()
+    recovered = all(sorted(got[l, b].tolist()) == sorted(int(d) for d in planted[b]) for l in range(Lr) for b in range(B))
+    kr_bytes = Lr * N * ROW_KR
+    scan_bytes = N * ROW_KR + B * N * 4
+    for h in host:
+        h.free()
+    return {
+        "metric": "batched routed decode: K̄r GB/s and tokens/s (32 queries, 10M-token bank)",
+        "value": round(kr_bytes / st / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(st * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "32 single-token queries, 18 routing layers of 156,250 pooled chunks (10M tokens), "
+                               "top-16 each, device gather, 2,048 local tokens", "n_docs": n_docs,
+                   "chunk_rows": N, "batch": B, "layers": Lr, "top_k": k, "local": L},
+        "decode_tokens_per_s": round(B / st, 1),
+        "route_ms": round(scan * 1e3, 4),
+        "planted_recovered_all": recovered,
+        "roofline": {"bound": "hbm", "achieved": round(scan_bytes / scan / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(scan_bytes / scan / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "route_mfma_kernel<32,128>", "bytes_per_launch": scan_bytes},
+    }
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -273,6 +462,12 @@ def main():
     from tests import workloads as W
 
     msa.lib()
+    if args.workload != "decode100m":
+        fn = run_prefill8k if args.workload == "prefill8k" else run_batch32
+        out = fn(args, torch, msa, msa_synth, device_fill, W)
+        print(json.dumps(out), flush=True)
+        ok = out.get("planted_recovered", out.get("planted_recovered_all"))
+        sys.exit(0 if ok else 1)
     wl = build_workload(args, torch, msa, msa_synth, device_fill, W)
     run = Runner(args, torch, msa, wl)
     run.arm_timers(args.steps * wl["L"])
