@@ -27,6 +27,36 @@ import time
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "long_context_memory_chunk_amd", "csrc")
+
+# HBM counter calibration: for a plain 4 GiB device-to-device copy (bench.py
+# --workload hbmcopy under rocprofv3 --pmc), FETCH_SIZE reads 2,097,168.6 KiB per
+# dispatch (mean of the 11 full-size copies) for the 4,194,304 KiB read,
+# WRITE_SIZE reads 4,194,304 KiB for the 4,194,304 KiB written.
+FETCH_SCALE = 4194304.0 / 2097168.6
+WRITE_SCALE = 1.0
+# FETCH_SIZE / WRITE_SIZE of the routing scan on the 100M-token bank (KiB per
+# dispatch, mean over 108 dispatches), taken on the sources whose digest is
+# given; a different digest means the kernel has changed since, and the
+# traffic is reported as unknown.
+SCAN_COUNTERS = {"digest": "298d048304a90e6c", "fetch_kib": 1562595.3, "write_kib": 6103.5}
+SCAN_SOURCES = ("route.hip", "common.hpp", "launch.hpp")
+
+
+def source_digest(names):
+    import hashlib
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(counters, sources):
+    """Calibrated HBM bytes per launch, or None if the kernel source changed."""
+    if source_digest(sources) != counters["digest"]:
+        return None
+    return int(round((counters["fetch_kib"] * FETCH_SCALE + counters["write_kib"] * WRITE_SCALE) * 1024))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
@@ -51,9 +81,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
-    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32"], default="decode100m",
+    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32", "hbmcopy"], default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
-                        "prefill8k / batch32: extra measurements on the 10M-token bank")
+                        "prefill8k / batch32: extra measurements on the 10M-token bank; "
+                        "hbmcopy: a plain 4 GiB device-to-device copy, the known-size kernel that "
+                        "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--gather", choices=["batch", "loop"], default="batch",
                    help="msa_gather submission: one hipMemcpyBatchAsync, or one hipMemcpyAsync per copy")
     return p.parse_args()
@@ -446,6 +478,30 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
     }
 
 
+def run_hbmcopy(args, torch, msa, msa_synth, device_fill, W):
+    """A plain copy of a 4 GiB device tensor into another, 10 launches: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch, against the 4 GiB
+    it must read and write, give the factor that turns those counters into
+    bytes for the other kernels."""
+    n = 2 << 30                                  # bf16 elements: 4 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    device_fill.fill_counter_bf16(src, args.seed, 1, 0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 10
+    same = bool(torch.equal(src[:1 << 20], dst[:1 << 20]))
+    return {"metric": "device copy GB/s (read + write)", "value": round(2 * n * 2 / ms / 1e6, 1), "unit": "GB/s",
+            "bytes_read_per_launch": n * 2, "bytes_written_per_launch": n * 2, "ms_per_launch": round(ms, 4),
+            "copy_checked": same}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -463,10 +519,10 @@ def main():
 
     msa.lib()
     if args.workload != "decode100m":
-        fn = run_prefill8k if args.workload == "prefill8k" else run_batch32
+        fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "hbmcopy": run_hbmcopy}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
         print(json.dumps(out), flush=True)
-        ok = out.get("planted_recovered", out.get("planted_recovered_all"))
+        ok = out.get("planted_recovered", out.get("planted_recovered_all", out.get("copy_checked")))
         sys.exit(0 if ok else 1)
     wl = build_workload(args, torch, msa, msa_synth, device_fill, W)
     run = Runner(args, torch, msa, wl)
@@ -507,6 +563,7 @@ def main():
     kr_bytes_step = L * N * ROW_KR
     scan_bytes = N * (ROW_KR + 4)            # K̄r read + one fp32 chunk score written
     achieved = scan_bytes / scan_avg_s / 1e9
+    traffic = counter_traffic(SCAN_COUNTERS, SCAN_SOURCES)
     out = {
         "metric": METRIC,
         "value": round(kr_bytes_step / step_s / 1e9, 2),
@@ -537,8 +594,9 @@ def main():
                           "Krbar_GBps": round(kr_bytes_step / dev_step_s / 1e9, 2),
                           "same_output_as_host_gather": same_out},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "route_scan_bf16_d128", "bytes_per_launch": scan_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "route_scan_bf16_d128", "bytes_per_launch": scan_bytes,
+                     "traffic_over_algorithmic": None if traffic is None else round(traffic / scan_bytes, 5)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
