@@ -81,9 +81,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
-    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32", "hbmcopy"], default="decode100m",
+    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32", "encode10m", "hbmcopy"],
+                   default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
                         "prefill8k / batch32: extra measurements on the 10M-token bank; "
+                        "encode10m: the offline encode of one layer of the 10M-token bank; "
                         "hbmcopy: a plain 4 GiB device-to-device copy, the known-size kernel that "
                         "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--gather", choices=["batch", "loop"], default="batch",
@@ -478,6 +480,63 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
     }
 
 
+ENCODE_STREAMS = (21, 22, 23)     # counter streams of the raw K, V, Kr of the encode workload
+
+
+def encode_10m_inputs(seed, torch, msa_synth, device_fill):
+    """Raw K, V, Kr [T, 8, 128] bf16 of one layer of the 10M-token bank (log-normal
+    document lengths), filled on the device from the counter generator."""
+    lens = msa_synth.lognormal_lengths(seed, 10_000_000)
+    tok = msa_synth.prefix_offsets(lens)
+    T = int(tok[-1])
+    raw = []
+    for st in ENCODE_STREAMS:
+        x = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        device_fill.fill_counter_bf16(x, seed, st, 0)
+        raw.append(x)
+    return lens, tok, raw
+
+
+def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
+    """Offline encode of one layer of the 10M-token bank: raw K, V, Kr
+    [10M, 8, 128] bf16 (61.4 GB) pooled into KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128]
+    (0.96 GB) with document-wise RoPE; every launch times the whole layer."""
+    lens, tok, (K, V, Kr) = encode_10m_inputs(args.seed, torch, msa_synth, device_fill)
+    coff = msa.msa_chunk_offsets(tok, CHUNK)
+    T, N = int(tok[-1]), int(coff[-1])
+    KVbar = torch.empty((N, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    Krbar = torch.empty((N, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    tok_d, coff_d = torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda()
+    ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+    enc = lambda: msa.msa_encode_pool(ctx, K, V, Kr, tok_d, coff_d, KVbar, Krbar, CHUNK)
+    for _ in range(args.warmup):
+        enc()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        enc()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = 3 * T * ROW_KR + N * (ROW_KV + ROW_KR)
+    finite = bool(torch.isfinite(KVbar).all()) and bool(torch.isfinite(Krbar).all())
+    ctx.close()
+    return {"metric": "offline encode GB/s (doc-wise RoPE + chunk mean-pool of K, V, Kr)",
+            "value": round(nbytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "one layer of the 10M-token bank: raw K, V, Kr [10M, 8, 128] bf16 -> "
+                                   "KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128], chunk 64",
+                       "tokens": T, "n_docs": len(lens), "chunk_rows": N, "max_doc_tokens": int(lens.max())},
+            "encode_kernel_ms": round(ms, 4), "outputs_finite": finite,
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": None, "kernel": "encode_pool_kernel", "bytes_per_launch": nbytes}}
+
+
 def run_hbmcopy(args, torch, msa, msa_synth, device_fill, W):
     """A plain copy of a 4 GiB device tensor into another, 10 launches: under
     rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch, against the 4 GiB
@@ -519,10 +578,12 @@ def main():
 
     msa.lib()
     if args.workload != "decode100m":
-        fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "hbmcopy": run_hbmcopy}[args.workload]
+        fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "encode10m": run_encode10m,
+              "hbmcopy": run_hbmcopy}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
         print(json.dumps(out), flush=True)
-        ok = out.get("planted_recovered", out.get("planted_recovered_all", out.get("copy_checked")))
+        ok = out.get("planted_recovered", out.get("planted_recovered_all",
+                                                  out.get("copy_checked", out.get("outputs_finite"))))
         sys.exit(0 if ok else 1)
     wl = build_workload(args, torch, msa, msa_synth, device_fill, W)
     run = Runner(args, torch, msa, wl)

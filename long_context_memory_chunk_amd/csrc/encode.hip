@@ -7,87 +7,137 @@
 // ruixiangma.github.io blog, 方法 › 稀疏注意力机制 and 文档级RoPE.
 //
 // Mapping (HBM-bound: every input byte is read once, 3/c of it written):
-//   one workgroup per document, 4 waves; wave w pools chunks w, w+4, ...;
-//   a lane owns a 16-byte slot of the first half of a head and the matching
-//   slot of the second half (the RoPE pair i, i + d/2) of K, V and Kr, and
-//   accumulates the chunk's rows in fp32 registers.  Row loads of one wave
-//   cover whole 128-byte segments.  cos/sin come from the context's table
-//   (float64 angles rounded to float32).
+//   one wave per pooled chunk over the whole bank (grid-stride), so a long
+//   document costs no more per wave than a short one; the wave finds its
+//   document by binary search in doc_chunk_off.  A lane owns a 16-byte slot
+//   of the first half of a head and the matching slot of the second half (the
+//   RoPE pair i, i + d/2) of K, V and Kr, and accumulates the chunk's rows in
+//   fp32 registers, in row order.  Rows are taken UNROLL at a time with all of
+//   their loads issued first (nontemporal: the raw tensors are streamed once),
+//   which keeps enough bytes in flight per wave to cover HBM latency.  Row
+//   loads of one wave cover whole 128-byte segments.  cos/sin come from the
+//   context's table (float64 angles rounded to float32).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace msa {
 namespace {
 
-template <typename T, int D>
+constexpr int kEncodeUnroll = 1;   // deeper unrolling measured no faster (bytes in flight per CU stay ~90 KB)
+
+template <typename T> struct Raw16;
+template <> struct Raw16<float> {
+    __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+        out[0] = __uint_as_float(v[0]); out[1] = __uint_as_float(v[1]);
+        out[2] = __uint_as_float(v[2]); out[3] = __uint_as_float(v[3]);
+    }
+};
+template <> struct Raw16<bf16_t> {
+    __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+        out[0] = bf16_lo(v[0]); out[1] = bf16_hi(v[0]);
+        out[2] = bf16_lo(v[1]); out[3] = bf16_hi(v[1]);
+        out[4] = bf16_lo(v[2]); out[5] = bf16_hi(v[2]);
+        out[6] = bf16_lo(v[3]); out[7] = bf16_hi(v[3]);
+    }
+};
+
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Largest d in [0, n_docs) with off[d] <= n (off non-decreasing, off[0] = 0).
+__device__ __forceinline__ int64_t doc_of_chunk(const int64_t* __restrict__ off, int64_t n_docs,
+                                                int64_t n) {
+    int64_t lo = 0, hi = n_docs - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= n) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <typename T, int D, int UNROLL>
 __global__ __launch_bounds__(256) void encode_pool_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Kr,
-    const int64_t* __restrict__ tok_off, const int64_t* __restrict__ chunk_off,
+    const int64_t* __restrict__ tok_off, const int64_t* __restrict__ chunk_off, int64_t n_docs,
     int64_t T_rows, int64_t N, int hkv, int chunk_len,
     const float2* __restrict__ rope_cs, int max_pos,
     T* __restrict__ KVbar, T* __restrict__ Krbar) {
     constexpr int VEC = Vec16<T>::kN;           // elements per 16-byte slot
     constexpr int HALF = D / 2;
     constexpr int SLOTS_PER_HEAD = HALF / VEC;
-    const int64_t doc = blockIdx.x;
-    const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-
-    int64_t s = tok_off[doc], e = tok_off[doc + 1];
-    s = s < 0 ? 0 : (s > T_rows ? T_rows : s);
-    e = e < s ? s : (e > T_rows ? T_rows : e);
-    int64_t c0 = chunk_off[doc], c1 = chunk_off[doc + 1];
-    c0 = c0 < 0 ? 0 : (c0 > N ? N : c0);
-    c1 = c1 < c0 ? c0 : (c1 > N ? N : c1);
-    const int64_t n_chunks_len = (e - s + chunk_len - 1) / chunk_len;
-    const int64_t n_chunks = (c1 - c0) < n_chunks_len ? (c1 - c0) : n_chunks_len;
-
     const int slots = hkv * SLOTS_PER_HEAD;
     const int64_t row_elems = int64_t(hkv) * D;
+    const int64_t n_waves = int64_t(gridDim.x) * (blockDim.x / kWave);
 
-    for (int64_t j = wave; j < n_chunks; j += 4) {
+    for (int64_t n = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; n < N;
+         n += n_waves) {
+        const int64_t doc = doc_of_chunk(chunk_off, n_docs, n);
+        int64_t s = tok_off[doc], e = tok_off[doc + 1];
+        s = s < 0 ? 0 : (s > T_rows ? T_rows : s);
+        e = e < s ? s : (e > T_rows ? T_rows : e);
+        const int64_t j = n - chunk_off[doc];
         const int64_t r0 = s + j * chunk_len;
+        if (j < 0 || r0 >= e) continue;         // inconsistent offsets: row n is left unwritten
         const int64_t r1 = (r0 + chunk_len < e) ? r0 + chunk_len : e;
         const float cnt = float(r1 - r0);
-        const int64_t n = c0 + j;
+
         for (int slot = lane; slot < slots; slot += kWave) {
             const int h = slot / SLOTS_PER_HEAD;
             const int i0 = (slot % SLOTS_PER_HEAD) * VEC;
-            float k1[VEC], k2[VEC], v1[VEC], v2[VEC], r1_[VEC], r2_[VEC];
+            float k1[VEC], k2[VEC], v1[VEC], v2[VEC], q1[VEC], q2[VEC];
 #pragma unroll
-            for (int u = 0; u < VEC; ++u) { k1[u] = k2[u] = v1[u] = v2[u] = r1_[u] = r2_[u] = 0.f; }
-            for (int64_t r = r0; r < r1; ++r) {
-                int pos = int(r - s);
-                pos = pos < max_pos ? pos : max_pos - 1;
-                const int64_t base = r * row_elems + int64_t(h) * D + i0;
-                float a[VEC], b[VEC], x[VEC];
-                Vec16<T>::load(K + base, a);
-                Vec16<T>::load(K + base + HALF, b);
-                const float2* cs = rope_cs + int64_t(pos) * HALF + i0;
+            for (int u = 0; u < VEC; ++u) { k1[u] = k2[u] = v1[u] = v2[u] = q1[u] = q2[u] = 0.f; }
+            const T* kp = K + r0 * row_elems + int64_t(h) * D + i0;
+            const T* vp = V + r0 * row_elems + int64_t(h) * D + i0;
+            const T* qp = Kr + r0 * row_elems + int64_t(h) * D + i0;
+            int64_t r = r0;
+            auto rows = [&](auto n_rows_c) {
+                constexpr int R = decltype(n_rows_c)::value;
+                u32x4 ka[R], kb[R], va[R], vb[R], qa[R], qb[R];
 #pragma unroll
-                for (int u = 0; u < VEC; ++u) {
-                    const float2 t = cs[u];
-                    k1[u] += a[u] * t.x - b[u] * t.y;
-                    k2[u] += b[u] * t.x + a[u] * t.y;
+                for (int u = 0; u < R; ++u) {
+                    const int64_t o = int64_t(u) * row_elems;
+                    ka[u] = ld_stream(kp + o); kb[u] = ld_stream(kp + o + HALF);
+                    va[u] = ld_stream(vp + o); vb[u] = ld_stream(vp + o + HALF);
+                    qa[u] = ld_stream(qp + o); qb[u] = ld_stream(qp + o + HALF);
                 }
-                Vec16<T>::load(V + base, x);
 #pragma unroll
-                for (int u = 0; u < VEC; ++u) v1[u] += x[u];
-                Vec16<T>::load(V + base + HALF, x);
+                for (int u = 0; u < R; ++u) {
+                    int pos = int(r + u - s);
+                    pos = pos < max_pos ? pos : max_pos - 1;
+                    const float2* cs = rope_cs + int64_t(pos) * HALF + i0;
+                    float a[VEC], b[VEC];
+                    Raw16<T>::unpack(ka[u], a);
+                    Raw16<T>::unpack(kb[u], b);
 #pragma unroll
-                for (int u = 0; u < VEC; ++u) v2[u] += x[u];
-                Vec16<T>::load(Kr + base, x);
+                    for (int w = 0; w < VEC; ++w) {
+                        const float2 t = cs[w];
+                        k1[w] += a[w] * t.x - b[w] * t.y;
+                        k2[w] += b[w] * t.x + a[w] * t.y;
+                    }
+                    Raw16<T>::unpack(va[u], a);
+                    Raw16<T>::unpack(vb[u], b);
 #pragma unroll
-                for (int u = 0; u < VEC; ++u) r1_[u] += x[u];
-                Vec16<T>::load(Kr + base + HALF, x);
+                    for (int w = 0; w < VEC; ++w) { v1[w] += a[w]; v2[w] += b[w]; }
+                    Raw16<T>::unpack(qa[u], a);
+                    Raw16<T>::unpack(qb[u], b);
 #pragma unroll
-                for (int u = 0; u < VEC; ++u) r2_[u] += x[u];
-            }
+                    for (int w = 0; w < VEC; ++w) { q1[w] += a[w]; q2[w] += b[w]; }
+                }
+                kp += R * row_elems; vp += R * row_elems; qp += R * row_elems;
+                r += R;
+            };
+            while (r + UNROLL <= r1) rows(std::integral_constant<int, UNROLL>{});
+            while (r < r1) rows(std::integral_constant<int, 1>{});
 #pragma unroll
             for (int u = 0; u < VEC; ++u) {
                 k1[u] /= cnt; k2[u] /= cnt;
                 v1[u] /= cnt; v2[u] /= cnt;
-                r1_[u] /= cnt; r2_[u] /= cnt;
+                q1[u] /= cnt; q2[u] /= cnt;
             }
             T* kv = KVbar + n * 2 * row_elems + int64_t(h) * D + i0;
             Vec16<T>::store(kv, k1);
@@ -95,8 +145,8 @@ __global__ __launch_bounds__(256) void encode_pool_kernel(
             Vec16<T>::store(kv + row_elems, v1);
             Vec16<T>::store(kv + row_elems + HALF, v2);
             T* kr = Krbar + n * row_elems + int64_t(h) * D + i0;
-            Vec16<T>::store(kr, r1_);
-            Vec16<T>::store(kr + HALF, r2_);
+            Vec16<T>::store(kr, q1);
+            Vec16<T>::store(kr + HALF, q2);
         }
     }
 }
@@ -106,9 +156,11 @@ hipError_t launch_typed(const msa_ctx* ctx, const void* K, const void* V, const 
                         const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs,
                         int64_t T_rows, int64_t N, int hkv, int chunk_len, void* KVbar,
                         void* Krbar, hipStream_t st) {
-    hipLaunchKernelGGL((encode_pool_kernel<T, D>), dim3(unsigned(n_docs)), dim3(256), 0, st,
+    const int64_t blocks = ceil_div(N, int64_t(4));
+    const unsigned grid = unsigned(blocks < (int64_t(1) << 30) ? blocks : (int64_t(1) << 30));
+    hipLaunchKernelGGL((encode_pool_kernel<T, D, kEncodeUnroll>), dim3(grid), dim3(256), 0, st,
                        static_cast<const T*>(K), static_cast<const T*>(V),
-                       static_cast<const T*>(Kr), tok_off, chunk_off, T_rows, N, hkv,
+                       static_cast<const T*>(Kr), tok_off, chunk_off, n_docs, T_rows, N, hkv,
                        chunk_len, ctx->rope_cs, ctx->max_pos, static_cast<T*>(KVbar),
                        static_cast<T*>(Krbar));
     return hipGetLastError();
@@ -120,7 +172,7 @@ hipError_t launch_encode(const msa_ctx* ctx, msa_dtype dt, const void* K, const 
                          const void* Kr, const int64_t* tok_off, const int64_t* chunk_off,
                          int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
                          void* KVbar, void* Krbar, hipStream_t st) {
-    if (n_docs == 0) return hipSuccess;
+    if (n_docs == 0 || N == 0) return hipSuccess;
     if (dt == MSA_BF16) {
         if (ctx->head_dim == 128)
             return launch_typed<bf16_t, 128>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N,

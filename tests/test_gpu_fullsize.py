@@ -278,3 +278,36 @@ def test_prefill8k_10m_layer_sampled(env):
         ref = oracle.sparse_attn(qi, rows[:, 0], rows[:, 1], [0, len(rows)], kl[None], vl[None], k,
                                  1 / math.sqrt(D), 1e6)
         assert np.max(np.abs(W.widen(got_o[0, i], "bf16") - ref[0, 0])) <= 2e-2, i
+
+
+@pytest.mark.timeout(900)
+def test_encode_10m_layer_sampled(env):
+    """The offline encode of one layer of the 10M-token bank (raw K, V, Kr
+    [10M, 8, 128] bf16, log-normal lengths up to 8,192 tokens), launched as
+    bench.py's encode workload launches it; the oracle pools 60 documents
+    (the longest, the shortest, the first, the last and 56 drawn at random)
+    from their regenerated raw rows."""
+    torch, msa, device, ctx = env
+    import bench
+    seed = 0
+    lens, tok, (K, V, Kr) = bench.encode_10m_inputs(seed, torch, msa_synth, device)
+    coff = msa.msa_chunk_offsets(tok, C)
+    N = int(coff[-1])
+    KVbar = torch.full((N, 2, Hkv, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Krbar = torch.full((N, Hkv, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    msa.msa_encode_pool(ctx, K, V, Kr, torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda(),
+                        KVbar, Krbar, C)
+    torch.cuda.synchronize()
+    del K, V, Kr
+    assert bool(torch.isfinite(KVbar).all()) and bool(torch.isfinite(Krbar).all())
+    n_docs = len(lens)
+    docs = {int(np.argmax(lens)), int(np.argmin(lens)), 0, n_docs - 1}
+    docs |= set(np.random.default_rng(9).choice(n_docs, 56, replace=False).tolist())
+    for d in sorted(docs):
+        s, e, c0, c1 = int(tok[d]), int(tok[d + 1]), int(coff[d]), int(coff[d + 1])
+        raw = [W.widen(W.counter_rows(seed, st, s, e, Hkv, D), "bf16") for st in bench.ENCODE_STREAMS]
+        Kb, Vb, Rb = oracle.encode_pool(*raw, np.array([0, e - s]), C, 1e6)
+        kv = W.widen(W.host_bits(KVbar[c0:c1]), "bf16")
+        kr = W.widen(W.host_bits(Krbar[c0:c1]), "bf16")
+        for got, ref in ((kv[:, 0], Kb), (kv[:, 1], Vb), (kr, Rb)):
+            assert W.rel_row_err(got, ref) <= 2 ** -8 + 1e-5, d
