@@ -17,8 +17,8 @@
 // the same loads (16-lane DPP sums of squares), runs 8 k-steps of
 // v_mfma_f32_32x32x16_bf16 into a per-group accumulator, and adds rn times
 // that accumulator to the running total.  K̄r enters the MFMA exactly; U is
-// rounded once to bf16 (relative error 2^-9 per element; see the design
-// notes for the score tolerance this implies).
+// rounded once to bf16 (relative error <= 2^-9 per element), which moves a
+// score by at most (1/Hq) sum_g 2^-9 |U_g| <= 2^-9, since |U_g| <= G.
 // Epilogue: Tq = 1 -> each row is its own query, scores are written; Tq a
 // multiple of BM -> the tile's column maxima over its BM tokens are written
 // to a partial array and route_mfma_tokmax takes the max over a query's tiles.

@@ -4,9 +4,13 @@ Tolerances (stated where used):
   pooled rows      fp32 1e-5, bf16 2e-2, relative per (chunk, head) row:
                    |got - ref| <= rtol * (|ref| + rms(ref row))
   attention output fp32 1e-3, bf16 2e-2, max-abs of the normalised output
-  chunk/doc scores 1e-4 absolute on the fp32-accumulating vector paths
-                   (1024-term fp32 sums of terms bounded by the head-group
-                   size; see the design notes for the derivation)
+  chunk/doc scores 1e-4 absolute on the fp32-accumulating vector paths: a
+                   score is (1/Hq) sum_g U_g . k_g/|k_g| with |U_g| <= G, and
+                   a 128-term fp32 dot product errs by at most 128 * 2^-24 *
+                   |U_g|, so the sum over Hkv groups / Hq errs by <= 8e-6;
+                   rsqrt and the unit-query error add ~1e-6
+                   3e-3 absolute on the matrix-core path, which rounds U to
+                   bf16 (relative 2^-9 per element): |delta s| <= 2^-9
   top-k            document id sets bit-exact on planted-margin inputs; on
                    unplanted inputs every selected id is a valid top-k under
                    the score tolerance and the order is (score desc, id asc)
