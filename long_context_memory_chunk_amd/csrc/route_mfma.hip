@@ -40,24 +40,63 @@ __global__ __launch_bounds__(256) void u_to_bf16_kernel(const float* __restrict_
     Ub[i] = (i < n_real) ? f32_to_bf16(U[i]) : uint16_t(0);
 }
 
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear id, and
+// each XCD has its own L2.  Consecutive workgroups of one XCD take the tiles of
+// one super-tile of SQ query tiles x SC chunk tiles, so the tiles in flight on
+// an XCD share their U and K̄r slices through its L2 (at 128 x 128 tiles and
+// SQ = SC = 8: 2 MB of U + 2 MB of K̄r), and K̄r is streamed from HBM once per
+// super-tile row instead of once per query tile.
+constexpr int kXcds = 8;
+
+struct TileOrder {
+    int64_t tq, tn;          // query tiles, chunk tiles
+    int sq, sc;              // super-tile extent (query tiles, chunk tiles)
+    int64_t n_sq;            // super-tiles along the queries
+    int64_t blocks;          // grid size (a multiple of kXcds * sq * sc)
+};
+
+__host__ __device__ inline TileOrder tile_order(int64_t tq, int64_t tn) {
+    TileOrder o;
+    o.tq = tq; o.tn = tn;
+    o.sq = tq < 8 ? int(tq) : 8;
+    o.sc = 8;
+    o.n_sq = (tq + o.sq - 1) / o.sq;
+    const int64_t n_super = o.n_sq * ((tn + o.sc - 1) / o.sc);
+    o.blocks = ((n_super + kXcds - 1) / kXcds) * kXcds * o.sq * o.sc;
+    return o;
+}
+
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void route_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void route_mfma_kernel(
     const uint16_t* __restrict__ Ub, int64_t Q, const uint16_t* __restrict__ Kr, int64_t N, int hkv,
-    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial) {
+    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial, TileOrder ord) {
     constexpr int WM = (BM >= 64) ? 2 : 1;        // waves along queries
     constexpr int WN = 4 / WM;                    // waves along chunks
     constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
     constexpr int MI = TM / 32, NI = TN / 32;     // 32x32 MFMA tiles per wave
+    constexpr int RU = BM * 16 / 256, RK = BN * 16 / 256;   // 16-byte pieces per thread
     __shared__ __attribute__((aligned(16))) uint16_t sU[BM * kStride];
     __shared__ __attribute__((aligned(16))) uint16_t sK[BN * kStride];
     __shared__ float sRn[BN];
     __shared__ float sMax[WM][BN];
 
+    // ---- which tile (see TileOrder)
+    const int64_t lin = blockIdx.x;
+    const int xcd = int(lin % kXcds);
+    const int64_t loc = lin / kXcds;
+    const int per = ord.sq * ord.sc;
+    const int64_t sup = (loc / per) * kXcds + xcd;
+    const int w = int(loc % per);
+    const int64_t qt = (sup % ord.n_sq) * ord.sq + w % ord.sq;
+    const int64_t ct = (sup / ord.n_sq) * ord.sc + w / ord.sq;
+    if (qt >= ord.tq || ct >= ord.tn) return;     // whole workgroup: padding of the grid
+
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t n0 = int64_t(blockIdx.x) * BN;
-    const int64_t q0 = int64_t(blockIdx.y) * BM;
+    const int64_t n0 = ct * BN;
+    const int64_t q0 = qt * BM;
     const int64_t row_elems = int64_t(hkv) * 128;
+    const int c = tid % 16;                       // 16-byte column of a 128-wide slice
 
     f32x16 tot[MI][NI], acc[MI][NI];
 #pragma unroll
@@ -67,19 +106,33 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) { tot[a][b][i] = 0.f; acc[a][b][i] = 0.f; }
 
-    for (int g = 0; g < hkv; ++g) {
-        // ---- stage U and K̄r slices of head group g; norms of the K̄r slices
-        for (int r = tid / 16; r < BM; r += 16) {
-            const int c = tid % 16;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(Ub + (q0 + r) * row_elems + g * 128 + c * 8);
-            *reinterpret_cast<u32x4*>(sU + r * kStride + c * 8) = v;
+    // ---- register prefetch of one head group's U and K̄r slices
+    u32x4 ru[RU], rk[RK];
+    auto fetch = [&](int g) {
+#pragma unroll
+        for (int j = 0; j < RU; ++j) {
+            const int r = tid / 16 + 16 * j;
+            ru[j] = *reinterpret_cast<const u32x4*>(Ub + (q0 + r) * row_elems + g * 128 + c * 8);
         }
-        for (int r = tid / 16; r < BN; r += 16) {
-            const int c = tid % 16;
-            int64_t n = n0 + r;
-            n = n < N ? n : N - 1;                       // tail rows: computed, never stored
-            const u32x4 v = __builtin_nontemporal_load(
+#pragma unroll
+        for (int j = 0; j < RK; ++j) {
+            int64_t n = n0 + tid / 16 + 16 * j;
+            n = n < N ? n : N - 1;                   // tail rows: computed, never stored
+            rk[j] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4*>(Kr + n * row_elems + g * 128 + c * 8));
+        }
+    };
+    fetch(0);
+
+    for (int g = 0; g < hkv; ++g) {
+        // ---- slices of group g to LDS; norms of the K̄r slices
+#pragma unroll
+        for (int j = 0; j < RU; ++j)
+            *reinterpret_cast<u32x4*>(sU + (tid / 16 + 16 * j) * kStride + c * 8) = ru[j];
+#pragma unroll
+        for (int j = 0; j < RK; ++j) {
+            const int r = tid / 16 + 16 * j;
+            const u32x4 v = rk[j];
             *reinterpret_cast<u32x4*>(sK + r * kStride + c * 8) = v;
             float s = 0.f, f;
             f = bf16_lo(v.x); s += f * f; f = bf16_hi(v.x); s += f * f;
@@ -90,6 +143,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
             if (c == 0) sRn[r] = __builtin_amdgcn_rsqf(fmaxf(s, kEps * kEps));
         }
         __syncthreads();
+        if (g + 1 < hkv) fetch(g + 1);               // in flight during this group's MFMAs
 
         // ---- 128-deep contraction of this group on the matrix cores
 #pragma unroll
@@ -153,7 +207,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(
 #pragma unroll
         for (int w = 1; w < WM; ++w) m = fmaxf(m, sMax[w][t]);
         const int64_t n = n0 + t;
-        if (n < N) partial[int64_t(blockIdx.y) * N + n] = m * inv_hq;
+        if (n < N) partial[qt * N + n] = m * inv_hq;
     }
 }
 
@@ -211,15 +265,16 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                        n_pad, Ub);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid(unsigned(ceil_div(a.N, p.bn)), unsigned(p.q_tiles));
+    const TileOrder ord = tile_order(p.q_tiles, ceil_div(a.N, p.bn));
+    const dim3 grid(unsigned(ord.blocks));
     const float inv_hq = 1.f / float(a.Hq);
     const uint16_t* Kr = static_cast<const uint16_t*>(a.Krbar);
     if (p.bm == 32)
         hipLaunchKernelGGL((route_mfma_kernel<32, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
-                           inv_hq, c, partial);
+                           inv_hq, c, partial, ord);
     else
         hipLaunchKernelGGL((route_mfma_kernel<128, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
-                           inv_hq, c, partial);
+                           inv_hq, c, partial, ord);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.Tq > 1) {
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
