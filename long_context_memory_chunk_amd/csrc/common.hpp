@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return uint16_t(u >> 16);
 }
 
+// Two floats -> packed bf16 bits (a in the low half) on the hardware
+// converter, which rounds to nearest even like f32_to_bf16.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_hw v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Load/store of a scalar element of either storage type as float.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -66,10 +66,29 @@ __host__ __device__ inline TileOrder tile_order(int64_t tq, int64_t tn) {
     return o;
 }
 
-template <int BM, int BN>
+// rn[n][g] = 1 / max(|K̄r[n][g]|, eps), for the prefill path, where every chunk
+// tile is used by many query tiles: 16 lanes per 128-wide slice, the same
+// per-lane sums and DPP reduction as the inline form in route_mfma_kernel.
+__global__ __launch_bounds__(256) void route_rnorm_kernel(const uint16_t* __restrict__ Kr, int64_t n_slices,
+                                                          float* __restrict__ rn) {
+    const int64_t slice = (int64_t(blockIdx.x) * 256 + threadIdx.x) / 16;
+    const int c = threadIdx.x % 16;
+    const int64_t sl = slice < n_slices ? slice : n_slices - 1;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kr + sl * 128 + c * 8));
+    float s = 0.f, f;
+    f = bf16_lo(v.x); s += f * f; f = bf16_hi(v.x); s += f * f;
+    f = bf16_lo(v.y); s += f * f; f = bf16_hi(v.y); s += f * f;
+    f = bf16_lo(v.z); s += f * f; f = bf16_hi(v.z); s += f * f;
+    f = bf16_lo(v.w); s += f * f; f = bf16_hi(v.w); s += f * f;
+    s = group_sum<16>(s);
+    if (c == 0 && slice < n_slices) rn[slice] = __builtin_amdgcn_rsqf(fmaxf(s, kEps * kEps));
+}
+
+template <int BM, int BN, bool PRE_RN>
 __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
     const uint16_t* __restrict__ Ub, int64_t Q, const uint16_t* __restrict__ Kr, int64_t N, int hkv,
-    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial, TileOrder ord) {
+    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial, TileOrder ord,
+    const float* __restrict__ rn_pre) {
     constexpr int WM = (BM >= 64) ? 2 : 1;        // waves along queries
     constexpr int WN = 4 / WM;                    // waves along chunks
     constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
@@ -99,12 +118,13 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
     const int c = tid % 16;                       // 16-byte column of a 128-wide slice
 
     f32x16 tot[MI][NI], acc[MI][NI];
+    const f32x16 zero = {};
 #pragma unroll
     for (int a = 0; a < MI; ++a)
 #pragma unroll
         for (int b = 0; b < NI; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) { tot[a][b][i] = 0.f; acc[a][b][i] = 0.f; }
+            for (int i = 0; i < 16; ++i) tot[a][b][i] = 0.f;
 
     // ---- register prefetch of one head group's U and K̄r slices
     u32x4 ru[RU], rk[RK];
@@ -134,6 +154,7 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
             const int r = tid / 16 + 16 * j;
             const u32x4 v = rk[j];
             *reinterpret_cast<u32x4*>(sK + r * kStride + c * 8) = v;
+            if constexpr (PRE_RN) continue;
             float s = 0.f, f;
             f = bf16_lo(v.x); s += f * f; f = bf16_hi(v.x); s += f * f;
             f = bf16_lo(v.y); s += f * f; f = bf16_hi(v.y); s += f * f;
@@ -160,19 +181,24 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
             for (int a = 0; a < MI; ++a)
 #pragma unroll
                 for (int b = 0; b < NI; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], ks == 0 ? zero : acc[a][b],
+                                                                        0, 0, 0);
         }
         // ---- scale by 1/|K̄r[n][g]| (one chunk column per lane) and accumulate
 #pragma unroll
         for (int b = 0; b < NI; ++b) {
-            const float rn = sRn[wn * TN + b * 32 + lane % 32];
+            float rn;
+            if constexpr (PRE_RN) {
+                int64_t n = n0 + wn * TN + b * 32 + lane % 32;
+                n = n < N ? n : N - 1;
+                rn = rn_pre[n * hkv + g];
+            } else {
+                rn = sRn[wn * TN + b * 32 + lane % 32];
+            }
 #pragma unroll
             for (int a = 0; a < MI; ++a)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    tot[a][b][i] += rn * acc[a][b][i];
-                    acc[a][b][i] = 0.f;
-                }
+                for (int i = 0; i < 16; ++i) tot[a][b][i] += rn * acc[a][b][i];
         }
         __syncthreads();
     }
@@ -225,7 +251,7 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
 struct Plan {
     int bm, bn;
     int64_t q_pad, q_tiles;
-    size_t ub_bytes, partial_bytes;
+    size_t ub_bytes, partial_bytes, rn_bytes;
 };
 
 Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
@@ -237,6 +263,7 @@ Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
     p.q_tiles = p.q_pad / p.bm;
     p.ub_bytes = align256(size_t(p.q_pad) * Hkv * 128 * 2);
     p.partial_bytes = (Tq == 1) ? 0 : align256(size_t(p.q_tiles) * N * 4);
+    p.rn_bytes = (p.q_tiles > 1) ? align256(size_t(N) * Hkv * 4) : 0;   // norms computed once, shared by the query tiles
     return p;
 }
 
@@ -252,7 +279,7 @@ size_t route_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, in
     (void)Hq;
     if (!route_mfma_applicable(dt, B, Tq, Hkv, D)) return 0;
     const Plan p = plan_for(B, Tq, Hkv, N);
-    return p.ub_bytes + p.partial_bytes;
+    return p.ub_bytes + p.partial_bytes + p.rn_bytes;
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void* ws, hipStream_t st) {
@@ -260,6 +287,7 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
     const int64_t Q = a.B * a.Tq;
     uint16_t* Ub = static_cast<uint16_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
+    float* rn = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
     const int64_t n_real = Q * a.Hkv * 128, n_pad = p.q_pad * a.Hkv * 128;
     hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, n_real,
                        n_pad, Ub);
@@ -269,12 +297,27 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
     const dim3 grid(unsigned(ord.blocks));
     const float inv_hq = 1.f / float(a.Hq);
     const uint16_t* Kr = static_cast<const uint16_t*>(a.Krbar);
-    if (p.bm == 32)
-        hipLaunchKernelGGL((route_mfma_kernel<32, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
-                           inv_hq, c, partial, ord);
-    else
-        hipLaunchKernelGGL((route_mfma_kernel<128, 128>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv, a.Tq,
-                           inv_hq, c, partial, ord);
+    if (p.rn_bytes) {
+        const int64_t n_slices = a.N * a.Hkv;
+        hipLaunchKernelGGL(route_rnorm_kernel, dim3(unsigned(ceil_div(n_slices * 16, 256))), dim3(256), 0, st, Kr,
+                           n_slices, rn);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (p.bm == 32) {
+        if (p.rn_bytes)
+            hipLaunchKernelGGL((route_mfma_kernel<32, 128, true>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
+                               a.Tq, inv_hq, c, partial, ord, rn);
+        else
+            hipLaunchKernelGGL((route_mfma_kernel<32, 128, false>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
+                               a.Tq, inv_hq, c, partial, ord, rn);
+    } else {
+        if (p.rn_bytes)
+            hipLaunchKernelGGL((route_mfma_kernel<128, 128, true>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
+                               a.Tq, inv_hq, c, partial, ord, rn);
+        else
+            hipLaunchKernelGGL((route_mfma_kernel<128, 128, false>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
+                               a.Tq, inv_hq, c, partial, ord, rn);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.Tq > 1) {
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
