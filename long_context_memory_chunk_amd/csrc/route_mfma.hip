@@ -55,11 +55,11 @@ struct TileOrder {
     int64_t blocks;          // grid size (a multiple of kXcds * sq * sc)
 };
 
-__host__ __device__ inline TileOrder tile_order(int64_t tq, int64_t tn) {
+__host__ __device__ inline TileOrder tile_order(int64_t tq, int64_t tn, int sq_max = 8, int sc = 8) {
     TileOrder o;
     o.tq = tq; o.tn = tn;
-    o.sq = tq < 8 ? int(tq) : 8;
-    o.sc = 8;
+    o.sq = tq < sq_max ? int(tq) : sq_max;
+    o.sc = sc;
     o.n_sq = (tq + o.sq - 1) / o.sq;
     const int64_t n_super = o.n_sq * ((tn + o.sc - 1) / o.sc);
     o.blocks = ((n_super + kXcds - 1) / kXcds) * kXcds * o.sq * o.sc;
@@ -128,7 +128,15 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
 
     // ---- register prefetch of one head group's U and K̄r slices
     u32x4 ru[RU], rk[RK];
+    float rnv = 0.f;                                  // precomputed norm of chunk n0 + tid (tid < BN)
     auto fetch = [&](int g) {
+        if constexpr (PRE_RN) {
+            if (tid < BN) {
+                int64_t n = n0 + tid;
+                n = n < N ? n : N - 1;
+                rnv = rn_pre[n * hkv + g];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < RU; ++j) {
             const int r = tid / 16 + 16 * j;
@@ -146,6 +154,9 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
 
     for (int g = 0; g < hkv; ++g) {
         // ---- slices of group g to LDS; norms of the K̄r slices
+        if constexpr (PRE_RN) {
+            if (tid < BN) sRn[tid] = rnv;
+        }
 #pragma unroll
         for (int j = 0; j < RU; ++j)
             *reinterpret_cast<u32x4*>(sU + (tid / 16 + 16 * j) * kStride + c * 8) = ru[j];
@@ -187,14 +198,7 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
         // ---- scale by 1/|K̄r[n][g]| (one chunk column per lane) and accumulate
 #pragma unroll
         for (int b = 0; b < NI; ++b) {
-            float rn;
-            if constexpr (PRE_RN) {
-                int64_t n = n0 + wn * TN + b * 32 + lane % 32;
-                n = n < N ? n : N - 1;
-                rn = rn_pre[n * hkv + g];
-            } else {
-                rn = sRn[wn * TN + b * 32 + lane % 32];
-            }
+            const float rn = sRn[wn * TN + b * 32 + lane % 32];
 #pragma unroll
             for (int a = 0; a < MI; ++a)
 #pragma unroll
@@ -248,15 +252,205 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
     cout[i] = m;
 }
 
+// ---------------------------------------------------------------- prefill: one GEMM
+//
+// For a prefill query (Tq a multiple of 256) the scores are computed as one
+// bf16 GEMM over the full Hkv*128-wide contraction,
+//     s[q][n] = (1/Hq) U[q] . K̂[n],   K̂[n][g] = K̄r[n][g] / max(|K̄r[n][g]|, eps),
+// with K̂ rounded once to bf16 by route_khat_pack (a second rounding next to
+// U's; the score moves by at most 2^-9 + 2^-9 = 2^-8).  Both operands are first
+// written in a packed tile layout: for a 256-row tile and a 64-wide stage of the
+// contraction, one 32 KB block in which the 16-byte unit u of row r sits at
+// unit r*8 + (u ^ swz(r)).  route_gemm_kernel then copies each block into LDS
+// with direct global->LDS loads (lane i of a wave writes LDS base + 16 i, so a
+// contiguous copy reproduces the layout), two stages deep, and the XOR swizzle
+// makes the 32 rows of a matrix-core operand read hit distinct LDS banks.
+// A workgroup (4 waves, 2 x 2) owns 256 queries x 256 chunks; a wave owns
+// 128 x 128, 16 accumulator tiles of v_mfma_f32_32x32x16_bf16.  The epilogue
+// writes the tile's column maxima over its 256 tokens.
+
+constexpr int GB = 256;          // GEMM tile rows (queries and chunks)
+constexpr int GK = 64;           // contraction width of one stage
+constexpr int kUnitsPerStage = GB * GK / 8;   // 16-byte units of one operand stage (2048)
+
+__host__ __device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// U (fp32 [Q][K]) -> packed bf16 tiles; rows >= Q are zero.  One thread per unit.
+__global__ __launch_bounds__(256) void route_u_pack(const float* __restrict__ U, int64_t Q, int64_t q_pad, int K,
+                                                    u32x4* __restrict__ Up) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;        // unit index in row-major order
+    const int units_per_row = K / 8;
+    if (i >= q_pad * units_per_row) return;
+    const int64_t q = i / units_per_row;
+    const int ku = int(i % units_per_row);                             // unit along the contraction
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (q < Q) {
+        const float* src = U + q * K + ku * 8;
+        w = u32x4{pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]), pack_bf16x2(src[4], src[5]),
+                  pack_bf16x2(src[6], src[7])};
+    }
+    const int64_t tile = q / GB;
+    const int r = int(q % GB), st = ku / 8, u = ku % 8;
+    const int S = K / GK;
+    Up[(tile * S + st) * kUnitsPerStage + r * 8 + (u ^ swz(r))] = w;
+}
+
+// K̄r (bf16 [N][Hkv][128]) -> normalised, packed bf16 tiles of K̂; rows >= N are
+// zero.  16 lanes per 128-wide slice: the slice norm is reduced across them.
+__global__ __launch_bounds__(256) void route_khat_pack(const uint16_t* __restrict__ Kr, int64_t N, int64_t n_pad,
+                                                       int hkv, u32x4* __restrict__ Kp) {
+    const int64_t slice = (int64_t(blockIdx.x) * 256 + threadIdx.x) / 16;  // (n, g) in [0, n_pad * hkv)
+    const int c = threadIdx.x % 16;
+    if (slice >= n_pad * hkv) return;                                       // whole 16-lane groups
+    const int64_t n = slice / hkv;
+    const int g = int(slice % hkv);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kr + slice * 128 + c * 8));
+    float x[8];
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss = group_sum<16>(ss);
+    const float rn = __builtin_amdgcn_rsqf(fmaxf(ss, kEps * kEps));
+    const u32x4 w = {pack_bf16x2(x[0] * rn, x[1] * rn), pack_bf16x2(x[2] * rn, x[3] * rn),
+                     pack_bf16x2(x[4] * rn, x[5] * rn), pack_bf16x2(x[6] * rn, x[7] * rn)};
+    const int ku = g * 16 + c;                                               // unit along the contraction
+    const int64_t tile = n / GB;
+    const int r = int(n % GB), st = ku / 8, u = ku % 8;
+    const int S = hkv * 128 / GK;
+    Kp[(tile * S + st) * kUnitsPerStage + r * 8 + (u ^ swz(r))] = w;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restrict__ Up, const u32x4* __restrict__ Kp,
+                                                            int64_t N, int S, float inv_hq,
+                                                            float* __restrict__ partial, TileOrder ord) {
+    // two stages, each buffer its own object: the compiler then knows a copy into
+    // one stage does not alias reads of the other, and waits only where it must
+    __shared__ __attribute__((aligned(16))) u32x4 sA0[kUnitsPerStage];
+    __shared__ __attribute__((aligned(16))) u32x4 sB0[kUnitsPerStage];
+    __shared__ __attribute__((aligned(16))) u32x4 sA1[kUnitsPerStage];
+    __shared__ __attribute__((aligned(16))) u32x4 sB1[kUnitsPerStage];
+    __shared__ float sMax[2][GB];
+
+    const int64_t lin = blockIdx.x;
+    const int xcd = int(lin % kXcds);
+    const int64_t loc = lin / kXcds;
+    const int per = ord.sq * ord.sc;
+    const int64_t sup = (loc / per) * kXcds + xcd;
+    const int w = int(loc % per);
+    const int64_t qt = (sup % ord.n_sq) * ord.sq + w % ord.sq;
+    const int64_t ct = (sup / ord.n_sq) * ord.sc + w / ord.sq;
+    if (qt >= ord.tq || ct >= ord.tn) return;     // whole workgroup: padding of the grid
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / 2, wn = wave % 2;
+    const u32x4* Ag = Up + qt * int64_t(S) * kUnitsPerStage;
+    const u32x4* Bg = Kp + ct * int64_t(S) * kUnitsPerStage;
+
+    // one stage = 2 x 32 KB; a wave copies 8 + 8 contiguous 1 KB pieces
+    auto dma = [&](int st, u32x4* dA, u32x4* dB) {
+        const u32x4* a = Ag + int64_t(st) * kUnitsPerStage;
+        const u32x4* b = Bg + int64_t(st) * kUnitsPerStage;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int piece = (i * 4 + wave) * kWave;
+            __builtin_amdgcn_global_load_lds(a + piece + lane, (lds_ptr)(dA + piece), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(b + piece + lane, (lds_ptr)(dB + piece), 16, 0, 0);
+        }
+    };
+
+    // operand addresses (units) inside a stage: row r, unit (2 ks + lane/32) ^ swz(r)
+    int offA[4], offB[4], sw[8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int ra = wm * 128 + a * 32 + lane % 32;
+        const int rb = wn * 128 + a * 32 + lane % 32;
+        offA[a] = ra * 8;
+        offB[a] = rb * 8;
+        sw[a] = swz(ra) ^ (lane / 32);
+        sw[4 + a] = swz(rb) ^ (lane / 32);
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+    // Per stage: all 32 operand reads of the stage into registers first, then the
+    // copy of the next stage into the other buffer (so no LDS read waits behind
+    // that copy), then the 64 products, which cover the copy's latency.
+    dma(0, sA0, sB0);
+    for (int st = 0; st < S; ++st) {
+        const bool odd = st & 1;
+        const u32x4* cA = odd ? sA1 : sA0;
+        const u32x4* cB = odd ? sB1 : sB0;
+        __builtin_amdgcn_s_waitcnt(0);            // this wave's copies of stage st have landed
+        __syncthreads();                          // ... and every other wave's
+        bf16x8 fa[GK / 16][4], fb[GK / 16][4];
+#pragma unroll
+        for (int ks = 0; ks < GK / 16; ++ks)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                fa[ks][a] = __builtin_bit_cast(bf16x8, cA[offA[a] + ((2 * ks) ^ sw[a])]);
+                fb[ks][a] = __builtin_bit_cast(bf16x8, cB[offB[a] + ((2 * ks) ^ sw[4 + a])]);
+            }
+        if (st + 1 < S) dma(st + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);   // last read before the barrier
+#pragma unroll
+        for (int ks = 0; ks < GK / 16; ++ks)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][a], fb[ks][b], acc[a][b], 0, 0, 0);
+    }
+
+    // ---- epilogue: column maxima over the tile's 256 tokens
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane < 32) sMax[wm][wn * 128 + b * 32 + lane] = m;
+    }
+    __syncthreads();
+    const int64_t n = ct * GB + tid;
+    if (n < N) partial[qt * N + n] = fmaxf(sMax[0][tid], sMax[1][tid]) * inv_hq;
+}
+
 struct Plan {
+    bool gemm;
     int bm, bn;
-    int64_t q_pad, q_tiles;
-    size_t ub_bytes, partial_bytes, rn_bytes;
+    int64_t q_pad, q_tiles, n_pad;
+    size_t ub_bytes, partial_bytes, rn_bytes, kp_bytes;
 };
 
 Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
     Plan p;
     const int64_t Q = B * Tq;
+    p.gemm = (Tq % GB == 0);
+    if (p.gemm) {
+        p.bm = p.bn = GB;
+        p.q_pad = Q;
+        p.q_tiles = Q / GB;
+        p.n_pad = ceil_div(N, int64_t(GB)) * GB;
+        p.ub_bytes = align256(size_t(Q) * Hkv * 128 * 2);
+        p.kp_bytes = align256(size_t(p.n_pad) * Hkv * 128 * 2);
+        p.partial_bytes = align256(size_t(p.q_tiles) * N * 4);
+        p.rn_bytes = 0;
+        return p;
+    }
+    p.kp_bytes = 0;
+    p.n_pad = N;
     p.bm = (Tq == 1 && Q <= 32) ? 32 : 128;
     p.bn = 128;
     p.q_pad = ceil_div(Q, p.bm) * p.bm;
@@ -279,19 +473,38 @@ size_t route_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, in
     (void)Hq;
     if (!route_mfma_applicable(dt, B, Tq, Hkv, D)) return 0;
     const Plan p = plan_for(B, Tq, Hkv, N);
-    return p.ub_bytes + p.partial_bytes + p.rn_bytes;
+    return p.ub_bytes + p.partial_bytes + p.rn_bytes + p.kp_bytes;
 }
 
 hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void* ws, hipStream_t st) {
     const Plan p = plan_for(a.B, a.Tq, a.Hkv, a.N);
     const int64_t Q = a.B * a.Tq;
+    hipError_t err;
+    if (p.gemm) {
+        const int K = a.Hkv * 128, S = K / GK;
+        u32x4* Up = static_cast<u32x4*>(ws);
+        float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
+        u32x4* Kp = reinterpret_cast<u32x4*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
+        hipLaunchKernelGGL(route_u_pack, dim3(unsigned(ceil_div(Q * (K / 8), 256))), dim3(256), 0, st, U, Q, Q, K, Up);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(route_khat_pack, dim3(unsigned(ceil_div(p.n_pad * a.Hkv * 16, 256))), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.Krbar), a.N, p.n_pad, a.Hkv, Kp);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const TileOrder ord = tile_order(p.q_tiles, p.n_pad / GB, 4, 8);
+        hipLaunchKernelGGL(route_gemm_kernel, dim3(unsigned(ord.blocks)), dim3(256), 0, st, Up, Kp, a.N, S,
+                           1.f / float(a.Hq), partial, ord);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
+                           a.N, int(a.Tq / GB), a.B, c);
+        return hipGetLastError();
+    }
     uint16_t* Ub = static_cast<uint16_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
     float* rn = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
     const int64_t n_real = Q * a.Hkv * 128, n_pad = p.q_pad * a.Hkv * 128;
     hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, n_real,
                        n_pad, Ub);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     const TileOrder ord = tile_order(p.q_tiles, ceil_div(a.N, p.bn));
     const dim3 grid(unsigned(ord.blocks));

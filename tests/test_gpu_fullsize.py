@@ -16,7 +16,8 @@ from tests import workloads as W
 pytestmark = pytest.mark.gpu
 
 Hq, Hkv, D, C = 32, 8, 128, 64
-MFMA_TOL = 3e-3
+MFMA_TOL = 3e-3     # batched decode on the matrix cores: U rounded to bf16, |delta s| <= 2^-9
+GEMM_TOL = 5e-3     # prefill GEMM: U and the unit keys rounded to bf16, |delta s| <= 2^-8
 VALU_TOL = 1e-4
 
 
@@ -240,11 +241,11 @@ def test_prefill8k_10m_layer_sampled(env):
         if dd in pd:
             kb[i] = prow[dd][n - coff[dd]]
     c_s = oracle.chunk_scores(Qr64, W.widen(kb, "bf16"))[0]
-    assert np.max(np.abs(chn[samp] - c_s)) <= MFMA_TOL
+    assert np.max(np.abs(chn[samp] - c_s)) <= GEMM_TOL
     p_idx = np.concatenate([np.arange(coff[d], coff[d + 1]) for d in planted])
     p_rows = np.concatenate([prow[int(d)] for d in planted])
     c_p = oracle.chunk_scores(Qr64, W.widen(p_rows, "bf16"))[0]
-    assert np.max(np.abs(chn[p_idx] - c_p)) <= MFMA_TOL
+    assert np.max(np.abs(chn[p_idx] - c_p)) <= GEMM_TOL
     # the planted documents beat every sampled chunk by the margin
     D_p = oracle.doc_scores(c_p[None], np.concatenate([[0], np.cumsum(np.diff(coff)[planted])]))[0]
     assert D_p.min() - c_s[[i for i, n in enumerate(samp) if int(np.searchsorted(coff, n, side='right')) - 1 not in pd]].max() >= 0.05
