@@ -223,22 +223,278 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     if (tid < G) part_ml[(bt * Hq + g * G + tid) * P + p] = make_float2(s_m[tid], s_l[tid]);
 }
 
+// ---------------------------------------------------------------- bf16, d = 128
+//
+// attn_decode_kernel: the same key space and mask as attn_split_kernel, laid
+// out for HBM bandwidth.  A workgroup (4 waves) owns one chunk of CK keys of
+// one (b, i, kv head g) and the G query heads that read g.  16 lanes hold one
+// key: lane c of the 16 owns bytes 16c .. 16c+15 of the 256-byte row, so one
+// wave instruction reads four whole rows; a wave's KPW keys are its key slot
+// s = lane / 16 plus 4 it, it = 0 .. KPW/4 - 1.  Every K and V load of the
+// wave is issued first, so a wave keeps its whole share of the chunk in
+// flight.  A local key's RoPE pair (i, i + 64) sits in lanes c and c + 8 of
+// the same row of 16 lanes and is exchanged with DPP row_ror:8.  A lane's
+// local keys are 4 positions apart, so its cos/sin advance by the fixed
+// rotation of 4 positions (angle addition, from the context's table row 4),
+// seeded from the table at its first local key.  The G dot products are
+// summed over the 16 lanes with DPP; P.V uses the same layout, and the four
+// key slots of a wave and the four waves are summed at the end.  Each chunk
+// writes a partial (m, l, o) that attn_combine_kernel merges.
+
+__device__ __forceinline__ uint32_t ror8_16(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));   // row_ror:8
+}
+
+template <int G, int CK>
+__global__ __launch_bounds__(256, 3) void attn_decode_kernel(
+    const bf16_t* __restrict__ Q, int Tq, int Hq, int hkv, const bf16_t* __restrict__ KVmem,
+    const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows,
+    const bf16_t* __restrict__ Kl, const bf16_t* __restrict__ Vl, int L, int q_offset, float scale,
+    const float2* __restrict__ rope_cs, int max_pos, int P,
+    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    constexpr int D = 128;
+    constexpr int KPW = CK / 4;                  // keys per wave
+    constexpr int NIT = KPW / 4;                 // keys per lane
+    __shared__ float lg[G][CK];
+    __shared__ float red[4][G][D];
+    __shared__ float s_m[G], s_l[G];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int slot = lane / 16, c = lane % 16;
+    const float sgn = (c & 8) ? 1.f : -1.f;      // first half: x1 c - x2 s; second: x2 c + x1 s
+    const int p = blockIdx.x, g = blockIdx.y;
+    const int64_t bt = blockIdx.z;
+    const int64_t b = bt / Tq;
+    const int i = int(bt % Tq);
+
+    int64_t r0 = mem_off[b], r1 = mem_off[b + 1];
+    r0 = r0 < 0 ? 0 : (r0 > cap ? cap : r0);
+    r1 = r1 < r0 ? r0 : (r1 > cap ? cap : r1);
+    if (r1 - r0 > max_rows) r1 = r0 + max_rows;
+    const int64_t M = r1 - r0;
+    const int64_t total = M + int64_t(L - Tq) + i + 1;
+    const int64_t k0 = int64_t(p) * CK;
+    const int64_t row_elems = int64_t(hkv) * D;
+    const int64_t hrow = bt * Hq + int64_t(g) * G;   // first query head row of this group
+
+    if (k0 >= total) {                           // no keys here: an empty partial
+        for (int idx = tid; idx < G * D; idx += 256) part_o[((hrow + idx / D) * P + p) * D + idx % D] = 0.f;
+        if (tid < G) part_ml[(hrow + tid) * P + p] = make_float2(-INFINITY, 0.f);
+        return;
+    }
+
+    // ---- loads, in the order they are consumed (the vector-memory counter
+    // completes in issue order): the raw query rows, the cos/sin of the query,
+    // of this lane's first local key and of a 4-position step, then every K
+    // row, then every V row of this lane's keys.  Keys past the end load the
+    // last valid key (in bounds) and are masked afterwards.
+    const int64_t kbase = k0 + wave * KPW + slot;    // key of it = 0; key(it) = kbase + 4 it
+    u32x4 qw[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) qw[hh] = *reinterpret_cast<const u32x4*>(Q + (hrow + hh) * D + c * 8);
+    const int64_t first_local = (M > kbase) ? (M - kbase + 3) / 4 : 0;   // first it with key >= M
+    float2 cq[8], rot[8], step[8];
+    {
+        int pos_q = q_offset + (L - Tq) + i;
+        pos_q = pos_q < max_pos ? pos_q : max_pos - 1;
+        int pos = q_offset + int(kbase + 4 * first_local - M);
+        pos = pos < 0 ? 0 : (pos < max_pos ? pos : max_pos - 1);
+        const float2* cs_q = rope_cs + int64_t(pos_q) * (D / 2) + (c % 8) * 8;
+        const float2* cs = rope_cs + int64_t(pos) * (D / 2) + (c % 8) * 8;
+        const float2* st = rope_cs + int64_t(4 < max_pos ? 4 : max_pos - 1) * (D / 2) + (c % 8) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { cq[e] = cs_q[e]; rot[e] = cs[e]; step[e] = st[e]; }
+    }
+    u32x4 kw[NIT], vw[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        int64_t key = kbase + 4 * it;
+        key = key < total ? key : total - 1;
+        const bf16_t* ks = (key >= M) ? Kl + ((b * L + (key - M)) * hkv + g) * D
+                                      : KVmem + (r0 + key) * 2 * row_elems + int64_t(g) * D;
+        kw[it] = *reinterpret_cast<const u32x4*>(ks + c * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        int64_t key = kbase + 4 * it;
+        key = key < total ? key : total - 1;
+        const bf16_t* vs = (key >= M) ? Vl + ((b * L + (key - M)) * hkv + g) * D
+                                      : KVmem + (r0 + key) * 2 * row_elems + row_elems + int64_t(g) * D;
+        vw[it] = *reinterpret_cast<const u32x4*>(vs + c * 8);
+    }
+
+    // this lane's 8 elements of the G rotated, scaled query heads
+    float q[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const u32x4 w = qw[hh];
+        const u32x4 pw = {ror8_16(w[0]), ror8_16(w[1]), ror8_16(w[2]), ror8_16(w[3])};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+            const float px = (e & 1) ? bf16_hi(pw[e / 2]) : bf16_lo(pw[e / 2]);
+            q[hh][e] = (x * cq[e].x + sgn * px * cq[e].y) * scale;
+        }
+    }
+
+    // ---- logits
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int64_t key = kbase + 4 * it;
+        const bool valid = key < total;
+        const u32x4 w = kw[it];
+        const u32x4 pw = {ror8_16(w[0]), ror8_16(w[1]), ror8_16(w[2]), ror8_16(w[3])};
+        float y[8];
+        if (it > first_local) {                  // advance cos/sin by 4 positions
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 r = rot[e];
+                rot[e] = make_float2(r.x * step[e].x - r.y * step[e].y, r.y * step[e].x + r.x * step[e].y);
+            }
+        }
+        if (it >= first_local) {                 // local key: rotate
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+                const float px = (e & 1) ? bf16_hi(pw[e / 2]) : bf16_lo(pw[e / 2]);
+                y[e] = x * rot[e].x + sgn * px * rot[e].y;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+        }
+        const int kl = wave * KPW + 4 * it + slot;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += y[e] * q[hh][e];
+            d = group_sum<16>(d);
+            if (c == hh) lg[hh][kl] = valid ? d : -INFINITY;
+        }
+    }
+    __syncthreads();
+
+    // ---- softmax of the chunk per head (wave w owns heads w, w+4, ...)
+    for (int hh = wave; hh < G; hh += 4) {
+        float mx = -INFINITY;
+        for (int t = lane; t < CK; t += kWave) mx = fmaxf(mx, lg[hh][t]);
+        mx = wave_max(mx);
+        float sum = 0.f;
+        for (int t = lane; t < CK; t += kWave) {
+            const float e = (lg[hh][t] == -INFINITY) ? 0.f : expf(lg[hh][t] - mx);
+            lg[hh][t] = e;
+            sum += e;
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) { s_m[hh] = mx; s_l[hh] = sum; }
+    }
+    __syncthreads();
+
+    // ---- P.V in the same layout
+    float o[G][8];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int kl = wave * KPW + 4 * it + slot;
+        const u32x4 w = vw[it];                  // keys past the end have weight 0
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float pw = lg[hh][kl];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[hh][e] += pw * v[e];
+        }
+    }
+    // sum the four key slots of the wave (lanes c, c+16, c+32, c+48), then the waves
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = o[hh][e];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            o[hh][e] = v;
+        }
+    if (slot == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][hh][c * 8 + e] = o[hh][e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int hh = idx / D, dd = idx % D;
+        const float v = (red[0][hh][dd] + red[1][hh][dd]) + (red[2][hh][dd] + red[3][hh][dd]);
+        part_o[((hrow + hh) * P + p) * D + dd] = v;
+    }
+    if (tid < G) part_ml[(hrow + tid) * P + p] = make_float2(s_m[tid], s_l[tid]);
+}
+
+// Merges the P partial (m, l, o) of one output row: the partials' weights
+// exp(m_p - m) and the weighted row sums are computed in parallel (weights
+// kept in LDS), then each thread sums its dimension over the partials with
+// several loads in flight.
+constexpr int kMaxParts = 1024;
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml, int P,
                                                          T* __restrict__ O) {
+    __shared__ float s_w[kMaxParts];
+    __shared__ float s_red[2][D / 64];
     const int64_t row = blockIdx.x;   // (b, i, h)
     const int dd = threadIdx.x;
+    const int lane = dd % kWave, wave = dd / kWave;
     float m = -INFINITY;
-    for (int p = 0; p < P; ++p) m = fmaxf(m, part_ml[row * P + p].x);
-    float l = 0.f, acc = 0.f;
-    for (int p = 0; p < P; ++p) {
+    for (int p = dd; p < P; p += D) m = fmaxf(m, part_ml[row * P + p].x);
+    m = wave_max(m);
+    if (lane == 0) s_red[0][wave] = m;
+    __syncthreads();
+    m = s_red[0][0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) m = fmaxf(m, s_red[0][w]);
+    float l = 0.f;
+    for (int p = dd; p < P; p += D) {
         const float2 ml = part_ml[row * P + p];
         const float w = (ml.x == -INFINITY) ? 0.f : expf(ml.x - m);
+        s_w[p] = w;
         l += w * ml.y;
-        acc += w * part_o[(row * P + p) * D + dd];
     }
+    l = wave_sum(l);
+    if (lane == 0) s_red[1][wave] = l;
+    __syncthreads();
+    l = s_red[1][0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) l += s_red[1][w];
+    float acc = 0.f;
+    int p = 0;
+    for (; p + 4 <= P; p += 4) {
+        const float o0 = part_o[(row * P + p) * D + dd], o1 = part_o[(row * P + p + 1) * D + dd];
+        const float o2 = part_o[(row * P + p + 2) * D + dd], o3 = part_o[(row * P + p + 3) * D + dd];
+        acc += s_w[p] * o0;
+        acc += s_w[p + 1] * o1;
+        acc += s_w[p + 2] * o2;
+        acc += s_w[p + 3] * o3;
+    }
+    for (; p < P; ++p) acc += s_w[p] * part_o[(row * P + p) * D + dd];
     Elem<T>::store(O, row * D + dd, acc / l);
+}
+
+// Chunk size of attn_decode_kernel: 64 keys, so that a wave's loads (8 KB)
+// and the register budget of three waves per SIMD leave many workgroups
+// resident per CU, in different phases (load / compute).
+int decode_chunk(int64_t, int, int, int, int64_t, int, int) { return 64; }
+
+bool decode_applicable(msa_dtype dt, int D, int Hq, int Hkv, int64_t max_rows, int L) {
+    const int G = Hq / Hkv;
+    return dt == MSA_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8) &&
+           max_rows + L <= int64_t(64) * kMaxParts;        // at most kMaxParts partials per row
 }
 
 int attn_parts(int64_t B, int Tq, int Hkv, int64_t max_rows, int L, int num_cus) {
@@ -264,6 +520,33 @@ hipError_t launch_split_g(const AttnArgs& a, float* part_o, float2* part_ml, int
     return hipGetLastError();
 }
 
+template <int G, int CK>
+hipError_t launch_decode_g(const AttnArgs& a, float* part_o, float2* part_ml, int P, hipStream_t st) {
+    hipLaunchKernelGGL((attn_decode_kernel<G, CK>), dim3(unsigned(P), unsigned(a.Hkv), unsigned(a.B * a.Tq)),
+                       dim3(256), 0, st, static_cast<const bf16_t*>(a.Q), a.Tq, a.Hq, a.Hkv,
+                       static_cast<const bf16_t*>(a.KVmem), a.mem_off, a.mem_rows_cap, a.max_rows,
+                       static_cast<const bf16_t*>(a.K_local), static_cast<const bf16_t*>(a.V_local), a.L,
+                       a.q_offset, a.scale, a.rope_cs, a.max_pos, P, part_o, part_ml);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
+                       part_o, part_ml, P, static_cast<bf16_t*>(a.O));
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnArgs& a, float* part_o, float2* part_ml, int P, int ck, hipStream_t st) {
+    switch (a.Hq / a.Hkv) {
+        case 1: return ck == 128 ? launch_decode_g<1, 128>(a, part_o, part_ml, P, st)
+                                 : launch_decode_g<1, 64>(a, part_o, part_ml, P, st);
+        case 2: return ck == 128 ? launch_decode_g<2, 128>(a, part_o, part_ml, P, st)
+                                 : launch_decode_g<2, 64>(a, part_o, part_ml, P, st);
+        case 4: return ck == 128 ? launch_decode_g<4, 128>(a, part_o, part_ml, P, st)
+                                 : launch_decode_g<4, 64>(a, part_o, part_ml, P, st);
+        case 8: return launch_decode_g<8, 64>(a, part_o, part_ml, P, st);
+        default: return hipErrorNotSupported;
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_split(const AttnArgs& a, float* part_o, float2* part_ml, int P, hipStream_t st) {
     switch (a.Hq / a.Hkv) {
@@ -285,7 +568,9 @@ bool attn_supported_group(int Hq, int Hkv) {
 
 size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t max_rows,
                       int L, int num_cus) {
-    const int P = attn_parts(B, Tq, Hkv, max_rows, L, num_cus);
+    const int P = decode_applicable(dt, D, Hq, Hkv, max_rows, L)
+                      ? int(ceil_div(max_rows + L, int64_t(decode_chunk(B, Tq, Hq, Hkv, max_rows, L, num_cus))))
+                      : attn_parts(B, Tq, Hkv, max_rows, L, num_cus);
     const size_t rows = size_t(B) * Tq * Hq * P;
     size_t split = align256(rows * D * sizeof(float)) + align256(rows * sizeof(float2));
     size_t mf = attn_mfma_workspace(dt, B, Tq, Hq, Hkv, D, max_rows, L);
@@ -295,6 +580,14 @@ size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, i
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (a.B == 0 || a.Tq == 0) return hipSuccess;
     if (attn_mfma_applicable(a)) return launch_attn_mfma(a, st);
+    if (decode_applicable(a.dt, a.D, a.Hq, a.Hkv, a.max_rows, a.L)) {
+        const int ck = decode_chunk(a.B, a.Tq, a.Hq, a.Hkv, a.max_rows, a.L, a.num_cus);
+        const int P = int(ceil_div(a.max_rows + a.L, int64_t(ck)));
+        const size_t rows = size_t(a.B) * a.Tq * a.Hq * P;
+        float* part_o = static_cast<float*>(a.ws);
+        float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align256(rows * a.D * sizeof(float)));
+        return launch_decode(a, part_o, part_ml, P, ck, st);
+    }
     const int P = attn_parts(a.B, a.Tq, a.Hkv, a.max_rows, a.L, a.num_cus);
     const size_t rows = size_t(a.B) * a.Tq * a.Hq * P;
     float* part_o = static_cast<float*>(a.ws);

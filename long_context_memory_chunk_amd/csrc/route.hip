@@ -22,8 +22,11 @@
 //                         HBM-bound (1 flop per byte at B*Tq = 1).
 //   route_scan_generic    any dtype/shape: one thread per (query, chunk).
 //   topk_partial          per-wave document max (LDS segmented max over
-//                         coalesced chunk-score loads) + running top-k.
-//   topk_final            merges the per-wave candidates (16 waves, then one).
+//                         coalesced chunk-score loads): every document's key
+//                         bits and each wave's largest key.
+//   topk_final            the K-th largest wave maximum bounds the K-th key
+//                         from below; only the few waves that reach it are
+//                         searched for the top k.
 // The top-k key is 64 bits: order-preserving bits of the fp32 document
 // score above (0xFFFFFFFF - doc id), so a larger key is a better document
 // and equal scores order by lower id, a total order.
@@ -281,17 +284,25 @@ __device__ __forceinline__ float unorder32(uint32_t o) {
 
 // Wave w of query b owns documents [256 w, 256 w + 256).  It stages their
 // chunk offsets in LDS, streams the chunk scores of their span with
-// coalesced loads, finds each chunk's document by binary search in LDS and
-// takes an LDS atomic max on the order-preserving bits (max is exact and
-// order-independent, so the result is deterministic), then offers the
-// document scores to its running top-K.
+// coalesced loads, finds each chunk's document and takes an LDS atomic max on
+// the order-preserving bits (max is exact and order-independent, so the result
+// is deterministic), then writes every document's bits and the wave's largest
+// composite key.
+// A chunk's document: the wave marks each document's first chunk as a bit in
+// LDS; for a window of 64 chunks, the lane's document is the number of marks
+// at or before its chunk (a popcount of the window's 64-bit mask under the
+// lane mask, plus the marks of earlier windows) minus one.  A wave whose span
+// exceeds the bit array, or that holds an empty document (two documents would
+// share one mark), finds documents by binary search in the offsets instead.
 constexpr int kDocsPerWave = 256;
+constexpr int kBitWords = 1024;                  // marks for spans of up to 32768 chunks per wave
 
 __global__ __launch_bounds__(256) void topk_partial_kernel(
-    const float* __restrict__ c, int64_t N, const int64_t* __restrict__ off, int64_t n_docs, int K,
-    int waves_per_b, uint64_t* __restrict__ cand, float* __restrict__ out_doc) {
+    const float* __restrict__ c, int64_t N, const int64_t* __restrict__ off, int64_t n_docs,
+    int waves_per_b, uint32_t* __restrict__ dkey, uint64_t* __restrict__ wmax, float* __restrict__ out_doc) {
     __shared__ int64_t s_off[4][kDocsPerWave + 1];
     __shared__ uint32_t s_max[4][kDocsPerWave];
+    __shared__ uint32_t s_bits[4][kBitWords + 2];
     const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
     const int w = blockIdx.x * 4 + wv;
     const bool active = w < waves_per_b;
@@ -312,67 +323,185 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(
     }
     for (int j = lane; j < kDocsPerWave; j += kWave) s_max[wv][j] = 0u;
     __syncthreads();
+
+    const int64_t lo_bound = s_off[wv][0];
+    const int64_t c1 = s_off[wv][nd];
+    const int64_t span = c1 - lo_bound;
+    bool ok = span <= int64_t(kBitWords) * 32;
+    for (int j = lane; j < nd; j += kWave) ok = ok && (s_off[wv][j + 1] > s_off[wv][j]);
+    const bool marks = nd > 0 && __all(ok);
+    if (marks) {
+        const int words = int((span + 31) / 32) + 2;
+        for (int i = lane; i < words; i += kWave) s_bits[wv][i] = 0u;
+    }
+    __syncthreads();
+    if (marks) {
+        for (int j = lane; j < nd; j += kWave) {
+            const int t = int(s_off[wv][j] - lo_bound);
+            atomicOr(&s_bits[wv][t >> 5], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+
     if (nd > 0) {
-        int64_t lo_bound = s_off[wv][0];
-        const int64_t c1 = s_off[wv][nd];
         const float* cb = c + b * N;
-        for (int64_t n0 = lo_bound; n0 < c1; n0 += kWave) {
-            const int64_t n = n0 + lane;
-            if (n < c1) {
-                const float v = cb[n];
-                int lo = 0, hi = nd;                 // largest j with s_off[j] <= n
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_off[wv][mid] <= n) lo = mid; else hi = mid;
+        if (marks) {
+            const uint64_t le = (lane == 63) ? ~0ull : ((1ull << (lane + 1)) - 1);
+            int before = 0;                          // marks in earlier windows
+            constexpr int U = 32;                    // windows whose loads are in flight together
+            for (int64_t n0 = lo_bound; n0 < c1; n0 += kWave * U) {
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t n = n0 + u * kWave + lane;
+                    v[u] = (n < c1) ? cb[n] : 0.f;
                 }
-                atomicMax(&s_max[wv][lo], order32(v));
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t w0 = n0 + u * kWave;
+                    if (w0 >= c1) break;
+                    const int t0 = int(w0 - lo_bound);   // multiple of 64: the window is words t0/32, t0/32 + 1
+                    const uint64_t m = uint64_t(s_bits[wv][t0 >> 5]) | (uint64_t(s_bits[wv][(t0 >> 5) + 1]) << 32);
+                    const int doc = before + __popcll(m & le) - 1;
+                    before += __popcll(m);
+                    if (w0 + lane < c1) atomicMax(&s_max[wv][doc], order32(v[u]));
+                }
+            }
+        } else {
+            for (int64_t n0 = lo_bound; n0 < c1; n0 += kWave) {
+                const int64_t n = n0 + lane;
+                if (n < c1) {
+                    const float v = cb[n];
+                    int lo = 0, hi = nd;                 // largest j with s_off[j] <= n
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (s_off[wv][mid] <= n) lo = mid; else hi = mid;
+                    }
+                    atomicMax(&s_max[wv][lo], order32(v));
+                }
             }
         }
     }
     __syncthreads();
-    uint64_t best = 0;
-    for (int base = 0; base < nd; base += kWave) {
-        const int j = base + lane;
-        uint64_t key = 0;
-        if (j < nd && s_off[wv][j + 1] > s_off[wv][j]) {
-            const float m = unorder32(s_max[wv][j]);
-            if (out_doc) out_doc[b * n_docs + d0 + j] = m;
-            key = make_key(m, uint32_t(d0 + j));
-        }
-        best = wave_offer(best, key, K, lane);
+    // each document's order-preserving score bits (0: no chunks), and the
+    // largest composite key (score, then lowest id) of the wave
+    uint64_t wbest = 0;
+    for (int j = lane; j < nd; j += kWave) {
+        const bool has = s_off[wv][j + 1] > s_off[wv][j];
+        const uint32_t o = has ? s_max[wv][j] : 0u;
+        if (out_doc && has) out_doc[b * n_docs + d0 + j] = unorder32(o);
+        dkey[b * n_docs + d0 + j] = o;
+        const uint64_t key = has ? ((uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(d0 + j))) : 0;
+        wbest = key > wbest ? key : wbest;
     }
-    if (active && lane < K) cand[(b * waves_per_b + w) * K + lane] = best;
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) {
+        const uint64_t y = shfl_xor64(wbest, j);
+        wbest = y > wbest ? y : wbest;
+    }
+    if (active && lane == 0) wmax[b * waves_per_b + w] = wbest;
 }
 
-// 16 waves each reduce a slice of the candidates to their top K, then wave 0
-// merges the 16 lists held in LDS.
+// One workgroup per query.  The K largest wave maxima are K distinct
+// documents, so the K-th of them (thr) is at most the K-th largest key
+// overall: every top-K document has a key >= thr and lies in a wave whose
+// maximum is >= thr.  (a) 16 waves reduce the wave maxima to their top K and
+// a pairwise merge tree combines the 16 lists (thr); (b) the waves that reach thr are listed (usually a
+// few more than K) and their documents with keys >= thr are gathered in LDS;
+// (c) wave 0 offers those to its top K.  If ties make more documents qualify
+// than the buffers hold, wave 0 offers every document of every qualifying wave
+// instead (exact, slower).
 constexpr int kFinalWaves = 16;
+constexpr int kSelCap = 1024;
+constexpr int kMaxQual = 1024;
 
 __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
-    const uint64_t* __restrict__ cand, int64_t n_cand, int K, int32_t* __restrict__ ids,
-    float* __restrict__ scores) {
+    const uint32_t* __restrict__ dkey, int64_t n_docs, const uint64_t* __restrict__ wmax, int W, int K,
+    int32_t* __restrict__ ids, float* __restrict__ scores) {
     __shared__ uint64_t lists[kFinalWaves][64];
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    __shared__ uint64_t sel[kSelCap];
+    __shared__ int qual[kMaxQual];
+    __shared__ int s_count, s_nq;
+    __shared__ uint64_t s_thr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
     const int64_t b = blockIdx.x;
-    const uint64_t* cb = cand + b * n_cand;
-    const int64_t per = ((n_cand + kFinalWaves - 1) / kFinalWaves + kWave - 1) / kWave * kWave;
-    const int64_t c0 = wave * per;
-    const int64_t c1 = (c0 + per < n_cand) ? c0 + per : n_cand;
+    const uint64_t* wm = wmax + b * W;
+    const uint32_t* db = dkey + b * n_docs;
+
+    // (a) thr = the K-th largest wave maximum
+    const int per = ((W + kFinalWaves - 1) / kFinalWaves + kWave - 1) / kWave * kWave;
+    const int c0 = wave * per, c1 = (c0 + per < W) ? c0 + per : W;
     uint64_t best = 0;
-    for (int64_t base = c0; base < c1; base += kWave) {
-        const uint64_t key = (base + lane < c1) ? cb[base + lane] : 0;
-        best = wave_offer(best, key, K, lane);
-    }
+    for (int base = c0; base < c1; base += kWave)
+        best = wave_offer(best, (base + lane < c1) ? wm[base + lane] : 0, K, lane);
     lists[wave][lane] = (lane < K) ? best : 0;
+    if (tid == 0) { s_count = 0; s_nq = 0; }
     __syncthreads();
+    // pairwise merge tree of the 16 sorted lists (4 levels)
+#pragma unroll
+    for (int active = kFinalWaves / 2; active >= 1; active >>= 1) {
+        uint64_t m = 0;
+        if (wave < active) m = wave_merge_desc(lists[2 * wave][lane], lists[2 * wave + 1][lane], lane);
+        __syncthreads();
+        if (wave < active) lists[wave][lane] = (lane < K) ? m : 0;
+        __syncthreads();
+    }
+    if (tid == 0) s_thr = lists[0][K - 1];
+    __syncthreads();
+    const uint64_t thr = s_thr;
+
+    // (b) qualifying waves, then their documents at or above thr
+    for (int i = tid; i < W; i += kFinalWaves * 64) {
+        const uint64_t m = wm[i];
+        if (m != 0 && m >= thr) {
+            const int p = atomicAdd(&s_nq, 1);
+            if (p < kMaxQual) qual[p] = i;
+        }
+    }
+    __syncthreads();
+    const int nq = s_nq;
+    constexpr int kWavesPerPass = kFinalWaves * 64 / kDocsPerWave;
+    if (nq <= kMaxQual) {
+        for (int q0 = 0; q0 < nq; q0 += kWavesPerPass) {
+            const int q = q0 + tid / kDocsPerWave;
+            if (q < nq) {
+                const int64_t doc = int64_t(qual[q]) * kDocsPerWave + tid % kDocsPerWave;
+                if (doc < n_docs) {
+                    const uint32_t o = db[doc];
+                    const uint64_t key = (uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(doc));
+                    if (o != 0 && key >= thr) {
+                        const int p = atomicAdd(&s_count, 1);
+                        if (p < kSelCap) sel[p] = key;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int count = s_count;
     if (wave != 0) return;
+
+    // (c) the top K
     best = 0;
-    const int per_batch = kWave / K;                  // lists packed into one 64-key offer
-    for (int w0 = 0; w0 < kFinalWaves; w0 += per_batch) {
-        const int w = w0 + lane / K, e = lane % K;
-        const uint64_t key = (lane < per_batch * K && w < kFinalWaves) ? lists[w][e] : 0;
-        best = wave_offer(best, key, K, lane);
+    if (nq <= kMaxQual && count <= kSelCap) {
+        for (int base = 0; base < count; base += kWave)
+            best = wave_offer(best, (base + lane < count) ? sel[base + lane] : 0, K, lane);
+    } else {
+        for (int w = 0; w < W; ++w) {
+            const uint64_t m = wm[w];
+            if (m == 0 || m < thr) continue;
+            for (int j0 = 0; j0 < kDocsPerWave; j0 += kWave) {
+                const int64_t doc = int64_t(w) * kDocsPerWave + j0 + lane;
+                uint64_t key = 0;
+                if (doc < n_docs) {
+                    const uint32_t o = db[doc];
+                    if (o != 0) key = (uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(doc));
+                }
+                best = wave_offer(best, key, K, lane);
+            }
+        }
     }
     if (lane < K) {
         ids[b * K + lane] = int32_t(0xFFFFFFFFu - uint32_t(best));
@@ -386,7 +515,7 @@ int topk_waves(int64_t n_docs) {
 }
 
 struct RouteWs {
-    size_t u_off, c_off, cand_off, mfma_off, total;
+    size_t u_off, c_off, dkey_off, wmax_off, mfma_off, total;
 };
 
 RouteWs route_ws_layout(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,
@@ -396,7 +525,8 @@ RouteWs route_ws_layout(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
     size_t o = 0;
     w.u_off = o;   o += align256(size_t(nq) * Hkv * D * sizeof(float));
     w.c_off = o;   o += align256(size_t(B) * N * sizeof(float));
-    w.cand_off = o; o += align256(size_t(B) * topk_waves(n_docs) * top_k * sizeof(uint64_t));
+    w.dkey_off = o; o += align256(size_t(B) * n_docs * sizeof(uint32_t));
+    w.wmax_off = o; o += align256(size_t(B) * topk_waves(n_docs) * sizeof(uint64_t));
     w.mfma_off = o; o += align256(route_mfma_workspace(dt, B, Tq, Hq, Hkv, D, N, num_cus));
     w.total = o;
     return w;
@@ -448,7 +578,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     char* ws = static_cast<char*>(a.ws);
     float* U = reinterpret_cast<float*>(ws + w.u_off);
     float* c = a.out_chunk ? a.out_chunk : reinterpret_cast<float*>(ws + w.c_off);
-    uint64_t* cand = reinterpret_cast<uint64_t*>(ws + w.cand_off);
+    uint32_t* dkey = reinterpret_cast<uint32_t*>(ws + w.dkey_off);
+    uint64_t* wmax = reinterpret_cast<uint64_t*>(ws + w.wmax_off);
     const int64_t nq = a.B * a.Tq;
     hipError_t err;
 
@@ -496,10 +627,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     // 3. document max + top-k
     const int wpb = topk_waves(a.n_docs);
     hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
-                       0, st, c, a.N, a.chunk_off, a.n_docs, a.top_k, wpb, cand, a.out_doc);
+                       0, st, c, a.N, a.chunk_off, a.n_docs, wpb, dkey, wmax, a.out_doc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalWaves * 64), 0, st, cand,
-                       int64_t(wpb) * a.top_k, a.top_k, a.out_ids, a.out_scores);
+    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalWaves * 64), 0, st, dkey,
+                       a.n_docs, wmax, wpb, a.top_k, a.out_ids, a.out_scores);
     return hipGetLastError();
 }
 

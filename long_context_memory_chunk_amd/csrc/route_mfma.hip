@@ -22,6 +22,8 @@
 // Epilogue: Tq = 1 -> each row is its own query, scores are written; Tq a
 // multiple of BM -> the tile's column maxima over its BM tokens are written
 // to a partial array and route_mfma_tokmax takes the max over a query's tiles.
+#include <type_traits>
+
 #include "route_mfma.hpp"
 
 namespace msa {
@@ -270,10 +272,14 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
 // writes the tile's column maxima over its 256 tokens.
 
 constexpr int GB = 256;          // GEMM tile rows (queries and chunks)
-constexpr int GK = 64;           // contraction width of one stage
-constexpr int kUnitsPerStage = GB * GK / 8;   // 16-byte units of one operand stage (2048)
+constexpr int GK = 32;           // contraction width of one stage
+constexpr int GU = GK / 8;       // 16-byte units per row of a stage
+constexpr int kUnitsPerStage = GB * GU;       // 16-byte units of one operand stage (1024 = 16 KB)
+constexpr int kStages = 4;       // stages in LDS: three copies in flight behind the one in use
 
-__host__ __device__ inline int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Row r's unit u sits at unit r*GU + (u ^ swz(r)): the 16 (or 8) rows that one
+// LDS cycle serves for a 16-byte operand read then fall in distinct banks.
+__host__ __device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // U (fp32 [Q][K]) -> packed bf16 tiles; rows >= Q are zero.  One thread per unit.
 __global__ __launch_bounds__(256) void route_u_pack(const float* __restrict__ U, int64_t Q, int64_t q_pad, int K,
@@ -290,9 +296,9 @@ __global__ __launch_bounds__(256) void route_u_pack(const float* __restrict__ U,
                   pack_bf16x2(src[6], src[7])};
     }
     const int64_t tile = q / GB;
-    const int r = int(q % GB), st = ku / 8, u = ku % 8;
+    const int r = int(q % GB), st = ku / GU, u = ku % GU;
     const int S = K / GK;
-    Up[(tile * S + st) * kUnitsPerStage + r * 8 + (u ^ swz(r))] = w;
+    Up[(tile * S + st) * kUnitsPerStage + r * GU + (u ^ swz(r))] = w;
 }
 
 // K̄r (bf16 [N][Hkv][128]) -> normalised, packed bf16 tiles of K̂; rows >= N are
@@ -318,22 +324,31 @@ __global__ __launch_bounds__(256) void route_khat_pack(const uint16_t* __restric
                      pack_bf16x2(x[4] * rn, x[5] * rn), pack_bf16x2(x[6] * rn, x[7] * rn)};
     const int ku = g * 16 + c;                                               // unit along the contraction
     const int64_t tile = n / GB;
-    const int r = int(n % GB), st = ku / 8, u = ku % 8;
+    const int r = int(n % GB), st = ku / GU, u = ku % GU;
     const int S = hkv * 128 / GK;
-    Kp[(tile * S + st) * kUnitsPerStage + r * 8 + (u ^ swz(r))] = w;
+    Kp[(tile * S + st) * kUnitsPerStage + r * GU + (u ^ swz(r))] = w;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// One 16-byte direct global->LDS copy per lane: lane i's 16 bytes land at LDS
+// byte address lds + 16 i (lds wave-uniform).  Written as asm so that the only
+// waits on these copies are the explicit ones below (the compiler would
+// otherwise make every LDS read wait for every copy in flight); the copy has no
+// register result.
+__device__ __forceinline__ void lds_copy16(const u32x4* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory count limited (expcnt and lgkmcnt left
+// at their maxima): GFX9 encoding, vmcnt in bits [3:0] and [15:14].
+#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
 __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restrict__ Up, const u32x4* __restrict__ Kp,
                                                             int64_t N, int S, float inv_hq,
                                                             float* __restrict__ partial, TileOrder ord) {
-    // two stages, each buffer its own object: the compiler then knows a copy into
-    // one stage does not alias reads of the other, and waits only where it must
-    __shared__ __attribute__((aligned(16))) u32x4 sA0[kUnitsPerStage];
-    __shared__ __attribute__((aligned(16))) u32x4 sB0[kUnitsPerStage];
-    __shared__ __attribute__((aligned(16))) u32x4 sA1[kUnitsPerStage];
-    __shared__ __attribute__((aligned(16))) u32x4 sB1[kUnitsPerStage];
+    __shared__ __attribute__((aligned(16))) u32x4 sA[kStages * kUnitsPerStage];
+    __shared__ __attribute__((aligned(16))) u32x4 sB[kStages * kUnitsPerStage];
     __shared__ float sMax[2][GB];
 
     const int64_t lin = blockIdx.x;
@@ -350,16 +365,19 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
     const int wm = wave / 2, wn = wave % 2;
     const u32x4* Ag = Up + qt * int64_t(S) * kUnitsPerStage;
     const u32x4* Bg = Kp + ct * int64_t(S) * kUnitsPerStage;
+    const uint32_t ldsA = uint32_t(size_t((lds_ptr)sA)), ldsB = uint32_t(size_t((lds_ptr)sB));
 
-    // one stage = 2 x 32 KB; a wave copies 8 + 8 contiguous 1 KB pieces
-    auto dma = [&](int st, u32x4* dA, u32x4* dB) {
+    // one stage = 2 x 16 KB; a wave copies 4 + 4 contiguous 1 KB pieces (8 copies)
+    constexpr int kCopies = 8;
+    auto dma = [&](int st) {
         const u32x4* a = Ag + int64_t(st) * kUnitsPerStage;
         const u32x4* b = Bg + int64_t(st) * kUnitsPerStage;
+        const uint32_t buf = uint32_t(st % kStages) * kUnitsPerStage;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kCopies / 2; ++i) {
             const int piece = (i * 4 + wave) * kWave;
-            __builtin_amdgcn_global_load_lds(a + piece + lane, (lds_ptr)(dA + piece), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(b + piece + lane, (lds_ptr)(dB + piece), 16, 0, 0);
+            lds_copy16(a + piece + lane, __builtin_amdgcn_readfirstlane(ldsA + (buf + piece) * 16));
+            lds_copy16(b + piece + lane, __builtin_amdgcn_readfirstlane(ldsB + (buf + piece) * 16));
         }
     };
 
@@ -369,8 +387,8 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
     for (int a = 0; a < 4; ++a) {
         const int ra = wm * 128 + a * 32 + lane % 32;
         const int rb = wn * 128 + a * 32 + lane % 32;
-        offA[a] = ra * 8;
-        offB[a] = rb * 8;
+        offA[a] = ra * GU;
+        offB[a] = rb * GU;
         sw[a] = swz(ra) ^ (lane / 32);
         sw[4 + a] = swz(rb) ^ (lane / 32);
     }
@@ -383,37 +401,58 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    // Per stage: all 32 operand reads of the stage into registers first, then the
-    // copy of the next stage into the other buffer (so no LDS read waits behind
-    // that copy), then the 64 products, which cover the copy's latency.
-    dma(0, sA0, sB0);
+    // Software pipeline over the 16-deep k-steps (two per stage), operands of
+    // one k-step ahead in registers (F0 / F1).  Stage st:
+    //   k-step (st, 0) from F0, while (st, 1) is read into F1 (buffer st);
+    //   wait for stage st + 1's copies (only stage st + 2's may remain in
+    //   flight), barrier;
+    //   k-step (st, 1) from F1, while (st + 1, 0) is read into F0 and stage
+    //   st + 3 is copied into the buffer of stage st - 1, last read during
+    //   k-step (st - 1, 0), before the previous barrier.
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    auto read_ks = [&](int st, int ks, bf16x8* xa, bf16x8* xb) {
+        const u32x4* cA = sA + (st % kStages) * kUnitsPerStage;
+        const u32x4* cB = sB + (st % kStages) * kUnitsPerStage;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            xa[a] = __builtin_bit_cast(bf16x8, cA[offA[a] + ((2 * ks) ^ sw[a])]);
+            xb[a] = __builtin_bit_cast(bf16x8, cB[offB[a] + ((2 * ks) ^ sw[4 + a])]);
+        }
+    };
+    auto mma_half = [&](const bf16x8* xa, const bf16x8* xb, int a0_) {
+#pragma unroll
+        for (int a = a0_; a < a0_ + 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], xb[b], acc[a][b], 0, 0, 0);
+    };
+
+    for (int st = 0; st < kStages - 1 && st < S; ++st) dma(st);
+    if (S > 2) MSA_WAIT_VMCNT(2 * kCopies); else if (S > 1) MSA_WAIT_VMCNT(kCopies); else MSA_WAIT_VMCNT(0);
+    __syncthreads();
+    read_ks(0, 0, a0, b0);
+
     for (int st = 0; st < S; ++st) {
-        const bool odd = st & 1;
-        const u32x4* cA = odd ? sA1 : sA0;
-        const u32x4* cB = odd ? sB1 : sB0;
-        __builtin_amdgcn_s_waitcnt(0);            // this wave's copies of stage st have landed
-        __syncthreads();                          // ... and every other wave's
-        bf16x8 fa[GK / 16][4], fb[GK / 16][4];
-#pragma unroll
-        for (int ks = 0; ks < GK / 16; ++ks)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                fa[ks][a] = __builtin_bit_cast(bf16x8, cA[offA[a] + ((2 * ks) ^ sw[a])]);
-                fb[ks][a] = __builtin_bit_cast(bf16x8, cB[offB[a] + ((2 * ks) ^ sw[4 + a])]);
-            }
-        if (st + 1 < S) dma(st + 1, odd ? sA0 : sA1, odd ? sB0 : sB1);   // last read before the barrier
-#pragma unroll
-        for (int ks = 0; ks < GK / 16; ++ks)
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][a], fb[ks][b], acc[a][b], 0, 0, 0);
+        const bool more = st + 1 < S;
+        mma_half(a0, b0, 0);
+        read_ks(st, 1, a1, b1);
+        mma_half(a0, b0, 2);
+        if (more) {
+            if (st + 2 < S) MSA_WAIT_VMCNT(kCopies); else MSA_WAIT_VMCNT(0);
+            __syncthreads();
+        }
+        mma_half(a1, b1, 0);
+        if (more) read_ks(st + 1, 0, a0, b0);
+        if (st + kStages - 1 < S) dma(st + kStages - 1);
+        mma_half(a1, b1, 2);
     }
 
-    // ---- epilogue: column maxima over the tile's 256 tokens
+    // ---- epilogue: column maxima over the tile's 256 tokens (one accumulator
+    // column block at a time: the scheduler barrier keeps the reads of the
+    // accumulation registers from being hoisted all at once)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+        __builtin_amdgcn_sched_barrier(0);
         float m = -INFINITY;
 #pragma unroll
         for (int a = 0; a < 4; ++a)

@@ -254,6 +254,51 @@ def test_route_ties_go_to_lowest_id(torch_mod, msa, ctx128):
     assert ids[0].tolist() == [1, 4, 6]
 
 
+def test_route_long_document_spans(torch_mod, msa, ctx128):
+    """A wave of 256 documents spanning more chunks than the document-start
+    marks cover (256 x 150 chunks) finds documents by binary search; the next
+    wave uses the marks.  16 planted documents over both waves come back."""
+    Hq, Hkv, d, k = 32, 8, 128, 16
+    counts = np.concatenate([np.full(256, 150), np.random.default_rng(71).integers(1, 20, size=44)])
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank("bf16", N, Hkv, d, 72)
+    Qr = msa_synth.normal_bf16(73, 4, (1, 1, Hq, d))
+    q = msa_synth.bf16_bits_to_f32(Qr)[0, 0]
+    planted = np.array([0, 3, 77, 128, 200, 254, 255, 256, 257, 260, 270, 280, 290, 297, 298, 299])
+    for j, doc in enumerate(planted):
+        Kb[coff[doc]:coff[doc + 1]] = msa_synth.planted_rows(74, 100 + j, q, Hkv, int(counts[doc]))
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, k, "bf16")
+    ids_ref, sc_ref, c_ref, D_ref = oracle.route(W.widen(Qr, "bf16"), W.widen(Kb, "bf16"), coff, k)
+    assert sorted(ids[0].tolist()) == sorted(ids_ref[0].tolist()) == planted.tolist()
+    assert np.max(np.abs(dc - D_ref)) <= SCORE_TOL
+
+
+def test_route_many_qualifying_candidates(torch_mod, msa, ctx128):
+    """25,600 one-chunk documents: wave 0 holds 16 documents at cosine ~0.8 and
+    waves 1..99 hold 15 documents each on the query's own direction (bit-
+    identical rows, so their scores tie exactly).  Every wave list's 16th key
+    is then at most wave 0's, and ~1,500 candidates reach that threshold: the
+    final selection takes its full-merge path.  Ties go to the lowest ids."""
+    Hq, Hkv, d, k = 32, 8, 128, 16
+    n_docs = 25600
+    coff = np.arange(n_docs + 1, dtype=np.int64)
+    Kb = _bank("bf16", n_docs, Hkv, d, 81)
+    hi = msa_synth.normal_bf16(82, 1, (Hkv, d))
+    Qr = np.stack([hi[h // (Hq // Hkv)] for h in range(Hq)])[None, None]
+    mid_f = 0.8 * msa_synth.bf16_bits_to_f32(hi) + 0.6 * msa_synth.normal_f32(82, 2, (Hkv, d))
+    mid = msa_synth.f32_to_bf16_bits(mid_f)
+    for doc in range(10, 26):
+        Kb[doc] = mid
+    for w in range(1, 100):
+        for doc in range(256 * w + 5, 256 * w + 20):
+            Kb[doc] = hi
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, k, "bf16")
+    ids_ref, sc_ref, c_ref, D_ref = oracle.route(W.widen(Qr, "bf16"), W.widen(Kb, "bf16"), coff, k)
+    expect = list(range(261, 276)) + [517]
+    assert ids[0].tolist() == ids_ref[0].tolist() == expect
+
+
 def test_route_is_deterministic(torch_mod, msa, ctx128):
     counts = np.random.default_rng(5).integers(1, 9, size=400)
     coff = msa_synth.prefix_offsets(counts)
