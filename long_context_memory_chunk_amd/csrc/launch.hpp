@@ -28,12 +28,17 @@ struct RouteArgs {
     void* ws;
     size_t ws_bytes;
     int num_cus;
-    hipEvent_t prof_start, prof_stop;   // recorded around the chunk-score kernel if set
+    hipEvent_t prof_start, prof_stop;   // recorded around the main chunk-score kernel if set
 };
 
 size_t route_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N,
                        int64_t n_docs, int top_k, int num_cus);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+// Records an optional profiling event (NULL: nothing to do).
+inline hipError_t record_if(hipEvent_t e, hipStream_t st) {
+    return e ? hipEventRecord(e, st) : hipSuccess;
+}
 
 struct AttnArgs {
     msa_dtype dt;

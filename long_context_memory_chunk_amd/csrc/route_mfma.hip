@@ -530,9 +530,11 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                            static_cast<const uint16_t*>(a.Krbar), a.N, p.n_pad, a.Hkv, Kp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const TileOrder ord = tile_order(p.q_tiles, p.n_pad / GB, 4, 8);
+        if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
         hipLaunchKernelGGL(route_gemm_kernel, dim3(unsigned(ord.blocks)), dim3(256), 0, st, Up, Kp, a.N, S,
                            1.f / float(a.Hq), partial, ord);
         if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
                            a.N, int(a.Tq / GB), a.B, c);
         return hipGetLastError();
@@ -555,6 +557,7 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                            n_slices, rn);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
     if (p.bm == 32) {
         if (p.rn_bytes)
             hipLaunchKernelGGL((route_mfma_kernel<32, 128, true>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
@@ -571,6 +574,7 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                                a.Tq, inv_hq, c, partial, ord, rn);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
     if (a.Tq > 1) {
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
                            a.N, int(a.Tq / p.bm), a.B, c);
