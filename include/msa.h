@@ -178,11 +178,15 @@ msa_status msa_route(msa_ctx* ctx, msa_dtype dt,
 
 /*
  * msa_route_time_next -- profiling aid, synchronous.  The next msa_route call
- * on this context records `start` on its stream immediately before its
- * chunk-score kernel and `stop` immediately after it, then forgets both, so
- * hipEventElapsedTime(start, stop) is that kernel's duration.  Both must be
- * events created on the context's device (or both NULL, which clears).  Not
- * for concurrent use of one context from several threads.
+ * on this context has its main chunk-score kernel (the streaming scan, the
+ * generic scan, or the matrix-core contraction; not the packing or top-k
+ * kernels around it) record `start` when it begins and `stop` when it ends,
+ * as part of that kernel's own dispatch, then forgets both; so
+ * hipEventElapsedTime(start, stop) is that kernel's duration and timing adds
+ * no gap between kernels.  With an empty bank (N = 0) both are recorded back
+ * to back.  Both must be events created with timing enabled on the context's
+ * device (or both NULL, which clears).  Not for concurrent use of one context
+ * from several threads.
  */
 msa_status msa_route_time_next(msa_ctx* ctx, hipEvent_t start, hipEvent_t stop);
 

@@ -11,6 +11,16 @@
 // (L - Tq) + i (causal), rotated here at position q_offset + j.  The query is
 // rotated at q_offset + (L - Tq) + i.
 //
+// Three kernels compute it; launch_attn takes the first that applies:
+//   attn_prefill_kernel (attn_mfma.hip)  bf16, d = 128, long query blocks:
+//                                        matrix cores.
+//   attn_decode_kernel (below)           bf16, d = 128, G in {1, 2, 4, 8}:
+//                                        decode and short queries, laid out
+//                                        for HBM bandwidth.
+//   attn_split_kernel                    any dtype, d in {64, 128}, any G.
+// The last two write partial (m, l, o) per key split; attn_combine merges
+// them exactly.
+//
 // attn_split (vector ALU, any Tq): a workgroup owns one (b, i, kv head g) and
 // the G = Hq/Hkv query heads that read g, so every key row loaded is used G
 // times.  Keys are taken 256 at a time: one key per thread for the logits,
@@ -18,8 +28,7 @@
 // coalesced wave access (D/64 elements per lane) and accumulating all G
 // heads in registers; an online softmax runs across the 256-key splits the
 // workgroup owns, and the four waves' partial sums meet in LDS at the end.
-// Splits are dealt to P workgroups; attn_combine merges the P partial
-// (m, l, o) exactly.
+// Splits are dealt to P workgroups.
 #include "common.hpp"
 #include "launch.hpp"
 #include "attn_mfma.hpp"

@@ -2,6 +2,8 @@
 // its launches; argument validation happens in api.hip before these run.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace msa {
@@ -38,6 +40,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 // Records an optional profiling event (NULL: nothing to do).
 inline hipError_t record_if(hipEvent_t e, hipStream_t st) {
     return e ? hipEventRecord(e, st) : hipSuccess;
+}
+
+// Launches a kernel with optional profiling events that the dispatch itself
+// records at the kernel's start and end (both NULL: a plain launch), so timing
+// a kernel puts no extra packet, and no gap, between it and its neighbours.
+template <typename F, typename... Args>
+hipError_t launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t start, hipEvent_t stop,
+                        Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, start, stop, 0, args...);
+    return hipGetLastError();
 }
 
 struct AttnArgs {

@@ -388,18 +388,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     // 1. unit-query group sums
     if ((err = launch_route_prep(a, U, st)) != hipSuccess) return err;
 
-    // 2. chunk scores c[B][N]; the matrix-core path records the profiling
-    // events around its GEMM itself, the VALU scans are one kernel each
-    if (route_mfma_applicable(a.dt, a.B, a.Tq, a.Hkv, a.D) && !route_scan_fast_applicable(a) && a.N > 0) {
+    // 2. chunk scores c[B][N]; the chunk-score kernel's dispatch records the
+    // profiling events itself (an empty bank records them back to back)
+    if (a.N == 0) {
+        if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
+        if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
+    } else if (route_scan_fast_applicable(a)) {
+        if ((err = launch_route_scan_fast(a, U, c, st)) != hipSuccess) return err;
+    } else if (route_mfma_applicable(a.dt, a.B, a.Tq, a.Hkv, a.D)) {
         if ((err = launch_route_mfma(a, U, c, ws + w.mfma_off, st)) != hipSuccess) return err;
     } else {
-        if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
-        if (a.N > 0) {
-            err = route_scan_fast_applicable(a) ? launch_route_scan_fast(a, U, c, st)
-                                                : launch_route_scan_generic(a, U, c, st);
-            if (err != hipSuccess) return err;
-        }
-        if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
+        if ((err = launch_route_scan_generic(a, U, c, st)) != hipSuccess) return err;
     }
 
     // 3. document max + top-k

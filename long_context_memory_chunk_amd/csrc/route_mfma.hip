@@ -1,6 +1,7 @@
 // Stage 2a on the matrix cores: routing scores as a dense contraction, for
-// batched decode (B*Tq > 4, Tq = 1) and multi-token query prefill (Tq a
-// multiple of 128).
+// batched decode (B*Tq > 4) and multi-token query prefill.  Two kernels:
+// route_mfma_kernel (below) for decode batches and short query blocks, and the
+// one-GEMM path (route_gemm_kernel, further down) for Tq a multiple of 256.
 //
 // Source: news.neo-ai.one MSA article, 全体設計 › アーキテクチャ (Fig. 2):
 // cosine similarity of Qr with K̄r, averaged over heads, maximised over
@@ -261,15 +262,18 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
 //     s[q][n] = (1/Hq) U[q] . K̂[n],   K̂[n][g] = K̄r[n][g] / max(|K̄r[n][g]|, eps),
 // with K̂ rounded once to bf16 by route_khat_pack (a second rounding next to
 // U's; the score moves by at most 2^-9 + 2^-9 = 2^-8).  Both operands are first
-// written in a packed tile layout: for a 256-row tile and a 64-wide stage of the
-// contraction, one 32 KB block in which the 16-byte unit u of row r sits at
-// unit r*8 + (u ^ swz(r)).  route_gemm_kernel then copies each block into LDS
+// written in a packed tile layout: for a 256-row tile and a 32-wide stage of the
+// contraction, one 16 KB block in which the 16-byte unit u of row r sits at
+// unit r*4 + (u ^ swz(r)).  route_gemm_kernel then copies each block into LDS
 // with direct global->LDS loads (lane i of a wave writes LDS base + 16 i, so a
-// contiguous copy reproduces the layout), two stages deep, and the XOR swizzle
-// makes the 32 rows of a matrix-core operand read hit distinct LDS banks.
-// A workgroup (4 waves, 2 x 2) owns 256 queries x 256 chunks; a wave owns
-// 128 x 128, 16 accumulator tiles of v_mfma_f32_32x32x16_bf16.  The epilogue
-// writes the tile's column maxima over its 256 tokens.
+// contiguous copy reproduces the layout) into a ring of four stages, three
+// copies in flight behind the stage in use, and the XOR swizzle makes the rows
+// of a matrix-core operand read hit distinct LDS banks.  A workgroup (4 waves,
+// 2 x 2) owns 256 queries x 256 chunks; a wave owns 128 x 128, 16 accumulator
+// tiles of v_mfma_f32_32x32x16_bf16.  Each stage is two k-steps of 16; the
+// operands of the next k-step are read from LDS while the matrix cores work on
+// the current one.  The epilogue writes the tile's column maxima over its 256
+// tokens.
 
 constexpr int GB = 256;          // GEMM tile rows (queries and chunks)
 constexpr int GK = 32;           // contraction width of one stage
@@ -530,11 +534,10 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                            static_cast<const uint16_t*>(a.Krbar), a.N, p.n_pad, a.Hkv, Kp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const TileOrder ord = tile_order(p.q_tiles, p.n_pad / GB, 4, 8);
-        if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
-        hipLaunchKernelGGL(route_gemm_kernel, dim3(unsigned(ord.blocks)), dim3(256), 0, st, Up, Kp, a.N, S,
+        err = launch_timed(route_gemm_kernel, dim3(unsigned(ord.blocks)), dim3(256), st, a.prof_start, a.prof_stop,
+                           static_cast<const u32x4*>(Up), static_cast<const u32x4*>(Kp), a.N, S,
                            1.f / float(a.Hq), partial, ord);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
+        if (err != hipSuccess) return err;
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
                            a.N, int(a.Tq / GB), a.B, c);
         return hipGetLastError();
@@ -557,24 +560,19 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
                            n_slices, rn);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if ((err = record_if(a.prof_start, st)) != hipSuccess) return err;
-    if (p.bm == 32) {
-        if (p.rn_bytes)
-            hipLaunchKernelGGL((route_mfma_kernel<32, 128, true>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
-                               a.Tq, inv_hq, c, partial, ord, rn);
-        else
-            hipLaunchKernelGGL((route_mfma_kernel<32, 128, false>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
-                               a.Tq, inv_hq, c, partial, ord, rn);
-    } else {
-        if (p.rn_bytes)
-            hipLaunchKernelGGL((route_mfma_kernel<128, 128, true>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
-                               a.Tq, inv_hq, c, partial, ord, rn);
-        else
-            hipLaunchKernelGGL((route_mfma_kernel<128, 128, false>), grid, dim3(256), 0, st, Ub, Q, Kr, a.N, a.Hkv,
-                               a.Tq, inv_hq, c, partial, ord, rn);
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = record_if(a.prof_stop, st)) != hipSuccess) return err;
+    const uint16_t* Ubc = Ub;
+    const float* rnc = rn;
+    if (p.bm == 32)
+        err = p.rn_bytes ? launch_timed(route_mfma_kernel<32, 128, true>, grid, dim3(256), st, a.prof_start, a.prof_stop,
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc)
+                         : launch_timed(route_mfma_kernel<32, 128, false>, grid, dim3(256), st, a.prof_start, a.prof_stop,
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc);
+    else
+        err = p.rn_bytes ? launch_timed(route_mfma_kernel<128, 128, true>, grid, dim3(256), st, a.prof_start, a.prof_stop,
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc)
+                         : launch_timed(route_mfma_kernel<128, 128, false>, grid, dim3(256), st, a.prof_start, a.prof_stop,
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc);
+    if (err != hipSuccess) return err;
     if (a.Tq > 1) {
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
                            a.N, int(a.Tq / p.bm), a.B, c);

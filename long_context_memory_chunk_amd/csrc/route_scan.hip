@@ -188,10 +188,9 @@ __global__ __launch_bounds__(256) void route_scan_generic(
 template <typename T, int D>
 hipError_t launch_scan_generic(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
     const int64_t total = a.B * a.N;
-    hipLaunchKernelGGL((route_scan_generic<T, D>), dim3(unsigned(ceil_div(total, 256))), dim3(256),
-                       0, st, static_cast<const T*>(a.Krbar), a.N, a.Hkv, U, a.B, a.Tq,
-                       1.f / float(a.Hq), c);
-    return hipGetLastError();
+    return launch_timed(route_scan_generic<T, D>, dim3(unsigned(ceil_div(total, 256))), dim3(256), st,
+                        a.prof_start, a.prof_stop, static_cast<const T*>(a.Krbar), a.N, a.Hkv, U, a.B, a.Tq,
+                        1.f / float(a.Hq), c);
 }
 
 template <int LPR, int NQ>
@@ -200,10 +199,9 @@ hipError_t launch_scan_fast(const RouteArgs& a, const float* U, float* c, hipStr
     int64_t blocks = ceil_div(groups, 4);
     const int64_t cap = int64_t(a.num_cus) * 4;   // 16 waves per CU, grid-strided over 64-row groups
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL((route_scan_bf16_d128<LPR, NQ>), dim3(unsigned(blocks)), dim3(256), 0, st,
-                       static_cast<const u32x4*>(a.Krbar), a.N, U, int(a.B), a.Tq,
-                       1.f / float(a.Hq), c);
-    return hipGetLastError();
+    return launch_timed(route_scan_bf16_d128<LPR, NQ>, dim3(unsigned(blocks)), dim3(256), st, a.prof_start,
+                        a.prof_stop, static_cast<const u32x4*>(a.Krbar), a.N, U, int(a.B), a.Tq,
+                        1.f / float(a.Hq), c);
 }
 
 template <int LPR>
