@@ -8,36 +8,45 @@
 //
 // Two kernels.
 //
-// attn_pack_kernel builds, once per (query b, KV head g), the key space in the
-// layout the matrix cores read, in the workspace:
-//   Kc[b][g][KP][d]  keys: the M_b memory rows as stored, then the L local keys
-//                    rotated at q_offset + j (fp32, rounded once to bf16), then
-//                    zeros up to KP (a multiple of 64);
-//   Vt[b][g][KP/64][d][64]  values, transposed per 64-key tile, each 16-key
-//                    group stored in the order the score accumulator holds its
-//                    keys (see below), so a P.V operand is one 16-byte read.
+// attn_pack_kernel builds, once per (query b, KV head g), the key space as the
+// matrix cores read it, in the workspace, one 16 KB block per 64-key tile:
+//   Kc  keys: the M_b memory rows as stored, then the L local keys rotated at
+//       q_offset + j (fp32, rounded once to bf16), then zeros up to KP (a
+//       multiple of 64); row r of a tile holds its 16 16-byte units with unit
+//       u at position u ^ (r & 15);
+//   Vt  values transposed per tile (row = dimension, 64 keys), each 16-key
+//       group in the order the score accumulator holds its keys (see below);
+//       row d holds its 8 units with unit u at position u ^ ((d >> 1) & 7).
+// The XOR swizzles make every matrix-core operand read below hit 64 distinct
+// LDS banks per 16 lanes, and a tile is copied to LDS as one contiguous block.
 // Every head of the group and every query tile reads these instead of
 // rotating and transposing the same keys again.
 //
-// attn_prefill_kernel: a workgroup (4 waves) owns 128 query tokens of one query
-// head h (KV head h / G); wave w owns tokens 32w .. 32w+31.  Keys are taken 64
-// at a time up to the last local key the tile can see; each 64-key tile of Kc
-// and Vt is 16 KB contiguous, copied to LDS with 16-byte accesses, and the next
-// tile is fetched into registers while this one is used.  Per tile:
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (two 32-key tiles, 8 k-steps
-//     over d), so each lane holds 32 scores of one query token (lanes l and
-//     l + 32 share a token);
-//   * masking only on tiles that cross a wave's causal edge; an online softmax
-//     in the log2 domain (scale 1/sqrt(d) and log2(e) folded into Q before its
-//     bf16 rounding).  The running max m is raised only when a score exceeds
-//     it by more than 2^8: l and O are always scaled by the same m, so the
-//     result is the same softmax, and the rescale of O is almost never taken;
-//   * O += P . V: the 16 keys of a k-step are contracted in the order the score
-//     accumulator holds them (lane half u holds keys {4u..4u+3, 8+4u..8+4u+3}),
-//     which is the order Vt stores them in, so P needs no shuffle.
-// Per-query rescale factors and row sums reach the output layout (query per
-// register) with one lane shuffle each.
+// attn_prefill_kernel: a workgroup (8 waves) owns 256 query tokens of one query
+// head h (KV head h / G); wave w owns tokens 32w .. 32w+31 and keeps them,
+// rotated and scaled, as matrix-core operands in registers.  Keys come 64 at a
+// time, up to the last local key the workgroup can see, through a ring of four
+// LDS tile slots filled by direct global->LDS copies three tiles ahead.
+// Iteration t of the key loop does, per wave:
+//   * the tile max of S(t) and, rarely, a raise of the running max;
+//   * S(t+1)^T = K(t+1) . Q^T on v_mfma_f32_32x32x16_bf16 (two 32-key halves,
+//     8 k-steps over d), each lane holding 32 scores of one query token
+//     (lanes l and l + 32 share a token), while the vector units exponentiate,
+//     sum and pack S(t): the two are independent, so they overlap;
+//   * O += P(t) . V(t): the 16 keys of a k-step are contracted in the order
+//     the score accumulator holds them (lane half u holds keys
+//     {4u..4u+3, 8+4u..8+4u+3}), which is the order Vt stores them in, so P
+//     needs no shuffle.
+// The softmax runs in the log2 domain (scale 1/sqrt(d) and log2(e) folded into
+// Q before its bf16 rounding); the running max m is raised only when a score
+// exceeds it by more than 2^8, and l and O always use the same m, so the
+// result is the same softmax.  Masks are applied only on tiles that cross a
+// wave's causal edge; tiles past it are skipped by that wave.  Workgroups take
+// the heaviest query tiles first, and when the (query, head) count is a
+// multiple of the 8 XCDs, consecutive heads (one KV group) share an XCD and
+// its L2.
 #include "attn_mfma.hpp"
+#include "lds_dma.hpp"
 
 namespace msa {
 namespace {
@@ -45,14 +54,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BQ = 128, BK = 64, DH = 128;
-constexpr int KST = DH + 8;      // K / Q tile row stride in LDS (bf16)
-constexpr int VST = BK + 8;      // transposed V tile row stride in LDS (bf16)
-constexpr int kSmemQ = BQ * KST;
-constexpr int kSmemKV = BK * KST + DH * VST;
-constexpr int kSmem = kSmemQ > kSmemKV ? kSmemQ : kSmemKV;
+constexpr int BK = 64, DH = 128;
+constexpr int kWaves = 8;                  // waves per workgroup
+constexpr int BQ = kWaves * 32;            // query tokens per workgroup
+constexpr int kTileUnits = BK * DH / 8;    // 16-byte units of one K (or V) tile: 1024 (16 KB)
+constexpr int kStages = 4;                 // LDS ring: three tiles in flight behind the one in use
+constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.f;     // raise the running max only past m + 8 (a factor 2^8)
+constexpr float kLazy = 8.f;               // raise the running max only past m + 8 (a factor 2^8)
 
 // Memory rows of query b, clamped as in attn.hip.
 __device__ __forceinline__ void mem_range(const int64_t* __restrict__ mem_off, int64_t b, int64_t cap,
@@ -71,11 +80,16 @@ __device__ __forceinline__ int acc_key(int p) {
     return (e / 4) * 8 + 4 * u + (e % 4);
 }
 
+// Unit positions inside a tile (16-byte units).
+__host__ __device__ inline int k_unit(int row, int u) { return row * 16 + (u ^ (row & 15)); }
+__host__ __device__ inline int v_unit(int d, int u) { return d * 8 + (u ^ ((d >> 1) & 7)); }
+
+constexpr int KST = DH + 8;      // V staging row stride in LDS (bf16), pack kernel only
+
 __global__ __launch_bounds__(256) void attn_pack_kernel(
     const uint16_t* __restrict__ KVmem, const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows,
     const uint16_t* __restrict__ Kl, const uint16_t* __restrict__ Vl, int L, int hkv, int q_offset,
-    const float2* __restrict__ rope, int max_pos, int64_t KP, uint16_t* __restrict__ Kc,
-    uint16_t* __restrict__ Vt) {
+    const float2* __restrict__ rope, int max_pos, int64_t KP, u32x4* __restrict__ Kc, u32x4* __restrict__ Vt) {
     __shared__ __attribute__((aligned(16))) uint16_t sV[BK * KST];
     const int tid = threadIdx.x;
     const int tile = blockIdx.x, g = blockIdx.y;
@@ -86,8 +100,10 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(
     const int64_t k0 = int64_t(tile) * BK;
     const int64_t kv_row = int64_t(hkv) * DH;
     const int64_t bg = b * hkv + g;
+    u32x4* kt = Kc + (bg * (KP / BK) + tile) * kTileUnits;
+    u32x4* vt = Vt + (bg * (KP / BK) + tile) * kTileUnits;
 
-    // keys: 64 keys x 8 slot pairs (i, i + 64)
+    // keys: 64 keys x 8 unit pairs (dimensions i, i + 64)
     for (int u = tid; u < BK * 8; u += 256) {
         const int kk = u / 8, c = (u % 8) * 8;
         const int64_t key = k0 + kk;
@@ -119,9 +135,8 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(
             w2 = u32x4{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]), pack_bf16x2(y2[4], y2[5]),
                        pack_bf16x2(y2[6], y2[7])};
         }
-        uint16_t* dst = Kc + (bg * KP + key) * DH;
-        *reinterpret_cast<u32x4*>(dst + c) = w1;
-        *reinterpret_cast<u32x4*>(dst + c + DH / 2) = w2;
+        kt[k_unit(kk, c / 8)] = w1;
+        kt[k_unit(kk, c / 8 + 8)] = w2;
     }
 
     // values: the 64 x 128 tile to LDS, then written transposed and permuted
@@ -134,7 +149,6 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(
         *reinterpret_cast<u32x4*>(sV + kk * KST + c) = w;
     }
     __syncthreads();
-    uint16_t* vt = Vt + ((bg * (KP / BK) + tile) * DH) * BK;
     for (int u = tid; u < DH * 8; u += 256) {
         const int d = u / 8, p0 = (u % 8) * 8;            // positions p0 .. p0+7 of row d
         uint32_t w[4];
@@ -144,64 +158,111 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(
             const int ka = (pa / 16) * 16 + acc_key(pa % 16), kb = (pb / 16) * 16 + acc_key(pb % 16);
             w[e] = uint32_t(sV[ka * KST + d]) | (uint32_t(sV[kb * KST + d]) << 16);
         }
-        *reinterpret_cast<u32x4*>(vt + d * BK + p0) = u32x4{w[0], w[1], w[2], w[3]};
+        vt[v_unit(d, p0 / 8)] = u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_prefill_kernel(
     const uint16_t* __restrict__ Q, int Tq, int Hq, int hkv, const int64_t* __restrict__ mem_off, int64_t cap,
     int64_t max_rows, int L, int q_offset, float qscale, const float2* __restrict__ rope, int max_pos,
-    int64_t KP, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, uint16_t* __restrict__ O) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
-    uint16_t* sQ = smem;                 // prologue only
-    uint16_t* sK = smem;                 // key loop (aliases sQ)
-    uint16_t* sVt = smem + BK * KST;
+    int64_t KP, const u32x4* __restrict__ Kc, const u32x4* __restrict__ Vt, uint16_t* __restrict__ O, int n_qt,
+    int64_t B) {
+    __shared__ __attribute__((aligned(16))) u32x4 sK[kStages * kTileUnits];
+    __shared__ __attribute__((aligned(16))) u32x4 sV[kStages * kTileUnits];
 
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int qt = int(gridDim.x) - 1 - int(blockIdx.x);          // longest (latest) tiles first
-    const int h = blockIdx.y;
-    const int64_t b = blockIdx.z;
+    // ---- which (query tile, batch, head): heaviest tiles first, one KV group per XCD
+    const int64_t n_bh = B * Hq;
+    const int64_t lin = blockIdx.x;
+    const int rank = int(lin / n_bh);
+    int64_t r = lin % n_bh;
+    if (n_bh % kXcds == 0) r = (r % kXcds) * (n_bh / kXcds) + r / kXcds;
+    const int qt = n_qt - 1 - rank;
+    const int64_t b = r / Hq;
+    const int h = int(r % Hq);
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave, half = lane / 32;
     const int G = Hq / hkv, g = h / G;
-    const int i0 = qt * BQ;
     const int64_t bg = b * hkv + g;
+    const int i0 = qt * BQ;
+    const int q_lo = i0 + wave * 32;                 // the wave's first token
+    const int qi = q_lo + lane % 32;                 // this lane's token (a column of S^T)
+    const bool q_valid = qi < Tq;
 
-    // ---- rotated, scaled query rows of this tile -> LDS (bf16)
-    for (int idx = tid; idx < BQ * (DH / 2); idx += 256) {
-        const int r = idx / (DH / 2), c = idx % (DH / 2);
-        const int i = i0 + r;
-        float y1 = 0.f, y2 = 0.f;
-        if (i < Tq) {
-            int pos = q_offset + (L - Tq) + i;
-            pos = pos < max_pos ? pos : max_pos - 1;
-            const int64_t qb = ((b * Tq + i) * Hq + h) * DH;
-            const float x1 = bf16_to_f32(Q[qb + c]), x2 = bf16_to_f32(Q[qb + c + DH / 2]);
-            const float2 cs = rope[int64_t(pos) * (DH / 2) + c];
-            y1 = (x1 * cs.x - x2 * cs.y) * qscale;
-            y2 = (x2 * cs.x + x1 * cs.y) * qscale;
-        }
-        sQ[r * KST + c] = f32_to_bf16(y1);
-        sQ[r * KST + c + DH / 2] = f32_to_bf16(y2);
-    }
-    __syncthreads();
-    bf16x8 qf[8];                        // B operand of S^T: d = 16 ks + 8 (lane/32) + e, query = lane % 32
+    // ---- rotated, scaled query token as B operands: qf[ks] holds d = 16 ks + 8 half + e
+    bf16x8 qf[8];
+    {
+        const int qs = q_valid ? qi : 0;
+        int pos = q_offset + (L - Tq) + qs;
+        pos = pos < max_pos ? pos : max_pos - 1;
+        const uint16_t* qrow = Q + ((b * Tq + qs) * Hq + h) * DH;
+        const float2* cs = rope + int64_t(pos) * (DH / 2);
+        const float sc = q_valid ? qscale : 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(sQ + (wave * 32 + lane % 32) * KST + ks * 16 + (lane / 32) * 8);
-    __syncthreads();
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 16 * ks + 8 * half;           // dimensions c0 .. c0+7 pair with c0+64 ..
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(qrow + c0);
+            const u32x4 x2 = *reinterpret_cast<const u32x4*>(qrow + c0 + DH / 2);
+            float y1[8], y2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float a = (e & 1) ? bf16_hi(x1[e / 2]) : bf16_lo(x1[e / 2]);
+                const float bb = (e & 1) ? bf16_hi(x2[e / 2]) : bf16_lo(x2[e / 2]);
+                const float2 rc = cs[c0 + e];
+                y1[e] = (a * rc.x - bb * rc.y) * sc;
+                y2[e] = (bb * rc.x + a * rc.y) * sc;
+            }
+            qf[ks] = __builtin_bit_cast(bf16x8, (u32x4{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]),
+                                                       pack_bf16x2(y1[4], y1[5]), pack_bf16x2(y1[6], y1[7])}));
+            qf[ks + 4] = __builtin_bit_cast(bf16x8, (u32x4{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]),
+                                                           pack_bf16x2(y2[4], y2[5]), pack_bf16x2(y2[6], y2[7])}));
+        }
+    }
 
-    // ---- key space of this tile
+    // ---- key space of this workgroup and of this wave
     int64_t r0, M;
     mem_range(mem_off, b, cap, max_rows, r0, M);
     const int last_q = (i0 + BQ < Tq ? i0 + BQ : Tq) - 1;
-    const int64_t jmax = int64_t(L - Tq) + last_q;                 // last local key any token here sees
-    const int n_tiles = int((M + jmax + 1 + BK - 1) / BK);
-    const int qi = i0 + wave * 32 + lane % 32;                      // this lane's query token
-    const int64_t lim = int64_t(L - Tq) + qi;                       // local key j visible iff j <= lim
-    const int q_lo = i0 + wave * 32;                                // the wave's first token
-    const int q_hi = (q_lo + 31 < Tq ? q_lo + 31 : Tq - 1);         // and last valid one
+    const int n_tiles = int((M + int64_t(L - Tq) + last_q + 1 + BK - 1) / BK);
+    const int q_hi = (q_lo + 31 < Tq ? q_lo + 31 : Tq - 1);
     const bool wave_live = q_lo < Tq;
     const bool wave_whole = q_lo + 31 < Tq;
-    const int64_t lim_lo = int64_t(L - Tq) + q_lo, lim_hi = int64_t(L - Tq) + q_hi;
+    const int64_t lim_lo = int64_t(L - Tq) + q_lo;   // local key j visible to every token of the wave iff j <= lim_lo
+    const int wave_tiles = wave_live ? int((M + int64_t(L - Tq) + q_hi + 1 + BK - 1) / BK) : 0;
+    // key index (in the tile's key space) up to which this lane's token sees
+    const int64_t see = q_valid ? M + int64_t(L - Tq) + qi : -1;
+
+    // ---- direct copies of tile t into ring slot t % kStages: 8 waves x 2 x 1 KB per tensor
+    const u32x4* kg = Kc + bg * (KP / BK) * kTileUnits;
+    const u32x4* vg = Vt + bg * (KP / BK) * kTileUnits;
+    const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
+    auto dma = [&](int t) {
+        const uint32_t slot = uint32_t(t % kStages) * kTileUnits;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int piece = (i * kWaves + wave) * kWave;
+            lds_copy16(kg + int64_t(t) * kTileUnits + piece + lane,
+                       __builtin_amdgcn_readfirstlane(ldsK + (slot + piece) * 16));
+            lds_copy16(vg + int64_t(t) * kTileUnits + piece + lane,
+                       __builtin_amdgcn_readfirstlane(ldsV + (slot + piece) * 16));
+        }
+    };
+    constexpr int kCopies = 4;                       // copies per wave per tile
+
+    // S(t)^T for this wave: rows = the tile's keys, columns = the wave's tokens
+    auto scores = [&](int t, f32x16 (&s)[2]) {
+        const u32x4* kt = sK + (t % kStages) * kTileUnits;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[tt][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, kt[k_unit(tt * 32 + lane % 32, 2 * ks + half)]);
+                s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[tt], 0, 0, 0);
+            }
+    };
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o[4];
@@ -210,135 +271,124 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-    // ---- register prefetch of one 64-key tile of Kc and Vt (16 KB each, contiguous)
-    const uint16_t* kc = Kc + bg * KP * DH;
-    const uint16_t* vtb = Vt + bg * KP * DH;
-    u32x4 rk[4], rv[4];
-    auto fetch = [&](int t) {
-        const u32x4* ks = reinterpret_cast<const u32x4*>(kc + int64_t(t) * BK * DH);
-        const u32x4* vs = reinterpret_cast<const u32x4*>(vtb + int64_t(t) * BK * DH);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            rk[j] = ks[tid + 256 * j];
-            rv[j] = vs[tid + 256 * j];
-        }
-    };
-    if (n_tiles > 0) fetch(0);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int64_t k0 = int64_t(t) * BK;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int u = tid + 256 * j;
-            *reinterpret_cast<u32x4*>(sK + (u / 16) * KST + (u % 16) * 8) = rk[j];
-            *reinterpret_cast<u32x4*>(sVt + (u / 8) * VST + (u % 8) * 8) = rv[j];
-        }
-        __syncthreads();
-        if (t + 1 < n_tiles) fetch(t + 1);
-
-        // tile class for this wave: every key visible to every token / none to any
-        const int64_t k_last = k0 + BK - 1;
-        const bool all_vis = wave_whole && (k_last < M || (k_last - M) <= lim_lo);
-        const bool none_vis = !wave_live || (k0 >= M && (k0 - M) > lim_hi);
-        if (!none_vis) {
-            // ---- S^T for two 32-key sub-tiles: rows = keys, columns = this wave's queries
-            f32x16 s[2];
+    // tile max of S(t) (masked on edge tiles) and the lazy raise of the running max
+    auto tile_max = [&](f32x16 (&s)[2], int t, bool full) {
+        if (!full) {
+            int64_t thr64 = see - int64_t(t) * BK;       // key offsets <= thr are visible
+            thr64 = thr64 < -1 ? -1 : (thr64 > BK ? BK : thr64);
+            const int thr = int(thr64);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[tt][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (tt * 32 + lane % 32) * KST + ks * 16 +
-                                                                      (lane / 32) * 8);
-                    s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[tt], 0, 0, 0);
-                }
-
-            // ---- mask (edge tiles only) and tile max; lanes l and l+32 share a query
-            if (!all_vis) {
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int64_t key = k0 + tt * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-                        const bool vis = (key < M || (key - M) <= lim) && qi < Tq;
-                        s[tt][i] = vis ? s[tt][i] : -INFINITY;
-                    }
-            }
-            float mt = -INFINITY;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-
-            // ---- lazy running max: raise it only past m + kLazy
-            const bool raise = mt > m_run + kLazy;
-            if (__any(raise)) {
-                const float m_new = raise ? mt : m_run;
-                const float corr = raise ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
-                l_run *= corr;
-                m_run = m_new;
-                // register i holds query (i/4)*8 + (lane/32)*4 + i%4 of this wave
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float f = __shfl(corr, (i / 4) * 8 + (lane / 32) * 4 + (i % 4));
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) o[dt][i] *= f;
+                    const int off = tt * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+                    s[tt][i] = (off <= thr) ? s[tt][i] : -INFINITY;
                 }
-            }
-            float rs = 0.f;
-            if (all_vis) {
+        }
+        float mt = -INFINITY;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = __builtin_amdgcn_exp2f(s[tt][i] - m_run);
-                        s[tt][i] = p;
-                        rs += p;
-                    }
-            } else {
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const bool raise = mt > m_run + kLazy;
+        if (__any(raise)) {
+            const float m_new = raise ? mt : m_run;
+            const float corr = raise ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.f;
+            l_run *= corr;
+            m_run = m_new;
+            // register i of O holds token (i/4)*8 + half*4 + i%4 of this wave
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+            for (int i = 0; i < 16; ++i) {
+                const float f = __shfl(corr, (i / 4) * 8 + half * 4 + (i % 4));
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float p = (s[tt][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - m_run);
-                        s[tt][i] = p;
-                        rs += p;
-                    }
-            }
-            rs += __shfl_xor(rs, 32);
-            l_run += rs;
-
-            // ---- O += P . V over 4 k-steps of 16 keys, in accumulator order; operands
-            // are assembled as packed dwords and bit-cast whole
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int tt = ks / 2, sp = ks % 2;
-                const u32x4 pw = {pack_bf16x2(s[tt][sp * 8 + 0], s[tt][sp * 8 + 1]),
-                                  pack_bf16x2(s[tt][sp * 8 + 2], s[tt][sp * 8 + 3]),
-                                  pack_bf16x2(s[tt][sp * 8 + 4], s[tt][sp * 8 + 5]),
-                                  pack_bf16x2(s[tt][sp * 8 + 6], s[tt][sp * 8 + 7])};
-                const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 vb = *reinterpret_cast<const bf16x8*>(sVt + (dt * 32 + lane % 32) * VST + ks * 16 +
-                                                                       (lane / 32) * 8);
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, o[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < 4; ++dt) o[dt][i] *= f;
             }
         }
+    };
+    // P(t) = exp2(S - m) packed as A operands of the 4 k-steps; row sums into l.
+    // On edge tiles a masked score gives 0 even where m is still -inf (a token
+    // past Tq, which sees nothing).
+    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&pa)[4], bool full) {
+        float rs = 0.f;
+        float p[2][16];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(s[tt][i] - m_run);
+                p[tt][i] = (full || s[tt][i] != -INFINITY) ? e : 0.f;
+                rs += p[tt][i];
+            }
+        rs += __shfl_xor(rs, 32);
+        l_run += rs;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int tt = ks / 2, sp = (ks % 2) * 8;
+            pa[ks] = __builtin_bit_cast(bf16x8, (u32x4{pack_bf16x2(p[tt][sp + 0], p[tt][sp + 1]),
+                                                       pack_bf16x2(p[tt][sp + 2], p[tt][sp + 3]),
+                                                       pack_bf16x2(p[tt][sp + 4], p[tt][sp + 5]),
+                                                       pack_bf16x2(p[tt][sp + 6], p[tt][sp + 7])}));
+        }
+    };
+    auto pv = [&](int t, const bf16x8 (&pa)[4]) {
+        const u32x4* vt = sV + (t % kStages) * kTileUnits;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, vt[v_unit(dt * 32 + lane % 32, 2 * ks + half)]);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vb, o[dt], 0, 0, 0);
+            }
+    };
+    // every key of tile t visible to every token of the wave
+    auto tile_full = [&](int t) { return wave_whole && int64_t(t) * BK + BK - 1 <= M + lim_lo; };
+
+    // ---- prologue: three tiles in flight, S(0)
+    for (int t = 0; t < kStages - 1 && t < n_tiles; ++t) dma(t);
+    if (n_tiles >= 3) MSA_WAIT_VMCNT(2 * kCopies);
+    else if (n_tiles == 2) MSA_WAIT_VMCNT(kCopies);
+    else MSA_WAIT_VMCNT(0);
+    __syncthreads();
+    f32x16 s_cur[2];
+    if (wave_tiles > 0) scores(0, s_cur);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        // tile t+1 in LDS for every wave, and every wave done with the slot tile t+3 reuses
+        if (t + 2 < n_tiles) MSA_WAIT_VMCNT(kCopies);
+        else MSA_WAIT_VMCNT(0);
         __syncthreads();
+        if (t + kStages - 1 < n_tiles) dma(t + kStages - 1);
+
+        f32x16 s_nxt[2];
+        bf16x8 pa[4];
+        if (t + 1 < wave_tiles && tile_full(t)) {
+            // common case: S(t+1) on the matrix cores while the vector units finish S(t)
+            tile_max(s_cur, t, true);
+            scores(t + 1, s_nxt);
+            probs(s_cur, pa, true);
+            pv(t, pa);
+        } else {
+            const bool full = tile_full(t);
+            if (t < wave_tiles) tile_max(s_cur, t, full);
+            if (t + 1 < wave_tiles) scores(t + 1, s_nxt);
+            if (t < wave_tiles) {
+                probs(s_cur, pa, full);
+                pv(t, pa);
+            }
+        }
+        if (t + 1 < wave_tiles) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) s_cur[tt] = s_nxt[tt];
+        }
     }
 
     // ---- normalise and store
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int qr = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+        const int qr = (i / 4) * 8 + half * 4 + (i % 4);
         const float lsum = __shfl(l_run, qr);
-        const int qtok = i0 + wave * 32 + qr;
+        const int qtok = q_lo + qr;
         if (qtok < Tq) {
             const float inv = 1.f / lsum;
             const int64_t ob = ((b * Tq + qtok) * Hq + h) * DH;
@@ -366,18 +416,21 @@ size_t attn_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
     const int64_t KP = keys_padded(a.max_rows, a.L);
     const size_t one = size_t(a.B) * a.Hkv * KP * DH * 2;
-    uint16_t* Kc = static_cast<uint16_t*>(a.ws);
-    uint16_t* Vt = reinterpret_cast<uint16_t*>(static_cast<char*>(a.ws) + align256(one));
+    u32x4* Kc = static_cast<u32x4*>(a.ws);
+    u32x4* Vt = reinterpret_cast<u32x4*>(static_cast<char*>(a.ws) + align256(one));
     hipLaunchKernelGGL(attn_pack_kernel, dim3(unsigned(KP / BK), unsigned(a.Hkv), unsigned(a.B)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.KVmem), a.mem_off, a.mem_rows_cap, a.max_rows,
                        static_cast<const uint16_t*>(a.K_local), static_cast<const uint16_t*>(a.V_local), a.L, a.Hkv,
                        a.q_offset, a.rope_cs, a.max_pos, KP, Kc, Vt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid(unsigned(ceil_div(a.Tq, BQ)), unsigned(a.Hq), unsigned(a.B));
-    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(a.Q), a.Tq, a.Hq,
-                       a.Hkv, a.mem_off, a.mem_rows_cap, a.max_rows, a.L, a.q_offset, a.scale * kLog2e, a.rope_cs,
-                       a.max_pos, KP, Kc, Vt, static_cast<uint16_t*>(a.O));
+    const int n_qt = int(ceil_div(a.Tq, BQ));
+    const int64_t blocks = int64_t(n_qt) * a.B * a.Hq;
+    hipLaunchKernelGGL(attn_prefill_kernel, dim3(unsigned(blocks)), dim3(kWaves * 64), 0, st,
+                       static_cast<const uint16_t*>(a.Q), a.Tq, a.Hq, a.Hkv, a.mem_off, a.mem_rows_cap, a.max_rows,
+                       a.L, a.q_offset, a.scale * kLog2e, a.rope_cs, a.max_pos, KP,
+                       static_cast<const u32x4*>(Kc), static_cast<const u32x4*>(Vt), static_cast<uint16_t*>(a.O),
+                       n_qt, a.B);
     return hipGetLastError();
 }
 

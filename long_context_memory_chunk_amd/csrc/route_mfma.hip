@@ -25,6 +25,7 @@
 // to a partial array and route_mfma_tokmax takes the max over a query's tiles.
 #include <type_traits>
 
+#include "lds_dma.hpp"
 #include "route_mfma.hpp"
 
 namespace msa {
@@ -333,21 +334,6 @@ __global__ __launch_bounds__(256) void route_khat_pack(const uint16_t* __restric
     Kp[(tile * S + st) * kUnitsPerStage + r * GU + (u ^ swz(r))] = w;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// One 16-byte direct global->LDS copy per lane: lane i's 16 bytes land at LDS
-// byte address lds + 16 i (lds wave-uniform).  Written as asm so that the only
-// waits on these copies are the explicit ones below (the compiler would
-// otherwise make every LDS read wait for every copy in flight); the copy has no
-// register result.
-__device__ __forceinline__ void lds_copy16(const u32x4* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-}
-
-// s_waitcnt with only the vector-memory count limited (expcnt and lgkmcnt left
-// at their maxima): GFX9 encoding, vmcnt in bits [3:0] and [15:14].
-#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
-
 __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restrict__ Up, const u32x4* __restrict__ Kp,
                                                             int64_t N, int S, float inv_hq,
                                                             float* __restrict__ partial, TileOrder ord) {
@@ -369,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
     const int wm = wave / 2, wn = wave % 2;
     const u32x4* Ag = Up + qt * int64_t(S) * kUnitsPerStage;
     const u32x4* Bg = Kp + ct * int64_t(S) * kUnitsPerStage;
-    const uint32_t ldsA = uint32_t(size_t((lds_ptr)sA)), ldsB = uint32_t(size_t((lds_ptr)sB));
+    const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
 
     // one stage = 2 x 16 KB; a wave copies 4 + 4 contiguous 1 KB pieces (8 copies)
     constexpr int kCopies = 8;
