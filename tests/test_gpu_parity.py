@@ -368,6 +368,8 @@ ATTN_CASES = [
     ("bf16", 128, 32, 8, 2, 200, 500, [0, 300], 16),  # partial query tile, one query without memory
     ("bf16", 128, 8, 8, 1, 130, 130, [70], 8),        # G = 1, ragged tile
     ("bf16", 128, 16, 1, 1, 96, 1000, [64], 16),      # G = 16
+    ("bf16", 128, 64, 8, 2, 1, 700, [90, 200], 16),   # G = 8 decode
+    ("bf16", 128, 32, 8, 4, 1, 8192, [500, 0, 1000, 37], 16),  # several 64-key chunks per workgroup
 ]
 
 
