@@ -238,6 +238,47 @@ def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
     assert np.max(np.abs(ch - c_ref)) <= _score_tol("bf16", d, B, Tq)
 
 
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq", [
+    ("bf16", 128, 32, 8, 1, 1),       # streaming scan
+    ("bf16", 128, 32, 8, 32, 1),      # matrix cores, decode batch
+    ("bf16", 128, 32, 8, 1, 256),     # prefill GEMM (normalised keys)
+    ("f32", 64, 8, 2, 1, 4),          # generic scan
+])
+def test_route_zero_vectors(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq):
+    """A zero routing key (whole row or one KV head) and a zero query head give
+    cosine 0 through max(|x|, eps), on every scan path."""
+    ctx = _ctx(d, ctx64, ctx128)
+    counts = np.random.default_rng(5).integers(1, 6, size=120)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank(dtype, N, Hkv, d, 61).copy()
+    Kb[::7] = 0                       # whole rows
+    Kb[3::11, Hkv - 1] = 0            # the last KV head of other rows
+    Qr = W.draw(62, 4, (B, Tq, Hq, d), dtype).copy()
+    Qr[:, :, 1] = 0                   # one query head of every token
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx, Qr, Kb, coff, 8, dtype)
+    c_ref = oracle.chunk_scores(W.widen(Qr, dtype), W.widen(Kb, dtype))
+    D_ref = oracle.doc_scores(c_ref, coff)
+    tol = _score_tol(dtype, d, B, Tq)
+    assert np.all(np.isfinite(ch))
+    assert np.max(np.abs(ch - c_ref)) <= tol
+    assert np.max(np.abs(dc - D_ref)) <= tol
+    for b in range(B):
+        _check_valid_topk(ids[b], sc[b], D_ref[b], tol)
+
+
+def test_route_single_document(torch_mod, msa, ctx128):
+    """A bank of one document: top-1 is that document, scored by its best chunk."""
+    Hq, Hkv, d = 32, 8, 128
+    coff = np.array([0, 5], dtype=np.int64)
+    Kb = _bank("bf16", 5, Hkv, d, 71)
+    Qr = msa_synth.normal_bf16(72, 4, (1, 1, Hq, d))
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx128, Qr, Kb, coff, 1, "bf16")
+    c_ref = oracle.chunk_scores(W.widen(Qr, "bf16"), W.widen(Kb, "bf16"))
+    assert ids.tolist() == [[0]]
+    assert abs(sc[0, 0] - c_ref[0].max()) <= _score_tol("bf16", d, 1, 1)
+
+
 def test_route_ties_go_to_lowest_id(torch_mod, msa, ctx128):
     Hq, Hkv, d = 32, 8, 128
     counts = np.array([2, 3, 1, 2, 3, 2, 1, 4])
@@ -370,6 +411,8 @@ ATTN_CASES = [
     ("bf16", 128, 16, 1, 1, 96, 1000, [64], 16),      # G = 16
     ("bf16", 128, 64, 8, 2, 1, 700, [90, 200], 16),   # G = 8 decode
     ("bf16", 128, 32, 8, 4, 1, 8192, [500, 0, 1000, 37], 16),  # several 64-key chunks per workgroup
+    ("bf16", 128, 32, 8, 2, 1, 1, [0, 5], 16),        # one local key; one query sees only it
+    ("f32", 64, 4, 2, 2, 1, 1, [0, 3], 4),            # the same on the generic kernel
 ]
 
 
