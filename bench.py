@@ -81,7 +81,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
-    p.add_argument("--workload", choices=["decode100m", "prefill8k", "batch32", "encode10m", "hbmcopy"],
+    p.add_argument("--workload", choices=["decode100m", "chunk100m", "prefill8k", "batch32", "encode10m", "hbmcopy"],
                    default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
                         "prefill8k / batch32: extra measurements on the 10M-token bank; "
@@ -118,17 +118,24 @@ class PinnedHost:
             self.addr = 0
 
 
-def build_workload(args, torch, msa, msa_synth, device_fill, W):
+def build_workload(args, torch, msa, msa_synth, device_fill, W, chunk_level=False):
+    """The 100M-token bank.  With chunk_level, every chunk is its own document
+    (offsets 0, 1, ..., N): routing then selects chunks, and the gather copies
+    one row per selected chunk."""
     seed, L, k = args.seed, args.layers, args.top_k
     lens = msa_synth.lognormal_lengths(seed, args.tokens)
     coff = msa_synth.ceil_chunk_offsets(lens, CHUNK)
     n_docs, N = len(lens), int(coff[-1])
     log(f"{args.tokens} tokens -> {n_docs} documents, {N} chunk rows per layer")
+    if chunk_level:
+        coff = np.arange(N + 1, dtype=np.int64)
+        n_docs = N
+        log("chunk-level selection: every chunk is a document")
     dev = torch.device("cuda:0")
     Krbar = torch.empty((L, N, Hkv, D), dtype=torch.bfloat16, device=dev)
     for l in range(L):
         device_fill.fill_counter_bf16(Krbar[l], seed, W.krbar_stream(l), 0)
-    planted = msa_synth.pick_planted(seed, 50, n_docs, k)
+    planted = msa_synth.pick_planted(seed, 60 if chunk_level else 50, n_docs, k)
     Qr_h = [msa_synth.normal_bf16(seed, 100 + l, (1, 1, Hq, D)) for l in range(L)]
     for l in range(L):
         q = msa_synth.bf16_bits_to_f32(Qr_h[l])[0, 0]
@@ -585,7 +592,7 @@ def main():
     from tests import workloads as W
 
     msa.lib()
-    if args.workload != "decode100m":
+    if args.workload not in ("decode100m", "chunk100m"):
         fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "encode10m": run_encode10m,
               "hbmcopy": run_hbmcopy}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
@@ -593,7 +600,8 @@ def main():
         ok = out.get("planted_recovered", out.get("planted_recovered_all",
                                                   out.get("copy_checked", out.get("outputs_finite"))))
         sys.exit(0 if ok else 1)
-    wl = build_workload(args, torch, msa, msa_synth, device_fill, W)
+    chunk_level = args.workload == "chunk100m"
+    wl = build_workload(args, torch, msa, msa_synth, device_fill, W, chunk_level)
     run = Runner(args, torch, msa, wl)
     build_host_store(args, torch, device_fill, W, wl)
     N, L, planted = wl["N"], wl["L"], sorted(int(d) for d in wl["planted"])
@@ -651,7 +659,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "100M-token bank, 18 routing layers, 1-token routed decode "
-                               "(route + top-16 + gather from pinned host memory + sparse attention per layer)",
+                               + ("(route + top-16 chunks (chunk-level selection) + gather from pinned host "
+                                  "memory + sparse attention per layer)" if chunk_level else
+                                  "(route + top-16 + gather from pinned host memory + sparse attention per layer)"),
+                   "selection": "chunks" if chunk_level else "documents",
                    "tokens": args.tokens, "n_docs": wl["n_docs"], "chunk_rows": N, "chunk": CHUNK,
                    "layers": L, "Hq": Hq, "Hkv": Hkv, "head_dim": D, "top_k": args.top_k,
                    "local": args.local, "Krbar_GB": round(kr_bytes_step / 1e9, 2),

@@ -126,6 +126,60 @@ def test_decode_100m_layer_full_oracle_topk(env):
 
 
 @pytest.mark.timeout(900)
+def test_chunk_level_topk_100m_layer(env):
+    """Chunk-level selection (documents of one chunk each: offsets 0, 1, ..., N)
+    on the 100M-token bank's layer 0: the top-16 chunks against the oracle over
+    every chunk, then both gathers copy one row per selected chunk."""
+    torch, msa, device, ctx = env
+    seed, k = 0, 16
+    lens = msa_synth.lognormal_lengths(seed, 100_000_000)
+    N = int(msa_synth.ceil_chunk_offsets(lens, C)[-1])
+    coff = np.arange(N + 1, dtype=np.int64)
+    Kr = torch.empty((N, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    device.fill_counter_bf16(Kr, seed, W.krbar_stream(0), 0)
+    planted = msa_synth.pick_planted(seed, 60, N, k)
+    Qr_h = msa_synth.normal_bf16(seed, 101, (1, 1, Hq, D))
+    q = msa_synth.bf16_bits_to_f32(Qr_h)[0, 0]
+    prow = []
+    for j, r in enumerate(planted):
+        rows = W.planted_pooled(seed, 0, q, Hkv, 1, tag=500 + j)
+        Kr[int(r):int(r) + 1].copy_(W.dev_bf16(rows))
+        prow.append(((int(r), int(r) + 1), rows))
+    coff_d = torch.from_numpy(coff).cuda()
+    ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    ws = msa.workspace(msa.msa_route_workspace_size(1, 1, 1, Hq, Hkv, N, N, k))
+    msa.msa_route(ctx, W.dev_bf16(Qr_h), Kr, coff_d, k, ids, ws, out_scores=sc)
+    torch.cuda.synchronize()
+    del Kr
+    c_ref = _oracle_scores_blocked(W.widen(Qr_h, "bf16"), seed, 0, coff, prow)
+    ids_ref, sc_ref = oracle.topk_docs(c_ref, k)             # documents of one chunk: chunk scores
+    got = ids.cpu().numpy()
+    assert sorted(got[0].tolist()) == sorted(ids_ref[0].tolist()) == sorted(planted.tolist())
+    assert sc_ref[0].min() - np.delete(c_ref[0], ids_ref[0]).max() >= 0.05
+    assert np.max(np.abs(sc.cpu().numpy() - sc_ref)) <= VALU_TOL
+
+    # both gathers: one 4 KB row per selected chunk, in ascending chunk order
+    host = _pinned_layer(torch, device, seed, 0, N)
+    dst = torch.empty((k, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    mo_h = torch.zeros(2, dtype=torch.int64, pin_memory=True)
+    mo_d = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    msa.msa_gather(host, 2 * Hkv * D * 2, N, coff, got.astype(np.int32), k, dst, k, mo_h, mo_d, side=side)
+    torch.cuda.current_stream().wait_stream(side)
+    dst2 = torch.empty_like(dst)
+    mo2 = torch.zeros(2, dtype=torch.int64, device="cuda")
+    wsg = msa.workspace(msa.msa_gather_device_workspace_size(1, k))
+    msa.msa_gather_device(ctx, host, 2 * Hkv * D * 2, N, coff_d, ids, dst2, k, mo2, wsg)
+    torch.cuda.synchronize()
+    rows = np.concatenate([msa_synth.counter_bf16(seed, W.kvbar_stream(0), int(r) * 2 * Hkv * D, 2 * Hkv * D)
+                           .reshape(1, 2, Hkv, D) for r in sorted(int(x) for x in ids_ref[0])])
+    assert int(mo_h[1]) == k and mo2.cpu().tolist() == [0, k]
+    assert np.array_equal(W.host_bits(dst), rows)
+    assert np.array_equal(W.host_bits(dst2), rows)
+
+
+@pytest.mark.timeout(900)
 def test_batch32_10m_layer_full_oracle(env):
     """32 single-token queries against one layer of the 10M-token bank
     (156,250 chunk rows, ~20K documents), matrix-core routing: every query's
