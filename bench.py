@@ -80,7 +80,9 @@ def parse():
     p.add_argument("--top-k", type=int, default=16)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-chunks", type=int, default=1_000_000)
+    p.add_argument("--cpu-sample-chunks", type=int, default=0,
+                   help="chunk rows per layer in the oracle sample (0: the whole layer)")
+    p.add_argument("--cpu-sample-layers", type=int, default=4, help="routing layers in the oracle sample")
     p.add_argument("--workload", choices=["decode100m", "chunk100m", "reuse100m", "prefill8k", "batch32", "encode10m",
                                           "hbmcopy"],
                    default="decode100m",
@@ -265,10 +267,10 @@ class Runner:
 
 
 def cpu_baseline(args, wl, W, msa_synth):
-    """The oracle, untuned, on a bounded sample of the same workload: layer
-    0's routing over the first S chunk rows (regenerated on the host; only
-    the oracle calls are timed) plus layer 0's full attention; scaled to one
-    18-layer step."""
+    """The oracle, untuned, on a bounded sample of the same workload: the
+    routing of the first few routing layers over their chunk rows
+    (regenerated on the host; only the oracle calls are timed) plus each
+    sampled layer's attention; scaled to one 18-layer step."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -277,33 +279,41 @@ def cpu_baseline(args, wl, W, msa_synth):
         threads = 1
     seed, k = args.seed, args.top_k
     coff, N = wl["coff"], wl["N"]
-    S = min(args.cpu_sample_chunks, N)
+    S = N if args.cpu_sample_chunks <= 0 else min(args.cpu_sample_chunks, N)
     n_docs_s = int(np.searchsorted(coff, S, side="right")) - 1      # documents fully inside
     S = int(coff[n_docs_s])
-    Kb = W.counter_bf16_threads(seed, W.krbar_stream(0), 0, S * Hkv * D).reshape(S, Hkv, D)
-    q0 = msa_synth.bf16_bits_to_f32(wl["Qr_h"][0])[0, 0]
-    for j, d in enumerate(wl["planted"]):
-        if coff[d + 1] <= S:
-            Kb[coff[d]:coff[d + 1]] = W.planted_pooled(seed, 0, q0, Hkv, int(coff[d + 1] - coff[d]), tag=j)
-    Qr64, Kb64 = W.widen(wl["Qr_h"][0], "bf16"), W.widen(Kb, "bf16")
-    t0 = time.perf_counter()
-    _ids, _, _, _ = oracle.route(Qr64, Kb64, coff[: n_docs_s + 1], min(k, n_docs_s))
-    t_route = time.perf_counter() - t0
-    # attention of layer 0 over the planted documents' pooled rows + local context
-    sel = sorted(int(d) for d in wl["planted"])
-    rows = [msa_synth.counter_bf16(seed, W.kvbar_stream(0), int(coff[d]) * 2 * Hkv * D,
-                                   int(coff[d + 1] - coff[d]) * 2 * Hkv * D).reshape(-1, 2, Hkv, D) for d in sel]
-    kv = W.widen(np.concatenate(rows), "bf16")
-    Qa, Kl, Vl = (W.widen(wl[n][0], "bf16") for n in ("Q_h", "Kl_h", "Vl_h"))
-    t0 = time.perf_counter()
-    oracle.sparse_attn(Qa, kv[:, 0], kv[:, 1], [0, len(kv)], Kl, Vl, k, 1 / math.sqrt(D), 1e6)
-    t_attn = time.perf_counter() - t0
-    t_step = wl["L"] * (t_route * N / S + t_attn)
+    n_layers = max(1, min(args.cpu_sample_layers, wl["L"]))
+    t_route = t_attn = 0.0
+    mem_rows = 0
+    for l in range(n_layers):
+        Kb = W.counter_bf16_threads(seed, W.krbar_stream(l), 0, S * Hkv * D).reshape(S, Hkv, D)
+        q = msa_synth.bf16_bits_to_f32(wl["Qr_h"][l])[0, 0]
+        for j, d in enumerate(wl["planted"]):
+            if coff[d + 1] <= S:
+                Kb[coff[d]:coff[d + 1]] = W.planted_pooled(seed, l, q, Hkv, int(coff[d + 1] - coff[d]), tag=j)
+        Qr64, Kb64 = W.widen(wl["Qr_h"][l], "bf16"), W.widen(Kb, "bf16")
+        del Kb
+        t0 = time.perf_counter()
+        oracle.route(Qr64, Kb64, coff[: n_docs_s + 1], min(k, n_docs_s))
+        t_route += time.perf_counter() - t0
+        del Kb64
+        # attention of the layer over the planted documents' pooled rows + local context
+        sel = sorted(int(d) for d in wl["planted"])
+        rows = [msa_synth.counter_bf16(seed, W.kvbar_stream(l % wl["HL"]), int(coff[d]) * 2 * Hkv * D,
+                                       int(coff[d + 1] - coff[d]) * 2 * Hkv * D).reshape(-1, 2, Hkv, D)
+                for d in sel]
+        kv = W.widen(np.concatenate(rows), "bf16")
+        mem_rows = len(kv)
+        Qa, Kl, Vl = (W.widen(wl[n][l], "bf16") for n in ("Q_h", "Kl_h", "Vl_h"))
+        t0 = time.perf_counter()
+        oracle.sparse_attn(Qa, kv[:, 0], kv[:, 1], [0, len(kv)], Kl, Vl, k, 1 / math.sqrt(D), 1e6)
+        t_attn += time.perf_counter() - t0
+    t_step = wl["L"] / n_layers * (t_route * N / S + t_attn)
     gb = wl["L"] * N * ROW_KR / 1e9
     return {"value": gb / t_step, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"layer 0 routing over {S} of {N} chunk rows ({n_docs_s} documents) "
-                      f"+ layer 0 attention ({len(kv)} memory rows + {args.local} local), "
-                      f"scaled x{N / S:.2f} (rows) and x{wl['L']} (layers); "
+            "sample": f"routing of layers 0..{n_layers - 1} over {S} of {N} chunk rows ({n_docs_s} documents) "
+                      f"+ their attention ({mem_rows} memory rows + {args.local} local), "
+                      f"scaled x{N / S:.2f} (rows) and x{wl['L'] / n_layers:.1f} (layers); "
                       f"{t_route + t_attn:.1f} s measured; {1 / t_step:.4f} tokens/s"}
 
 
