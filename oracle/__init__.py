@@ -17,7 +17,9 @@ Sources (the pages the method is taken from):
   host memory fetched on demand.
 * ruixiangma.github.io blog "Memory-Sparse-Attention", 方法 › 稀疏注意力机制
   (fixed-length chunks, mean pooling, cosine top-k documents) and 文档级RoPE.
-* github-eval-reports review of MSA, 核心模块 (head mean first, then token max).
+* github-eval-reports review of MSA, 核心模块 (head mean first, then token max)
+  and 核心能力 › 端到端可训练框架 (one differentiable loop); the blog's 训练策略
+  (generation loss plus an auxiliary routing loss) for the backward.
 
 Every reading taken where the pages are silent is listed in the module that
 takes it.  Parity status of each function is stated in its module docstring.
@@ -30,6 +32,7 @@ from .route import (cosine, chunk_scores, chunk_scores_loops, doc_scores,
                     topk_docs, route, EPS)
 from .gather import gather_rows
 from .attention import sparse_attn, sparse_attn_loops
+from .backward import sparse_attn_lse, sparse_attn_bwd, doc_score_argmax, route_score_bwd
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_to_f64",
@@ -39,4 +42,5 @@ __all__ = [
     "route", "EPS",
     "gather_rows",
     "sparse_attn", "sparse_attn_loops",
+    "sparse_attn_lse", "sparse_attn_bwd", "doc_score_argmax", "route_score_bwd",
 ]
