@@ -297,6 +297,60 @@ msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt,
                            int q_offset, float scale, void* O,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * msa_sparse_attn_lse -- msa_sparse_attn that also saves, per output row, the
+ * statistic its backward recomputes the softmax from.  Same arguments, plus
+ *   lse            device float [B][Tq][Hq]: natural-log log-sum-exp over the
+ *                  row's visible keys of scale * q~.k~ (4-byte aligned).
+ * (Training forward; sources as msa_sparse_attn_bwd.)
+ */
+msa_status msa_sparse_attn_lse(msa_ctx* ctx, msa_dtype dt,
+                               const void* Q, int64_t B, int Tq, int Hq,
+                               const void* KVmem, const int64_t* mem_off,
+                               int64_t mem_rows_cap, int64_t max_rows_per_query,
+                               const void* K_local, const void* V_local, int L, int Hkv,
+                               int q_offset, float scale, void* O, float* lse,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * msa_sparse_attn_bwd -- gradients of msa_sparse_attn with respect to Q, the
+ * memory rows K̄/V̄ and the local K/V, given dO = dLoss/dO.
+ * ([blog] 训练策略: the model is trained with the generation loss, which
+ * reaches these inputs through the sparse attention, plus an auxiliary routing
+ * loss; [rev] 核心能力 › 端到端可训练框架: retrieval and generation form one
+ * differentiable loop.)
+ * With P the softmax of a row, dP_j = dO.v_j, D = dO.O, dS_j = P_j (dP_j - D):
+ *     dV_j = sum_i P_ij dO_i       dk~_j = scale sum_i dS_ij q~_i
+ *     dq~_i = scale sum_j dS_ij k~_j
+ * summed over the G query heads of a KV head; dQ and dK_local are the rotated
+ * gradients turned back by their RoPE angle; memory keys get dk~ itself.
+ *   dt             MSA_BF16 only, head dim 128 (else MSA_ERR_UNSUPPORTED).
+ *   Q .. scale     exactly as passed to the forward.
+ *   O              device [B][Tq][Hq][d]: the forward's output.
+ *   dO             device [B][Tq][Hq][d].
+ *   lse            device float [B][Tq][Hq] from msa_sparse_attn_lse.
+ *   dQ             device [B][Tq][Hq][d] (written).
+ *   dKVmem         device [mem_rows_cap][2][Hkv][d] (dK̄ then dV̄ per row):
+ *                  the rows each query uses are written, others untouched;
+ *                  the row ranges of different queries must not overlap.
+ *   dK_local, dV_local  device [B][L][Hkv][d] (written).
+ *   workspace      device, >= msa_sparse_attn_bwd_workspace_size(...) bytes.
+ * Gradients are bf16, accumulated in fp32; no atomics, so results do not
+ * depend on scheduling.  Outputs must not alias inputs.
+ */
+size_t msa_sparse_attn_bwd_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv,
+                                          int64_t max_rows_per_query, int L);
+
+msa_status msa_sparse_attn_bwd(msa_ctx* ctx, msa_dtype dt,
+                               const void* Q, int64_t B, int Tq, int Hq,
+                               const void* KVmem, const int64_t* mem_off,
+                               int64_t mem_rows_cap, int64_t max_rows_per_query,
+                               const void* K_local, const void* V_local, int L, int Hkv,
+                               int q_offset, float scale,
+                               const void* O, const void* dO, const float* lse,
+                               void* dQ, void* dKVmem, void* dK_local, void* dV_local,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@ EXPORTS = [
     "msa_encode_pool", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
     "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
     "msa_sparse_attn_workspace_size", "msa_sparse_attn",
+    "msa_sparse_attn_lse", "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
 ]
 
 
@@ -61,6 +62,11 @@ _SIGS = {
     "msa_sparse_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
                               P, SZ, P]),
+    "msa_sparse_attn_lse": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
+                                  P, P, SZ, P]),
+    "msa_sparse_attn_bwd_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
+    "msa_sparse_attn_bwd": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32,
+                                  P, P, P, P, P, P, P, P, SZ, P]),
 }
 
 
@@ -254,6 +260,37 @@ def msa_sparse_attn(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local
                                  _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
+
+
+def msa_sparse_attn_lse(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local, q_offset, scale,
+                        O, lse, workspace, stream=None):
+    """msa_sparse_attn plus lse float32 [B, Tq, Hq] (the saved row statistic)."""
+    B, Tq, Hq, d = Q.shape
+    _, L, Hkv, _ = K_local.shape
+    cap = KVmem.shape[0] if KVmem is not None else 0
+    _check(lib().msa_sparse_attn_lse(ctx.handle, _dtype(Q), _ptr(Q), B, Tq, Hq, _ptr(KVmem),
+                                     _ptr(mem_off), cap, max_rows_per_query, _ptr(K_local),
+                                     _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O), _ptr(lse),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def msa_sparse_attn_bwd_workspace_size(dtype, B, Tq, Hq, Hkv, max_rows_per_query, L):
+    return lib().msa_sparse_attn_bwd_workspace_size(dtype, B, Tq, Hq, Hkv, max_rows_per_query, L)
+
+
+def msa_sparse_attn_bwd(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local, q_offset, scale,
+                        O, dO, lse, dQ, dKVmem, dK_local, dV_local, workspace, stream=None):
+    """Gradients: dQ like Q, dKVmem like KVmem, dK_local/dV_local like K_local."""
+    B, Tq, Hq, d = Q.shape
+    _, L, Hkv, _ = K_local.shape
+    cap = KVmem.shape[0] if KVmem is not None else 0
+    _check(lib().msa_sparse_attn_bwd(ctx.handle, _dtype(Q), _ptr(Q), B, Tq, Hq, _ptr(KVmem),
+                                     _ptr(mem_off), cap, max_rows_per_query, _ptr(K_local),
+                                     _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O), _ptr(dO),
+                                     _ptr(lse), _ptr(dQ), _ptr(dKVmem), _ptr(dK_local), _ptr(dV_local),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
 
 
 def workspace(nbytes, device="cuda"):

@@ -429,12 +429,14 @@ size_t msa_sparse_attn_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, i
     return msa::attn_workspace(dt, B, Tq, Hq, Hkv, 128, max_rows_per_query, L, cus);
 }
 
-msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
-                           const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
-                           int64_t max_rows_per_query, const void* K_local, const void* V_local, int L,
-                           int Hkv, int q_offset, float scale, void* O, void* workspace, size_t ws_bytes,
-                           hipStream_t stream) {
-    const char* fn = "msa_sparse_attn";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the forward and backward attention calls.
+msa_status check_attn(const char* fn, msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                      const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap, int64_t max_rows_per_query,
+                      const void* K_local, const void* V_local, int L, int Hkv, int q_offset, float scale) {
     if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
     if (!dtype_ok(dt)) return fail(MSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dt));
     if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || L < 1)
@@ -450,11 +452,23 @@ msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B,
         return fail(MSA_ERR_INVALID_ARG, "%s: negative row count", fn);
     if (B * Tq > 65535LL * 1024) return fail(MSA_ERR_UNSUPPORTED, "%s: B*Tq too large", fn);
     if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
-    if (!Q || !mem_off || !K_local || !V_local || !O || (mem_rows_cap > 0 && !KVmem))
+    if (!Q || !mem_off || !K_local || !V_local || (mem_rows_cap > 0 && !KVmem))
         return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (!aligned16(K_local) || !aligned16(V_local) || (KVmem && !aligned16(KVmem)) || !aligned16(Q) ||
-        !aligned16(O))
+    if (!aligned16(K_local) || !aligned16(V_local) || (KVmem && !aligned16(KVmem)) || !aligned16(Q))
         return fail(MSA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    return MSA_OK;
+}
+
+msa_status sparse_attn_fwd(const char* fn, msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                           const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
+                           int64_t max_rows_per_query, const void* K_local, const void* V_local, int L, int Hkv,
+                           int q_offset, float scale, void* O, float* lse, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    msa_status s = check_attn(fn, ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap, max_rows_per_query,
+                              K_local, V_local, L, Hkv, q_offset, scale);
+    if (s != MSA_OK) return s;
+    if (!O) return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned16(O)) return fail(MSA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
     const size_t need = msa::attn_workspace(dt, B, Tq, Hq, Hkv, ctx->head_dim, max_rows_per_query, L,
                                             ctx->num_cus);
     if (!workspace || !aligned256(workspace) || ws_bytes < need)
@@ -462,11 +476,81 @@ msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B,
                     ws_bytes);
     msa::AttnArgs a{dt, Q, B, Tq, Hq, Hkv, ctx->head_dim, L, KVmem, mem_off, mem_rows_cap,
                     max_rows_per_query, K_local, V_local, q_offset, scale, O, workspace, ws_bytes,
-                    ctx->rope_cs, ctx->max_pos, ctx->num_cus};
+                    ctx->rope_cs, ctx->max_pos, ctx->num_cus, lse};
     DeviceGuard dg(ctx->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_sparse_attn: hipSetDevice");
     hipError_t e = msa::launch_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn: launch");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                           const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
+                           int64_t max_rows_per_query, const void* K_local, const void* V_local, int L,
+                           int Hkv, int q_offset, float scale, void* O, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    return sparse_attn_fwd("msa_sparse_attn", ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap,
+                           max_rows_per_query, K_local, V_local, L, Hkv, q_offset, scale, O, nullptr, workspace,
+                           ws_bytes, stream);
+}
+
+msa_status msa_sparse_attn_lse(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                               const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
+                               int64_t max_rows_per_query, const void* K_local, const void* V_local, int L,
+                               int Hkv, int q_offset, float scale, void* O, float* lse, void* workspace,
+                               size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "msa_sparse_attn_lse";
+    if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(MSA_ERR_INVALID_ARG, "%s: lse must be a non-NULL, 4-byte aligned device pointer", fn);
+    return sparse_attn_fwd(fn, ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap, max_rows_per_query, K_local,
+                           V_local, L, Hkv, q_offset, scale, O, lse, workspace, ws_bytes, stream);
+}
+
+size_t msa_sparse_attn_bwd_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv,
+                                          int64_t max_rows_per_query, int L) {
+    if (dt != MSA_BF16 || B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || max_rows_per_query < 0 || L < 1) return 0;
+    return msa::attn_bwd_workspace(B, Tq, Hq, Hkv, max_rows_per_query, L);
+}
+
+msa_status msa_sparse_attn_bwd(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                               const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
+                               int64_t max_rows_per_query, const void* K_local, const void* V_local, int L,
+                               int Hkv, int q_offset, float scale, const void* O, const void* dO,
+                               const float* lse, void* dQ, void* dKVmem, void* dK_local, void* dV_local,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "msa_sparse_attn_bwd";
+    msa_status s = check_attn(fn, ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap, max_rows_per_query,
+                              K_local, V_local, L, Hkv, q_offset, scale);
+    if (s != MSA_OK) return s;
+    if (dt != MSA_BF16 || ctx->head_dim != 128)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: the backward takes bf16 with head dim 128", fn);
+    if (!O || !dO || !lse || !dQ || !dK_local || !dV_local || (mem_rows_cap > 0 && !dKVmem))
+        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned16(O) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK_local) || !aligned16(dV_local) ||
+        (dKVmem && !aligned16(dKVmem)) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(MSA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned (lse 4-byte)", fn);
+    const size_t need = msa::attn_bwd_workspace(B, Tq, Hq, Hkv, max_rows_per_query, L);
+    if (!workspace || !aligned256(workspace) || ws_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
+                    ws_bytes);
+    msa::AttnBwdArgs a{};
+    a.f = msa::AttnArgs{dt, Q, B, Tq, Hq, Hkv, ctx->head_dim, L, KVmem, mem_off, mem_rows_cap,
+                        max_rows_per_query, K_local, V_local, q_offset, scale, const_cast<void*>(O), workspace,
+                        ws_bytes, ctx->rope_cs, ctx->max_pos, ctx->num_cus, nullptr};
+    a.dO = dO;
+    a.lse = lse;
+    a.dQ = dQ;
+    a.dKVmem = dKVmem;
+    a.dK_local = dK_local;
+    a.dV_local = dV_local;
+    DeviceGuard dg(ctx->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_sparse_attn_bwd: hipSetDevice");
+    hipError_t e = msa::launch_attn_bwd(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_bwd: launch");
     return ok();
 }
 

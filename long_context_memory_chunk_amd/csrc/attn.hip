@@ -19,7 +19,8 @@
 //                                        for HBM bandwidth.
 //   attn_split_kernel                    any dtype, d in {64, 128}, any G.
 // The last two write partial (m, l, o) per key split; attn_combine merges
-// them exactly.
+// them exactly.  Every path can also write each row's log-sum-exp (the
+// statistic the backward in attn_bwd.hip recomputes the softmax from).
 //
 // attn_split (vector ALU, any Tq): a workgroup owns one (b, i, kv head g) and
 // the G = Hq/Hkv query heads that read g, so every key row loaded is used G
@@ -511,7 +512,7 @@ constexpr int kMaxParts = 1024;
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml, int P,
-                                                         T* __restrict__ O) {
+                                                         T* __restrict__ O, float* __restrict__ lse) {
     __shared__ float s_w[kMaxParts];
     __shared__ float s_red[2][D / 64];
     const int64_t row = blockIdx.x;   // (b, i, h)
@@ -550,6 +551,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     }
     for (; p < P; ++p) acc += s_w[p] * part_o[(row * P + p) * D + dd];
     Elem<T>::store(O, row * D + dd, acc / l);
+    if (lse != nullptr && dd == 0) lse[row] = m + logf(l);
 }
 
 // Chunks per workgroup of attn_decode_kernel: about four workgroups per CU,
@@ -596,7 +598,7 @@ hipError_t launch_split_g(const AttnArgs& a, float* part_o, float2* part_ml, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(D), 0, st,
-                       part_o, part_ml, P, static_cast<T*>(a.O));
+                       part_o, part_ml, P, static_cast<T*>(a.O), a.lse);
     return hipGetLastError();
 }
 
@@ -610,7 +612,7 @@ hipError_t launch_decode_g(const AttnArgs& a, float* part_o, float2* part_ml, De
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
-                       part_o, part_ml, pl.P, static_cast<bf16_t*>(a.O));
+                       part_o, part_ml, pl.P, static_cast<bf16_t*>(a.O), a.lse);
     return hipGetLastError();
 }
 

@@ -61,18 +61,8 @@ constexpr int kTileUnits = BK * DH / 8;    // 16-byte units of one K (or V) tile
 constexpr int kStages = 4;                 // LDS ring: three tiles in flight behind the one in use
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;               // raise the running max only past m + 8 (a factor 2^8)
-
-// Memory rows of query b, clamped as in attn.hip.
-__device__ __forceinline__ void mem_range(const int64_t* __restrict__ mem_off, int64_t b, int64_t cap,
-                                          int64_t max_rows, int64_t& r0, int64_t& M) {
-    int64_t a = mem_off[b], e = mem_off[b + 1];
-    a = a < 0 ? 0 : (a > cap ? cap : a);
-    e = e < a ? a : (e > cap ? cap : e);
-    if (e - a > max_rows) e = a + max_rows;
-    r0 = a;
-    M = e - a;
-}
 
 // Position in a 16-key group -> key in that group (the score accumulator's order).
 __device__ __forceinline__ int acc_key(int p) {
@@ -166,7 +156,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_prefill_kernel(
     const uint16_t* __restrict__ Q, int Tq, int Hq, int hkv, const int64_t* __restrict__ mem_off, int64_t cap,
     int64_t max_rows, int L, int q_offset, float qscale, const float2* __restrict__ rope, int max_pos,
     int64_t KP, const u32x4* __restrict__ Kc, const u32x4* __restrict__ Vt, uint16_t* __restrict__ O, int n_qt,
-    int64_t B) {
+    int64_t B, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) u32x4 sK[kStages * kTileUnits];
     __shared__ __attribute__((aligned(16))) u32x4 sV[kStages * kTileUnits];
 
@@ -383,7 +373,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_prefill_kernel(
         }
     }
 
-    // ---- normalise and store
+    // ---- normalise and store (and the row's log-sum-exp, natural log, if asked)
+    if (lse != nullptr && half == 0 && q_valid)
+        lse[(b * Tq + qi) * Hq + h] = (m_run + log2f(l_run)) * kLn2;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int qr = (i / 4) * 8 + half * 4 + (i % 4);
@@ -430,7 +422,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
                        static_cast<const uint16_t*>(a.Q), a.Tq, a.Hq, a.Hkv, a.mem_off, a.mem_rows_cap, a.max_rows,
                        a.L, a.q_offset, a.scale * kLog2e, a.rope_cs, a.max_pos, KP,
                        static_cast<const u32x4*>(Kc), static_cast<const u32x4*>(Vt), static_cast<uint16_t*>(a.O),
-                       n_qt, a.B);
+                       n_qt, a.B, a.lse);
     return hipGetLastError();
 }
 

@@ -70,7 +70,33 @@ struct AttnArgs {
     const float2* rope_cs;
     int max_pos;
     int num_cus;
+    float* lse = nullptr;   // optional [B][Tq][Hq]: natural-log log-sum-exp of each row's scaled logits
 };
+
+// Memory rows of query b: mem_off[b] .. mem_off[b+1]-1 clamped to [0, cap] and
+// to max_rows rows.
+__device__ __forceinline__ void mem_range(const int64_t* __restrict__ mem_off, int64_t b, int64_t cap,
+                                          int64_t max_rows, int64_t& r0, int64_t& M) {
+    int64_t a = mem_off[b], e = mem_off[b + 1];
+    a = a < 0 ? 0 : (a > cap ? cap : a);
+    e = e < a ? a : (e > cap ? cap : e);
+    if (e - a > max_rows) e = a + max_rows;
+    r0 = a;
+    M = e - a;
+}
+
+// Backward of the attention (attn_bwd.hip): bf16, d = 128.
+struct AttnBwdArgs {
+    AttnArgs f;             // the forward's arguments (O read, not written; ws is the backward's)
+    const void* dO;         // [B][Tq][Hq][d]
+    const float* lse;       // [B][Tq][Hq], as the forward saved it
+    void* dQ;               // [B][Tq][Hq][d]
+    void* dKVmem;           // [mem_rows_cap][2][Hkv][d]: rows of each query's memory written
+    void* dK_local;         // [B][L][Hkv][d]
+    void* dV_local;
+};
+size_t attn_bwd_workspace(int64_t B, int Tq, int Hq, int Hkv, int64_t max_rows, int L);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
 constexpr int kMaxGatherB = 1024;
 size_t gather_device_workspace(int64_t B);

@@ -1,0 +1,214 @@
+"""Backward of the sparse attention on the GPU vs the oracle, through the C ABI.
+
+Tolerances (stated where used):
+  lse      2e-2 absolute in bf16, 1e-3 in fp32: the logits the forward
+           exponentiates carry the bf16 rounding of the rotated, scaled
+           query and of the rotated local keys (relative 2^-9 per element), a
+           random-sign error of about sqrt(d) * 2^-9 * scale |q_c k_c| ~ 3e-3
+           on unit-variance inputs; the log-sum-exp inherits at most the
+           largest logit error.
+  grads    2e-2 of max |ref| per gradient tensor (the bf16 attention bar):
+           the GPU recomputes P from bf16 operands and the bf16 forward output
+           (D = dO . O), contracts bf16 P, dS, dO, Q and K with fp32
+           accumulation and stores bf16, each a relative 2^-9 rounding.
+"""
+
+import numpy as np
+import pytest
+
+import msa_synth
+import oracle
+from tests import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"bf16": 2e-2, "f32": 1e-3}
+GRAD_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def torch_mod(gpu):
+    import torch
+    return torch
+
+
+@pytest.fixture(scope="module")
+def msa(gpu):
+    import long_context_memory_chunk_amd as m
+    m.lib()   # raises if the library is missing: no fallback
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctx128(msa):
+    c = msa.msa_ctx_create(0, 128, 1e6, 16384)
+    yield c
+    c.close()
+
+
+@pytest.fixture(scope="module")
+def ctx64(msa):
+    c = msa.msa_ctx_create(0, 64, 1e4, 4096)
+    yield c
+    c.close()
+
+
+def _inputs(seed, dtype, d, Hq, Hkv, B, Tq, L, rows):
+    mem_off = msa_synth.prefix_offsets(rows)
+    M = int(mem_off[-1])
+    return dict(mem_off=mem_off, M=M,
+                Q=W.draw(seed, 1, (B, Tq, Hq, d), dtype),
+                KV=W.draw(seed, 2, (max(M, 1), 2, Hkv, d), dtype),
+                Kl=W.draw(seed, 3, (B, L, Hkv, d), dtype),
+                Vl=W.draw(seed, 4, (B, L, Hkv, d), dtype),
+                dO=W.draw(seed, 5, (B, Tq, Hq, d), dtype))
+
+
+def _forward_lse(torch, msa, ctx, x, dtype, rows, qoff):
+    B, Tq, Hq, d = x["Q"].shape
+    L, Hkv = x["Kl"].shape[1:3]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = {k: W.dev(x[k], dtype) for k in ("Q", "KV", "Kl", "Vl")}
+    O = torch.full((B, Tq, Hq, d), float("nan"), dtype=tdt, device="cuda")
+    lse = torch.full((B, Tq, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    mo = torch.from_numpy(x["mem_off"]).cuda()
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1 if dtype == "bf16" else 0, B, Tq, Hq, Hkv,
+                                                          max(rows), L))
+    msa.msa_sparse_attn_lse(ctx, dev["Q"], dev["KV"], mo, max(rows), dev["Kl"], dev["Vl"], qoff,
+                            W.scale_of(d), O, lse, ws)
+    return dev, mo, O, lse
+
+
+LSE_CASES = [
+    # dtype, d, Hq, Hkv, B, Tq, L, rows per query, q_offset
+    ("bf16", 128, 32, 8, 1, 256, 256, [152], 16),     # matrix-core prefill path
+    ("bf16", 128, 32, 8, 2, 200, 500, [0, 300], 16),  # matrix cores, partial tile
+    ("bf16", 128, 32, 8, 3, 1, 700, [30, 0, 300], 16),  # decode path
+    ("f32", 64, 4, 2, 1, 32, 32, [64], 4),            # generic split path
+    ("bf16", 128, 16, 1, 1, 7, 19, [260], 33),        # generic split path, G = 16
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,L,rows,qoff", LSE_CASES)
+def test_sparse_attn_lse_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, L, rows, qoff):
+    torch = torch_mod
+    ctx = ctx128 if d == 128 else ctx64
+    x = _inputs(91, dtype, d, Hq, Hkv, B, Tq, L, rows)
+    _, _, O, lse = _forward_lse(torch, msa, ctx, x, dtype, rows, qoff)
+    torch.cuda.synchronize()
+    kv = W.widen(x["KV"], dtype)
+    args = (W.widen(x["Q"], dtype), kv[:, 0], kv[:, 1], x["mem_off"], W.widen(x["Kl"], dtype),
+            W.widen(x["Vl"], dtype), qoff, W.scale_of(d), ctx.rope_theta)
+    ref_lse = oracle.sparse_attn_lse(*args)
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= LSE_TOL[dtype]
+    ref_o = oracle.sparse_attn(*args)            # the output is unchanged by saving lse
+    assert np.max(np.abs(W.widen(W.host_bits(O), dtype) - ref_o)) <= (2e-2 if dtype == "bf16" else 1e-3)
+
+
+BWD_CASES = [
+    # Hq, Hkv, B, Tq, L, rows per query, q_offset
+    (32, 8, 1, 64, 600, [250], 32),        # G = 4, several key tiles, causal edge
+    (32, 8, 2, 200, 500, [0, 300], 16),    # partial query tile, one query without memory
+    (8, 8, 1, 130, 130, [70], 8),          # G = 1, Tq = L, ragged tiles
+    (16, 1, 1, 96, 1000, [64], 16),        # G = 16: four workgroups per query tile
+    (64, 8, 2, 1, 700, [90, 200], 16),     # one query token (decode shape), G = 8
+    (4, 2, 1, 33, 40, [5], 4),             # G = 2, one token past a tile
+    (32, 8, 2, 1, 1, [0, 5], 16),          # one local key; one query sees only it
+    (32, 8, 1, 300, 300, [1], 16),         # Tq = L, one memory row
+]
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+@pytest.mark.parametrize("Hq,Hkv,B,Tq,L,rows,qoff", BWD_CASES)
+def test_sparse_attn_bwd_parity(torch_mod, msa, ctx128, Hq, Hkv, B, Tq, L, rows, qoff):
+    torch = torch_mod
+    d = 128
+    print(f"\nbwd case Hq={Hq} Hkv={Hkv} B={B} Tq={Tq} L={L} rows={rows}", flush=True)
+    x = _inputs(93, "bf16", d, Hq, Hkv, B, Tq, L, rows)
+    dev, mo, O, lse = _forward_lse(torch, msa, ctx128, x, "bf16", rows, qoff)
+    dO = W.dev_bf16(x["dO"])
+    nan = lambda t: torch.full_like(t, float("nan"))
+    dQ, dKV, dKl, dVl = nan(dev["Q"]), nan(dev["KV"]), nan(dev["Kl"]), nan(dev["Vl"])
+    ws = msa.workspace(msa.msa_sparse_attn_bwd_workspace_size(1, B, Tq, Hq, Hkv, max(rows), L))
+    msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, max(rows), dev["Kl"], dev["Vl"], qoff,
+                            W.scale_of(d), O, dO, lse, dQ, dKV, dKl, dVl, ws)
+    torch.cuda.synchronize()
+    kv = W.widen(x["KV"], "bf16")
+    ref = oracle.sparse_attn_bwd(W.widen(x["Q"], "bf16"), kv[:, 0], kv[:, 1], x["mem_off"],
+                                 W.widen(x["Kl"], "bf16"), W.widen(x["Vl"], "bf16"), qoff, W.scale_of(d),
+                                 ctx128.rope_theta, W.widen(x["dO"], "bf16"))
+    dkv = W.widen(W.host_bits(dKV), "bf16")
+    M = x["M"]
+    got = [W.widen(W.host_bits(dQ), "bf16"), dkv[:M, 0], dkv[:M, 1],
+           W.widen(W.host_bits(dKl), "bf16"), W.widen(W.host_bits(dVl), "bf16")]
+    want = [ref[0], ref[1][:M], ref[2][:M], ref[3], ref[4]]
+    for name, g, r in zip(["dQ", "dK_mem", "dV_mem", "dK_local", "dV_local"], got, want):
+        if r.size == 0:
+            continue
+        assert np.all(np.isfinite(g)), name
+        assert _rel(g, r) <= GRAD_TOL, (name, _rel(g, r))
+
+
+def test_sparse_attn_bwd_leaves_other_memory_rows_alone(torch_mod, msa, ctx128):
+    # query 0 reads rows 10..29 and query 1 rows 30..69 of an 80-row buffer:
+    # rows 0..9 and 70..79 belong to nobody and must keep their contents
+    torch = torch_mod
+    x = _inputs(95, "bf16", 128, 32, 8, 2, 40, 80, [20, 40])
+    mem_off = np.array([10, 30, 70], dtype=np.int64)
+    KV = W.draw(95, 6, (80, 2, 8, 128), "bf16")
+    Q, Kl, Vl, KVd = W.dev_bf16(x["Q"]), W.dev_bf16(x["Kl"]), W.dev_bf16(x["Vl"]), W.dev_bf16(KV)
+    mo = torch.from_numpy(mem_off).cuda()
+    O = torch.empty_like(Q)
+    lse = torch.empty((2, 40, 32), dtype=torch.float32, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 2, 40, 32, 8, 40, 80))
+    msa.msa_sparse_attn_lse(ctx128, Q, KVd, mo, 40, Kl, Vl, 16, W.scale_of(128), O, lse, ws)
+    dQ, dKl, dVl = torch.empty_like(Q), torch.empty_like(Kl), torch.empty_like(Vl)
+    dKV = torch.full_like(KVd, 1.0)
+    sentinel = 0x3F80                                     # bf16 1.0
+    wsb = msa.workspace(msa.msa_sparse_attn_bwd_workspace_size(1, 2, 40, 32, 8, 40, 80))
+    msa.msa_sparse_attn_bwd(ctx128, Q, KVd, mo, 40, Kl, Vl, 16, W.scale_of(128), O, W.dev_bf16(x["dO"]), lse,
+                            dQ, dKV, dKl, dVl, wsb)
+    torch.cuda.synchronize()
+    bits = W.host_bits(dKV)
+    assert np.all(bits[:10] == sentinel) and np.all(bits[70:] == sentinel)
+    kv = W.widen(KV, "bf16")
+    ref = oracle.sparse_attn_bwd(W.widen(x["Q"], "bf16"), kv[:, 0], kv[:, 1], mem_off,
+                                 W.widen(x["Kl"], "bf16"), W.widen(x["Vl"], "bf16"), 16, W.scale_of(128),
+                                 ctx128.rope_theta, W.widen(x["dO"], "bf16"))
+    got = W.widen(bits, "bf16")
+    assert _rel(got[10:70, 0], ref[1][10:70]) <= GRAD_TOL
+    assert _rel(got[10:70, 1], ref[2][10:70]) <= GRAD_TOL
+
+
+def test_sparse_attn_bwd_is_deterministic(torch_mod, msa, ctx128):
+    torch = torch_mod
+    x = _inputs(97, "bf16", 128, 32, 8, 1, 96, 300, [100])
+    dev, mo, O, lse = _forward_lse(torch, msa, ctx128, x, "bf16", [100], 16)
+    ws = msa.workspace(msa.msa_sparse_attn_bwd_workspace_size(1, 1, 96, 32, 8, 100, 300))
+    outs = []
+    for _ in range(2):
+        g = [torch.empty_like(dev["Q"]), torch.empty_like(dev["KV"]), torch.empty_like(dev["Kl"]),
+             torch.empty_like(dev["Vl"])]
+        msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, 100, dev["Kl"], dev["Vl"], 16,
+                                W.scale_of(128), O, W.dev_bf16(x["dO"]), lse, *g, ws)
+        outs.append([W.host_bits(t) for t in g])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_sparse_attn_bwd_rejects_unsupported(torch_mod, msa, ctx64):
+    torch = torch_mod
+    x = _inputs(99, "bf16", 64, 4, 2, 1, 4, 8, [3])
+    dev = {k: W.dev_bf16(x[k]) for k in ("Q", "KV", "Kl", "Vl", "dO")}
+    lse = torch.zeros((1, 4, 4), dtype=torch.float32, device="cuda")
+    mo = torch.tensor([0, 3], dtype=torch.int64, device="cuda")
+    ws = msa.workspace(1 << 20)
+    with pytest.raises(msa.MsaError) as e:                       # head dim 64
+        msa.msa_sparse_attn_bwd(ctx64, dev["Q"], dev["KV"], mo, 3, dev["Kl"], dev["Vl"], 4, 0.125,
+                                dev["Q"], dev["dO"], lse, torch.empty_like(dev["Q"]),
+                                torch.empty_like(dev["KV"]), torch.empty_like(dev["Kl"]),
+                                torch.empty_like(dev["Vl"]), ws)
+    assert e.value.status == msa.MSA_ERR_UNSUPPORTED
