@@ -84,11 +84,12 @@ def parse():
                    help="chunk rows per layer in the oracle sample (0: the whole layer)")
     p.add_argument("--cpu-sample-layers", type=int, default=4, help="routing layers in the oracle sample")
     p.add_argument("--workload", choices=["decode100m", "chunk100m", "reuse100m", "prefill8k", "batch32", "encode10m",
-                                          "hbmcopy"],
+                                          "train8k", "hbmcopy"],
                    default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
                         "prefill8k / batch32: extra measurements on the 10M-token bank; "
                         "encode10m: the offline encode of one layer of the 10M-token bank; "
+                        "train8k: forward (saving log-sum-exp) + backward of the prefill-shaped attention; "
                         "hbmcopy: a plain 4 GiB device-to-device copy, the known-size kernel that "
                         "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--gen-tokens", type=int, default=64, help="reuse100m: tokens generated after assembly")
@@ -524,6 +525,69 @@ def encode_10m_inputs(seed, torch, msa_synth, device_fill):
     return lens, tok, raw
 
 
+def run_train8k(args, torch, msa, msa_synth, device_fill, W):
+    """The training pass of one routing layer's sparse attention at the
+    prefill shape: 8,192 query tokens over [242 memory rows ; 8,192 local
+    tokens] (242 = the rows the top-32 gather of the 10M-token bank yields),
+    the forward saving each row's log-sum-exp, then the backward (dQ, dK̄,
+    dV̄, dK, dV)."""
+    seed, T, M, qoff = args.seed, 8192, 242, 32
+    Q = torch.empty((1, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    dO = torch.empty_like(Q)
+    KV = torch.empty((M, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    Kl = torch.empty((1, T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    Vl = torch.empty_like(Kl)
+    for t_, st in ((Q, 720), (KV, 721), (Kl, 722), (Vl, 723), (dO, 724)):
+        device_fill.fill_counter_bf16(t_, seed, st, 0)
+    ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+    mo = torch.tensor([0, M], dtype=torch.int64, device="cuda")
+    O = torch.empty_like(Q)
+    lse = torch.empty((1, T, Hq), dtype=torch.float32, device="cuda")
+    dQ, dKV, dKl, dVl = torch.empty_like(Q), torch.empty_like(KV), torch.empty_like(Kl), torch.empty_like(Vl)
+    ws_f = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, T, Hq, Hkv, M, T))
+    ws_b = msa.workspace(msa.msa_sparse_attn_bwd_workspace_size(1, 1, T, Hq, Hkv, M, T))
+    scale = 1.0 / math.sqrt(D)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    f_s, f_e, b_e = ev(), ev(), ev()
+    t_f, t_b, t_step = [], [], []
+    for it in range(args.warmup + args.steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        f_s.record()
+        msa.msa_sparse_attn_lse(ctx, Q, KV, mo, M, Kl, Vl, qoff, scale, O, lse, ws_f)
+        f_e.record()
+        msa.msa_sparse_attn_bwd(ctx, Q, KV, mo, M, Kl, Vl, qoff, scale, O, dO, lse, dQ, dKV, dKl, dVl, ws_b)
+        b_e.record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            t_step.append(time.perf_counter() - t0)
+            t_f.append(f_s.elapsed_time(f_e) / 1e3)
+            t_b.append(f_e.elapsed_time(b_e) / 1e3)
+    finite = all(bool(torch.isfinite(t_.float()).all()) for t_ in (O, lse, dQ, dKV, dKl, dVl))
+    pairs = M * T + T * (T + 1) / 2                   # (token, visible key) pairs per head
+    fwd_flop = 4.0 * D * Hq * pairs                   # S = Q K^T, O = P V
+    bwd_flop = 10.0 * D * Hq * pairs                  # S, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K
+    tf, tb, ts = float(np.mean(t_f)), float(np.mean(t_b)), float(np.mean(t_step))
+    ctx.close()
+    return {
+        "metric": "sparse-attention training pass on the matrix cores (8,192 tokens over [242 memory rows ; "
+                  "8,192 local], one layer)",
+        "value": round(bwd_flop / tb / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ts * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "forward with saved log-sum-exp + backward of the causal prefill attention, "
+                               "8,192 query tokens, 242 memory rows, 8,192 local keys, Hq 32, Hkv 8, d 128",
+                   "tokens": T, "memory_rows": M, "Hq": Hq, "Hkv": Hkv, "head_dim": D},
+        "fwd_ms": round(tf * 1e3, 4), "fwd_TFLOPs": round(fwd_flop / tf / 1e12, 1),
+        "bwd_ms": round(tb * 1e3, 4), "bwd_TFLOPs": round(bwd_flop / tb / 1e12, 1),
+        "outputs_finite": finite,
+        "roofline": {"bound": "mfma", "achieved": round(bwd_flop / tb / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_flop / tb / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "msa_sparse_attn_bwd (four kernels)",
+                     "flop_per_launch": bwd_flop},
+    }
+
+
 def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
     """Offline encode of one layer of the 10M-token bank: raw K, V, Kr
     [10M, 8, 128] bf16 (61.4 GB) pooled into KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128]
@@ -706,7 +770,7 @@ def main():
     msa.lib()
     if args.workload not in ("decode100m", "chunk100m"):
         fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "encode10m": run_encode10m,
-              "hbmcopy": run_hbmcopy, "reuse100m": run_reuse100m}[args.workload]
+              "hbmcopy": run_hbmcopy, "reuse100m": run_reuse100m, "train8k": run_train8k}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
         print(json.dumps(out), flush=True)
         ok = out.get("planted_recovered", out.get("planted_recovered_all", out.get(

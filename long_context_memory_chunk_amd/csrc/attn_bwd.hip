@@ -33,15 +33,21 @@
 //   read below hits distinct LDS banks across each 16 lanes, and a tile is
 //   staged into LDS as one flat 8 KB copy.
 //
-//   bwd_dkdv    a workgroup (4 waves) owns 128 keys of one (b, KV head); wave w
-//               keeps its 32 keys' K and V as matrix-core operands in registers
-//               and accumulates their dK and dV there.  It walks the query
-//               tiles of the G query heads from the first token that sees its
-//               keys, each staged in LDS by direct global->LDS copies one tile
-//               ahead, and per 32 x 32 block runs S = Q K^T and dP = dO V^T on
+//   bwd_dkdv    a workgroup (8 waves) owns 128 keys of one (b, KV head).  Waves
+//               0..3 form dV and waves 4..7 dK, wave w taking keys
+//               32 (w % 4) .. +31, so a SIMD runs one wave of each role and
+//               each wave holds only its role's accumulators (32 x 128 fp32)
+//               next to its keys' K (and, for dK, V) as matrix-core operands:
+//               everything stays in the 256 registers of two waves per SIMD.
+//               The workgroup walks the query tiles that can see its keys from
+//               the last one down, the G query heads of a tile together (so the
+//               workgroups of one KV head running at the same time read the
+//               same tiles, from L2), each staged in LDS by direct
+//               global->LDS copies one tile ahead.  Per 32 x 32 block a wave
+//               runs S = Q K^T (and, for dK, dP = dO V^T) on
 //               v_mfma_f32_32x32x16_bf16 (keys along the accumulator's
-//               columns), forms P and dS in registers, then dV += P^T dO and
-//               dK += dS^T Q against the transposed tiles.  A k-step takes its
+//               columns), forms P (or dS) in registers, then dV += P^T dO (or
+//               dK += dS^T Q) against the transposed tile.  A k-step takes its
 //               16 queries in the order the accumulator holds them ({16k + 4u
 //               .. +3, 16k + 8 + 4u .. +3} for lane half u), which is two
 //               8-byte units of a transposed row, so P and dS need no shuffle.
@@ -51,9 +57,10 @@
 //               wave keeps its Q and dO as operands and walks the key tiles its
 //               tokens can see: S^T = K Q^T and dP^T = V dO^T (tokens along the
 //               columns), then dQ^T += K^T dS^T.
-// dQ is computed apart from dK/dV (two more matrix products per block) so that
-// no gradient is accumulated with atomics: every output element is written once,
-// in bf16, and the result does not depend on scheduling.  Workgroups take the
+// S is formed twice in bwd_dkdv (once per role) and dQ apart from dK/dV (S and
+// dP again), so that no gradient is accumulated with atomics: every output
+// element is written once, in bf16, and the result does not depend on
+// scheduling.  Workgroups take the
 // heaviest tiles first; when B * Hkv is a multiple of the 8 XCDs, all
 // workgroups of one (b, KV head) share an XCD and its L2.
 #include "launch.hpp"
@@ -71,6 +78,7 @@ constexpr int kTile = RB * DH / 8;           // 16-byte units of a tile: 512 (8 
 constexpr int kStat = 16;                    // 16-byte units of a query tile's statistics (64 floats)
 constexpr int kKeysWg = 128;                 // keys per bwd_dkdv workgroup (4 waves x 32)
 constexpr int kStageQ = 4 * kTile + kStat;   // one bwd_dkdv stage: Q, Q^T, dO, dO^T, statistics
+constexpr int kStagesQ = 2;                  // bwd_dkdv: tile it in use while tile it+1 arrives
 constexpr int kStageK = 3 * kTile;           // one bwd_dq stage: K, K^T, V
 constexpr int PST = DH + 8;                  // LDS staging row stride (bf16) of the prep kernels
 constexpr float kLog2e = 1.4426950408889634f;
@@ -227,13 +235,13 @@ __device__ __forceinline__ bf16x8 pack_operand(const float* v) {
     return __builtin_bit_cast(bf16x8, pack8(v));
 }
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const u32x4* __restrict__ QB, const u32x4* __restrict__ QT, const u32x4* __restrict__ OB,
     const u32x4* __restrict__ OT, const u32x4* __restrict__ ST, const u32x4* __restrict__ KB,
     const u32x4* __restrict__ VB, const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows, int Tq,
     int Hq, int hkv, int L, int q_offset, const float2* __restrict__ rope, int max_pos, int nqb, int nkb,
     int64_t B, uint16_t* __restrict__ dKVmem, uint16_t* __restrict__ dKl, uint16_t* __restrict__ dVl) {
-    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2 * kStageQ];
+    __shared__ __attribute__((aligned(16))) u32x4 sbuf[kStagesQ * kStageQ];
     const int64_t n_bg = B * hkv;
     const int kt = int(blockIdx.x / n_bg);          // key tiles in order: the first (heaviest) first
     const int64_t bg = blockIdx.x % n_bg;
@@ -241,6 +249,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int g = int(bg % hkv);
     const int tid = threadIdx.x, lane = tid % kWave, half = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const bool kside = wave >= 4;                   // waves 4..7 form dK, waves 0..3 dV
+    const int kq = wave % 4;                        // the wave's quarter of the 128 keys
     int64_t r0, M;
     mem_range(mem_off, b, cap, max_rows, r0, M);
     const int64_t n_keys = M + L;
@@ -249,43 +259,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int G = Hq / hkv;
     const int64_t shift = M + (L - Tq);             // token i sees keys 0 .. shift + i
     const int qb0 = k0 <= shift ? 0 : int((k0 - shift) / RB);
-    const int per_head = nqb - qb0;
-    const int n_it = G * per_head;
-    const int64_t kw0 = k0 + 32 * wave;             // the wave's first key
+    const int n_it = G * (nqb - qb0);
+    const int64_t kw0 = k0 + 32 * kq;               // the wave's first key
     const int qbw = kw0 <= shift ? 0 : int((kw0 - shift) / RB);   // the wave's first query tile
+    const int wave_its = G * (nqb - qbw);           // the wave works on the first wave_its tiles of the walk
     const int64_t kcol = kw0 + lane % 32;           // this lane's key (a column of S)
 
+    // K (both roles, for S) and V (dK role, for dP) of the wave's 32 keys as B operands
     bf16x8 kf[8], vf[8];
     {
-        const int64_t tk = (bg * nkb + kt * 4 + wave) * kTile;
+        const int64_t tk = (bg * nkb + kt * 4 + kq) * kTile;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             kf[ks] = __builtin_bit_cast(bf16x8, KB[tk + row_unit(lane % 32, 2 * ks + half)]);
-            vf[ks] = __builtin_bit_cast(bf16x8, VB[tk + row_unit(lane % 32, 2 * ks + half)]);
+            vf[ks] = kside ? __builtin_bit_cast(bf16x8, VB[tk + row_unit(lane % 32, 2 * ks + half)]) : kf[ks];
         }
     }
-    f32x16 dk[4], dv[4];
+    f32x16 acc[4];                                  // dV (waves 0..3) or dK (waves 4..7)
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dk[n][i] = dv[n][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
 
     const uint32_t lds0 = lds_addr(sbuf);
+    // walk order: query tiles from the last down to qb0, the G heads of a tile
+    // together, so the workgroups of one (b, KV head) running at the same time
+    // read the same tiles and share them in L2
     auto dma = [&](int it) {
-        const int h = g * G + it / per_head, qb = qb0 + it % per_head;
+        const int h = g * G + it % G, qb = nqb - 1 - it / G;
         const int64_t qt = (b * Hq + h) * nqb + qb;
-        const uint32_t sb = lds0 + uint32_t(it & 1) * kStageQ * 16;
+        const uint32_t sb = lds0 + uint32_t(it % kStagesQ) * kStageQ * 16;
         if (wave == 0 && lane < kStat)
             lds_copy16(ST + qt * kStat + lane, __builtin_amdgcn_readfirstlane(sb + 4 * kTile * 16));
         const u32x4* srcs[4] = {QB, QT, OB, OT};
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int piece = i * 4 + wave;
-                lds_copy16(srcs[tt] + qt * kTile + piece * 64 + lane,
-                           __builtin_amdgcn_readfirstlane(sb + (tt * kTile + piece * 64) * 16));
-            }
+            lds_copy16(srcs[tt] + qt * kTile + wave * 64 + lane,
+                       __builtin_amdgcn_readfirstlane(sb + (tt * kTile + wave * 64) * 16));
     };
 
     dma(0);
@@ -293,52 +303,57 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         MSA_WAIT_VMCNT(0);
         __syncthreads();                            // tile it in LDS; every wave done with tile it - 1
         if (it + 1 < n_it) dma(it + 1);
-        const int qb = qb0 + it % per_head;
-        if (qb < qbw) continue;                     // no token of this tile sees the wave's keys
-        const u32x4* sQ = sbuf + (it & 1) * kStageQ;
+        if (it >= wave_its) continue;               // no token of this tile sees the wave's keys
+        const u32x4* sQ = sbuf + (it % kStagesQ) * kStageQ;
         const u32x4* sQT = sQ + kTile;
         const u32x4* sO = sQ + 2 * kTile;
         const u32x4* sOT = sQ + 3 * kTile;
         const float* sst = reinterpret_cast<const float*>(sQ + 4 * kTile);
+        const int i0 = (nqb - 1 - it / G) * RB;
+        // every token of the tile sees every key of the wave (rows past Tq have P = 0 anyway)
+        const bool full = shift + i0 >= kw0 + 31;
 
-        f32x16 s, dp;
+        // S = Q K^T (both roles), dP = dO V^T (dK role)
+        f32x16 sc, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const bf16x8 qa = __builtin_bit_cast(bf16x8, sQ[row_unit(lane % 32, 2 * ks + half)]);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-            const bf16x8 oa = __builtin_bit_cast(bf16x8, sO[row_unit(lane % 32, 2 * ks + half)]);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sc, 0, 0, 0);
         }
-        const int i0 = qb * RB;
-        // every token of the tile sees every key of the wave (rows past Tq have P = 0 anyway)
-        const bool full = shift + i0 >= kw0 + 31;
-        float p[16], ds[16];
+        if (kside) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 oa = __builtin_bit_cast(bf16x8, sO[row_unit(lane % 32, 2 * ks + half)]);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+            }
+        }
+        // P (dV role) or dS = P (dP - D) (dK role), packed as A operands
+        float w[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float4 l4 = *reinterpret_cast<const float4*>(sst + 8 * j + 4 * half);
-            const float4 d4 = *reinterpret_cast<const float4*>(sst + 32 + 8 * j + 4 * half);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+            float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kside) d4 = *reinterpret_cast<const float4*>(sst + 32 + 8 * j + 4 * half);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * j + e;
-                float pv = __builtin_amdgcn_exp2f(s[i] * kLog2e - lv[e]);
+                float pv = __builtin_amdgcn_exp2f(sc[i] * kLog2e - lv[e]);
                 if (!full && kcol > shift + i0 + acc_row(i, half)) pv = 0.f;
-                p[i] = pv;
-                ds[i] = pv * (dp[i] - dv4[e]);
+                w[i] = kside ? pv * (dp[i] - dd[e]) : pv;
             }
         }
-        const bf16x8 pa[2] = {pack_operand(p), pack_operand(p + 8)};
-        const bf16x8 da[2] = {pack_operand(ds), pack_operand(ds + 8)};
+        const bf16x8 wa[2] = {pack_operand(w), pack_operand(w + 8)};
+        // dV += P^T dO or dK += dS^T Q, against the transposed tile
+        const u32x4* tt = kside ? sQT : sOT;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int c = n * 32 + lane % 32;
-                dv[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], tr_operand(sOT, c, kk, half), dv[n], 0, 0, 0);
-                dk[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], tr_operand(sQT, c, kk, half), dk[n], 0, 0, 0);
-            }
+            for (int n = 0; n < 4; ++n)
+                acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk], tr_operand(tt, n * 32 + lane % 32, kk, half),
+                                                                 acc[n], 0, 0, 0);
     }
 
     // ---- store: register i holds key kw0 + acc_row(i, half), column n*32 + lane%32
@@ -348,26 +363,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const int64_t key = kw0 + acc_row(i, half);
         if (key >= n_keys) continue;
         if (key < M) {
-            uint16_t* rk = dKVmem + ((r0 + key) * 2) * kv_row + int64_t(g) * DH + lane % 32;
+            uint16_t* row = dKVmem + ((r0 + key) * 2 + (kside ? 0 : 1)) * kv_row + int64_t(g) * DH + lane % 32;
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                rk[n * 32] = f32_to_bf16(dk[n][i]);
-                rk[kv_row + n * 32] = f32_to_bf16(dv[n][i]);
-            }
+            for (int n = 0; n < 4; ++n) row[n * 32] = f32_to_bf16(acc[n][i]);
         } else {
             const int64_t j = key - M;
-            int pos = q_offset + int(j);
-            pos = pos < max_pos ? pos : max_pos - 1;
             const int64_t base = ((b * L + j) * hkv + g) * DH + lane % 32;
+            if (kside) {
+                int pos = q_offset + int(j);
+                pos = pos < max_pos ? pos : max_pos - 1;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const float2 cs = rope[int64_t(pos) * (DH / 2) + n * 32 + lane % 32];
-                const float y1 = dk[n][i], y2 = dk[n + 2][i];
-                dKl[base + n * 32] = f32_to_bf16(y1 * cs.x + y2 * cs.y);
-                dKl[base + n * 32 + DH / 2] = f32_to_bf16(y2 * cs.x - y1 * cs.y);
+                for (int n = 0; n < 2; ++n) {
+                    const float2 cs = rope[int64_t(pos) * (DH / 2) + n * 32 + lane % 32];
+                    const float y1 = acc[n][i], y2 = acc[n + 2][i];
+                    dKl[base + n * 32] = f32_to_bf16(y1 * cs.x + y2 * cs.y);
+                    dKl[base + n * 32 + DH / 2] = f32_to_bf16(y2 * cs.x - y1 * cs.y);
+                }
+            } else {
+#pragma unroll
+                for (int n = 0; n < 4; ++n) dVl[base + n * 32] = f32_to_bf16(acc[n][i]);
             }
-#pragma unroll
-            for (int n = 0; n < 4; ++n) dVl[base + n * 32] = f32_to_bf16(dv[n][i]);
         }
     }
 }
@@ -564,7 +579,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t n_bg = f.B * f.Hkv;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(unsigned(int64_t(l.n_kt) * n_bg)), dim3(256), 0, st, QB, QT, OB, OT,
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(unsigned(int64_t(l.n_kt) * n_bg)), dim3(512), 0, st, QB, QT, OB, OT,
                        reinterpret_cast<const u32x4*>(ST), KB, VB, f.mem_off, f.mem_rows_cap, f.max_rows, f.Tq,
                        f.Hq, f.Hkv, f.L, f.q_offset, f.rope_cs, f.max_pos, l.nqb, l.nkb, f.B,
                        static_cast<uint16_t*>(a.dKVmem), static_cast<uint16_t*>(a.dK_local),

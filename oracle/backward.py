@@ -140,6 +140,47 @@ def sparse_attn_bwd(Q, mem_K, mem_V, mem_off, K_loc, V_loc, k_off, scale, theta,
     return dQ, dmK, dmV, dKl, dVl
 
 
+def sparse_attn_bwd_sampled(Q, mem_K, mem_V, K_loc, V_loc, k_off, scale, theta, dO, g, q_rows, key_rows,
+                            row_block=1024):
+    """Selected outputs of sparse_attn_bwd for one query (no batch axis) and
+    one KV head g, for sizes where the full gradients are too large to form:
+    dQ[q_rows, h] for the G query heads h of g, and dK, dV of the keys
+    key_rows (indices into [memory ; local]; memory rows as stored, local
+    keys turned back by their angle).  Every query row's softmax is formed
+    whole; rows are visited row_block at a time only to bound memory.
+    Returns float64 (dQ [len(q_rows), G, d], dK [len(key_rows), d],
+    dV [len(key_rows), d])."""
+    Q = np.asarray(Q, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    Tq, Hq, d = Q.shape
+    L, Hkv = np.asarray(K_loc).shape[:2]
+    G = Hq // Hkv
+    qr, keys, vals, visible, q_pos, k_pos, M = _rows(Q, mem_K, mem_V, K_loc, V_loc, k_off, scale, theta)
+    kg, vg = keys[:, g, :], vals[:, g, :]
+    q_rows = np.asarray(q_rows)
+    key_rows = np.asarray(key_rows)
+    dq = np.zeros((len(q_rows), G, d))
+    dk = np.zeros((len(key_rows), d))
+    dv = np.zeros((len(key_rows), d))
+    for hh in range(G):
+        h = g * G + hh
+        for r0 in range(0, Tq, row_block):
+            r1 = min(Tq, r0 + row_block)
+            P, _ = _softmax_rows(scale * (qr[r0:r1, h, :] @ kg.T), visible[r0:r1])
+            dPm = dO[r0:r1, h, :] @ vg.T
+            dS = P * (dPm - np.sum(P * dPm, axis=1, keepdims=True))
+            dk += scale * (dS[:, key_rows].T @ qr[r0:r1, h, :])
+            dv += P[:, key_rows].T @ dO[r0:r1, h, :]
+            sel = (q_rows >= r0) & (q_rows < r1)
+            if np.any(sel):
+                dq[sel, hh] = scale * (dS[q_rows[sel] - r0] @ kg)
+    dq = rope(dq, -q_pos[q_rows][:, None], theta)
+    loc = key_rows >= M
+    if np.any(loc):
+        dk[loc] = rope(dk[loc], -k_pos[key_rows[loc] - M], theta)
+    return dq, dk, dv
+
+
 def doc_score_argmax(Qr, Krbar, doc_chunk_off, eps=EPS):
     """Document scores with the (chunk, token) that attains each.
 

@@ -149,6 +149,7 @@ def test_sparse_attn_bwd_parity(torch_mod, msa, ctx128, Hq, Hkv, B, Tq, L, rows,
         if r.size == 0:
             continue
         assert np.all(np.isfinite(g)), name
+        print(f"{name}: rel max err {_rel(g, r):.3e}", flush=True)
         assert _rel(g, r) <= GRAD_TOL, (name, _rel(g, r))
 
 
@@ -212,3 +213,50 @@ def test_sparse_attn_bwd_rejects_unsupported(torch_mod, msa, ctx64):
                                 torch.empty_like(dev["KV"]), torch.empty_like(dev["Kl"]),
                                 torch.empty_like(dev["Vl"]), ws)
     assert e.value.status == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_sparse_attn_bwd_full_size_sampled(torch_mod, msa, ctx128):
+    """The training-pass shape and launch the bench times: 8,192 tokens over
+    [242 memory rows ; 8,192 local keys], Hq 32, Hkv 8, inputs from the same
+    counter streams.  Sampled outputs of one KV group against the oracle:
+    dQ of 40 tokens (first, ragged middle, last) for the group's four heads,
+    dK and dV of 48 keys (memory rows, the memory/local boundary, the last
+    local keys)."""
+    from msa_synth import device as device_fill
+    torch = torch_mod
+    seed, T, M, qoff, Hq, Hkv, d = 0, 8192, 242, 32, 32, 8, 128
+    shapes = {"Q": (1, T, Hq, d), "KV": (M, 2, Hkv, d), "Kl": (1, T, Hkv, d), "Vl": (1, T, Hkv, d),
+              "dO": (1, T, Hq, d)}
+    streams = {"Q": 720, "KV": 721, "Kl": 722, "Vl": 723, "dO": 724}
+    dev = {}
+    for k, shp in shapes.items():
+        dev[k] = torch.empty(shp, dtype=torch.bfloat16, device="cuda")
+        device_fill.fill_counter_bf16(dev[k], seed, streams[k], 0)
+    mo = torch.tensor([0, M], dtype=torch.int64, device="cuda")
+    O = torch.empty_like(dev["Q"])
+    lse = torch.empty((1, T, Hq), dtype=torch.float32, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, T, Hq, Hkv, M, T))
+    msa.msa_sparse_attn_lse(ctx128, dev["Q"], dev["KV"], mo, M, dev["Kl"], dev["Vl"], qoff, W.scale_of(d), O, lse, ws)
+    g_ = [torch.empty_like(dev[k]) for k in ("Q", "KV", "Kl", "Vl")]
+    wsb = msa.workspace(msa.msa_sparse_attn_bwd_workspace_size(1, 1, T, Hq, Hkv, M, T))
+    msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, M, dev["Kl"], dev["Vl"], qoff, W.scale_of(d), O,
+                            dev["dO"], lse, *g_, wsb)
+    torch.cuda.synchronize()
+    dQ, dKV, dKl, dVl = (W.widen(W.host_bits(t), "bf16") for t in g_)
+
+    host = {k: W.widen(W.counter_bf16_threads(seed, streams[k], 0, int(np.prod(shp))).reshape(shp), "bf16")
+            for k, shp in shapes.items()}
+    g = 5
+    G = Hq // Hkv
+    q_rows = np.concatenate([np.arange(8), [1000, 4095, 4096, 4097, 6001], np.arange(T - 27, T)])
+    key_rows = np.concatenate([[0, 1, 100, 240, 241], np.arange(242, 250), [242 + 31, 242 + 32, 4000, 8191],
+                               np.arange(M + T - 30, M + T)])
+    rq, rk, rv = oracle.sparse_attn_bwd_sampled(host["Q"][0], host["KV"][:, 0], host["KV"][:, 1], host["Kl"][0],
+                                                host["Vl"][0], qoff, W.scale_of(d), ctx128.rope_theta,
+                                                host["dO"][0], g, q_rows, key_rows)
+    got_q = dQ[0][q_rows][:, g * G:(g + 1) * G]
+    allk = np.concatenate([dKV[:, 0, g], dKl[0, :, g]])
+    allv = np.concatenate([dKV[:, 1, g], dVl[0, :, g]])
+    for name, got, ref in (("dQ", got_q, rq), ("dK", allk[key_rows], rk), ("dV", allv[key_rows], rv)):
+        print(f"\n{name}: rel max err {_rel(got, ref):.3e}", flush=True)
+        assert _rel(got, ref) <= GRAD_TOL, name

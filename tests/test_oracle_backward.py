@@ -81,6 +81,26 @@ def test_attention_gradient_identities():
     np.testing.assert_allclose(lhs, rhs, rtol=1e-10)
 
 
+def test_sampled_attention_gradients_match_the_full_ones():
+    rng = np.random.default_rng(13)
+    B, Tq, L, Hq, Hkv, d, M = 1, 11, 14, 8, 2, 16, 5
+    c = _attn_case(rng, B, Tq, L, Hq, Hkv, d, M=(M,))
+    dO = rng.standard_normal(c["Q"].shape)
+    dQ, dmK, dmV, dKl, dVl = bw.sparse_attn_bwd(**c, dO=dO)
+    q_rows = np.array([0, 3, 4, 10])
+    key_rows = np.array([0, 4, 5, 9, 18])                  # memory rows and local keys
+    for g in range(Hkv):
+        dq, dk, dv = bw.sparse_attn_bwd_sampled(c["Q"][0], c["mem_K"], c["mem_V"], c["K_loc"][0], c["V_loc"][0],
+                                                c["k_off"], c["scale"], THETA, dO[0], g, q_rows, key_rows,
+                                                row_block=4)
+        G = Hq // Hkv
+        np.testing.assert_allclose(dq, dQ[0][q_rows][:, g * G:(g + 1) * G], rtol=1e-11, atol=1e-13)
+        allk = np.concatenate([dmK[:, g], dKl[0, :, g]])
+        allv = np.concatenate([dmV[:, g], dVl[0, :, g]])
+        np.testing.assert_allclose(dk, allk[key_rows], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dv, allv[key_rows], rtol=1e-11, atol=1e-13)
+
+
 def test_attention_single_key_row_has_no_query_gradient():
     # Tq = L and no memory: query 0 sees only local key 0, a softmax over one
     # key is constantly 1, so dQ of token 0 is 0 and dV of key 0 collects dO.
