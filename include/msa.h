@@ -177,6 +177,42 @@ msa_status msa_route(msa_ctx* ctx, msa_dtype dt,
                      void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * msa_route_bwd -- gradients of the document scores of msa_route with respect
+ * to Qr and K̄r, given dscore = dLoss/dscore.  ([blog] 训练策略: the router is
+ * trained by an auxiliary routing loss, a supervised contrastive loss over
+ * relevant and irrelevant document blocks, through the document scores;
+ * [rev] 核心能力 › 端到端可训练框架.)
+ * score[b,doc] = max over the doc's chunks n and tokens t of
+ * (1/Hq) sum_h cos(Qr[b,t,h], K̄r[n,h/G]); the max passes its gradient to its
+ * arg max (n*, t*) only, the lowest chunk and then the lowest token among
+ * equal scores (scores compared in fp32).  With w = dscore[b,doc]/Hq, c_h the
+ * cosine of head h at (n*, t*) and ^ the division by the eps-clamped norm:
+ *     dQr[b,t*,h] += w (k^ - c_h q^_h) / |q_h|
+ *     dK̄r[n*,g]   += w sum_{h in g} (q^_h - c_h k^) / |k|
+ * (a norm at or below eps is a constant: the second term drops and |.| is eps).
+ *   Qr, Krbar, doc_chunk_off, B, Tq, Hq, N, Hkv, n_docs  as for msa_route;
+ *                  Hkv * head_dim a power of two from 64 to 2048; N * Tq < 2^32.
+ *   dscore         device float [B][n_docs]; documents with 0 are skipped.
+ *   dQr            device float [B][Tq][Hq][d] (written, every element).
+ *   dKrbar         device float [N][Hkv][d]: rows of chunks inside some
+ *                  document are written (0 where no gradient arrives); rows
+ *                  outside every document are untouched.
+ *   out_arg        optional device int32 [B][n_docs][2] (8-byte aligned):
+ *                  (n*, t*) per document, (-1, -1) where dscore is 0.
+ *   workspace      device, >= msa_route_bwd_workspace_size(...) bytes.
+ * Every sum runs in a fixed order (no atomics); the result does not depend on
+ * scheduling.
+ */
+size_t msa_route_bwd_workspace_size(int64_t B, int Tq, int Hq, int Hkv, int64_t N, int64_t n_docs);
+
+msa_status msa_route_bwd(msa_ctx* ctx, msa_dtype dt,
+                         const void* Qr, int64_t B, int Tq, int Hq,
+                         const void* Krbar, int64_t N, int Hkv,
+                         const int64_t* doc_chunk_off, int64_t n_docs,
+                         const float* dscore, float* dQr, float* dKrbar, int32_t* out_arg,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * msa_route_time_next -- profiling aid, synchronous.  The next msa_route call
  * on this context has its main chunk-score kernel (the streaming scan, the
  * generic scan, or the matrix-core contraction; not the packing or top-k

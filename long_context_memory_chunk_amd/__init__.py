@@ -25,6 +25,7 @@ EXPORTS = [
     "msa_abi_version", "msa_last_error", "msa_status_string",
     "msa_ctx_create", "msa_ctx_destroy", "msa_chunk_offsets",
     "msa_encode_pool", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
+    "msa_route_bwd_workspace_size", "msa_route_bwd",
     "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
     "msa_sparse_attn_workspace_size", "msa_sparse_attn",
     "msa_sparse_attn_lse", "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
@@ -56,6 +57,8 @@ _SIGS = {
     "msa_route_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I64, I32]),
     "msa_route": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, I32, P, P, P, P, P, SZ, P]),
     "msa_route_time_next": (I32, [P, P, P]),
+    "msa_route_bwd_workspace_size": (SZ, [I64, I32, I32, I32, I64, I64]),
+    "msa_route_bwd": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, P, P, P, P, P, SZ, P]),
     "msa_gather": (I32, [P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, P, P]),
     "msa_gather_device_workspace_size": (SZ, [I64, I32]),
     "msa_gather_device": (I32, [P, P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, SZ, P]),
@@ -211,6 +214,22 @@ def msa_route_time_next(ctx, start=None, stop=None):
     (so the underlying event exists), or None to clear."""
     h = lambda e: None if e is None else e.cuda_event
     _check(lib().msa_route_time_next(ctx.handle, h(start), h(stop)))
+
+
+def msa_route_bwd_workspace_size(B, Tq, Hq, Hkv, N, n_docs):
+    return lib().msa_route_bwd_workspace_size(B, Tq, Hq, Hkv, N, n_docs)
+
+
+def msa_route_bwd(ctx, Qr, Krbar, doc_chunk_off, dscore, dQr, dKrbar, workspace, out_arg=None, stream=None):
+    """Qr [B, Tq, Hq, d]; Krbar [N, Hkv, d]; doc_chunk_off int64 device [n_docs+1];
+    dscore float32 [B, n_docs]; dQr float32 like Qr; dKrbar float32 like Krbar;
+    out_arg optional int32 [B, n_docs, 2]."""
+    B, Tq, Hq, d = Qr.shape
+    N, Hkv, _ = Krbar.shape
+    _check(lib().msa_route_bwd(ctx.handle, _dtype(Qr), _ptr(Qr), B, Tq, Hq, _ptr(Krbar), N, Hkv,
+                               _ptr(doc_chunk_off), doc_chunk_off.numel() - 1, _ptr(dscore), _ptr(dQr),
+                               _ptr(dKrbar), _ptr(out_arg), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def msa_gather(host_KVbar, row_bytes, n_rows_host, doc_chunk_off_host, ids_host, top_k,

@@ -278,6 +278,50 @@ msa_status msa_route(msa_ctx* ctx, msa_dtype dt, const void* Qr, int64_t B, int 
     return ok();
 }
 
+size_t msa_route_bwd_workspace_size(int64_t B, int Tq, int Hq, int Hkv, int64_t N, int64_t n_docs) {
+    if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || N < 1 || n_docs < 1) return 0;
+    return msa::route_bwd_workspace(B, Tq, Hq, Hkv, 128, N, n_docs);   // sized for head dim 128
+}
+
+msa_status msa_route_bwd(msa_ctx* ctx, msa_dtype dt, const void* Qr, int64_t B, int Tq, int Hq,
+                         const void* Krbar, int64_t N, int Hkv, const int64_t* doc_chunk_off, int64_t n_docs,
+                         const float* dscore, float* dQr, float* dKrbar, int32_t* out_arg, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "msa_route_bwd";
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+    if (!dtype_ok(dt)) return fail(MSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dt));
+    if (B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || N < 1 || n_docs < 1)
+        return fail(MSA_ERR_INVALID_ARG, "%s: B, Tq, Hq, Hkv, N and n_docs must be >= 1", fn);
+    if (Hq % Hkv) return fail(MSA_ERR_INVALID_ARG, "%s: Hq %% Hkv != 0 (%d, %d)", fn, Hq, Hkv);
+    const int RW = Hkv * ctx->head_dim;
+    if (RW % 64 || RW > 2048 || (RW / 64) & (RW / 64 - 1))
+        return fail(MSA_ERR_UNSUPPORTED, "%s: Hkv * head_dim must be 64 .. 2048, a power of two", fn);
+    if (B > 65535 || n_docs > 0x7FFFFFFFLL || Tq > 65535)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: B, Tq or n_docs too large", fn);
+    if (N * int64_t(Tq) > 0xFFFFFFF0LL || N > 0x7FFFFFFFLL)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: N * Tq must stay below 2^32", fn);
+    if (!Qr || !Krbar || !doc_chunk_off || !dscore || !dQr || !dKrbar)
+        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (out_arg && (reinterpret_cast<uintptr_t>(out_arg) & 7u))
+        return fail(MSA_ERR_INVALID_ARG, "%s: out_arg must be 8-byte aligned", fn);
+    const size_t need = msa::route_bwd_workspace(B, Tq, Hq, Hkv, ctx->head_dim, N, n_docs);
+    if (!workspace || !aligned256(workspace) || ws_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
+                    ws_bytes);
+    msa::RouteBwdArgs a{};
+    a.r = msa::RouteArgs{dt, Qr, B, Tq, Hq, Hkv, ctx->head_dim, Krbar, N, doc_chunk_off, n_docs, 1,
+                         nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes, ctx->num_cus, nullptr, nullptr};
+    a.dscore = dscore;
+    a.dQr = dQr;
+    a.dKr = dKrbar;
+    a.arg_out = out_arg;
+    DeviceGuard dg(ctx->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_route_bwd: hipSetDevice");
+    hipError_t e = msa::launch_route_bwd(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "msa_route_bwd: launch");
+    return ok();
+}
+
 msa_status msa_route_time_next(msa_ctx* ctx, hipEvent_t start, hipEvent_t stop) {
     if (!ctx) return fail(MSA_ERR_INVALID_ARG, "msa_route_time_next: ctx is NULL");
     if ((start == nullptr) != (stop == nullptr))

@@ -37,6 +37,17 @@ size_t route_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, 
                        int64_t n_docs, int top_k, int num_cus);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 
+// Backward of the document score (route_bwd.hip).
+struct RouteBwdArgs {
+    RouteArgs r;            // Qr, B, Tq, Hq, Hkv, D, Krbar, N, chunk_off, n_docs, dt, ws
+    const float* dscore;    // [B][n_docs]
+    float* dQr;             // [B][Tq][Hq][D]
+    float* dKr;             // [N][Hkv][D]
+    void* arg_out;          // optional int32 [B][n_docs][2]: (chunk, token) of each arg max, -1 if none
+};
+size_t route_bwd_workspace(int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int64_t n_docs);
+hipError_t launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
+
 // Records an optional profiling event (NULL: nothing to do).
 inline hipError_t record_if(hipEvent_t e, hipStream_t st) {
     return e ? hipEventRecord(e, st) : hipSuccess;

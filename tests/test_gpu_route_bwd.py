@@ -1,0 +1,156 @@
+"""Backward of the document score on the GPU vs the oracle, through the C ABI.
+
+Tolerances (stated where used):
+  arg max   (chunk, token) of every document bit-exact, on inputs whose best
+            and second-best (chunk, token) scores differ by more than 1e-4
+            (checked here with the oracle); the GPU compares fp32 scores
+            whose error is below 1e-5 (the fp32 group fold of the forward).
+  grads     1e-4 of max |ref| per tensor: fp32 sums of unit vectors scaled by
+            the document gradients, from inputs the oracle widens exactly.
+"""
+
+import numpy as np
+import pytest
+
+import msa_synth
+import oracle
+from tests import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-4
+GRAD_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def torch_mod(gpu):
+    import torch
+    return torch
+
+
+@pytest.fixture(scope="module")
+def msa(gpu):
+    import long_context_memory_chunk_amd as m
+    m.lib()   # raises if the library is missing: no fallback
+    return m
+
+
+@pytest.fixture(scope="module")
+def ctxs(msa):
+    c = {128: msa.msa_ctx_create(0, 128, 1e6, 16384), 64: msa.msa_ctx_create(0, 64, 1e4, 4096)}
+    yield c
+    for v in c.values():
+        v.close()
+
+
+def _scores_all(Qr, Kr):
+    """s[b, n, t]: the oracle's score of every (chunk, token) pair."""
+    return np.stack([oracle.chunk_scores(Qr[:, t:t + 1], Kr) for t in range(Qr.shape[1])], axis=2)
+
+
+def _margins_ok(Qr, Kr, off):
+    s = _scores_all(Qr, Kr)
+    for doc in range(len(off) - 1):
+        blk = s[:, off[doc]:off[doc + 1], :].reshape(s.shape[0], -1)
+        if blk.shape[1] > 1:
+            top2 = np.sort(blk, axis=1)[:, -2:]
+            if np.min(top2[:, 1] - top2[:, 0]) <= MARGIN:
+                return False
+    return True
+
+
+def _rel(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+CASES = [
+    # dtype, d, Hq, Hkv, B, Tq, chunks per document, zero-gradient documents
+    ("f32", 64, 4, 2, 1, 32, [16] * 64, [3, 40]),                 # tiny fp32 shape (64 docs x 16 chunks)
+    ("bf16", 128, 32, 8, 2, 16, [2, 16, 5, 9, 1, 12] * 8, [0]),   # Qwen3-4B-shaped heads, ragged documents
+    ("bf16", 128, 32, 8, 4, 1, [1] * 300, []),                    # chunk-level selection, one decode token
+    ("bf16", 128, 64, 16, 1, 8, [4, 7, 3] * 10, [5]),             # Hkv 16: rows of 2,048 elements
+    ("f32", 64, 2, 1, 3, 5, [3, 1, 8] * 7, [1, 2]),               # Hkv 1, d 64: rows of 64 elements
+    ("bf16", 128, 32, 8, 1, 4, [40, 3], []),                      # a document staged in several blocks
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,lens,zero_docs", CASES)
+def test_route_bwd_parity(torch_mod, msa, ctxs, dtype, d, Hq, Hkv, B, Tq, lens, zero_docs):
+    torch = torch_mod
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, n_docs = int(off[-1]), len(lens)
+    for seed in range(101, 111):                 # the first seed whose arg maxes have a margin
+        Qr = W.draw(seed, 1, (B, Tq, Hq, d), dtype)
+        Kr = W.draw(seed, 2, (N, Hkv, d), dtype)
+        if _margins_ok(W.widen(Qr, dtype), W.widen(Kr, dtype), off):
+            break
+    else:
+        pytest.fail("no seed with arg-max margins")
+    print(f"\nroute bwd case {dtype} d={d} Hq={Hq} Hkv={Hkv} B={B} Tq={Tq} docs={n_docs} seed={seed}", flush=True)
+    dscore = msa_synth.normal_f32(seed, 3, (B, n_docs)).astype(np.float32)
+    dscore[:, zero_docs] = 0.0
+    dQr = torch.full((B, Tq, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    dKr = torch.full((N, Hkv, d), float("nan"), dtype=torch.float32, device="cuda")
+    arg = torch.full((B, n_docs, 2), -7, dtype=torch.int32, device="cuda")
+    ws = msa.workspace(msa.msa_route_bwd_workspace_size(B, Tq, Hq, Hkv, N, n_docs))
+    msa.msa_route_bwd(ctxs[d], W.dev(Qr, dtype), W.dev(Kr, dtype), torch.from_numpy(off).cuda(),
+                      torch.from_numpy(dscore).cuda(), dQr, dKr, ws, out_arg=arg)
+    torch.cuda.synchronize()
+    q64, k64 = W.widen(Qr, dtype), W.widen(Kr, dtype)
+    _, ac, at = oracle.doc_score_argmax(q64, k64, off)
+    got_arg = arg.cpu().numpy()
+    live = dscore != 0
+    assert np.array_equal(got_arg[..., 0][live], ac[live])
+    assert np.array_equal(got_arg[..., 1][live], at[live])
+    assert np.all(got_arg[~live] == -1)
+    rq, rk = oracle.route_score_bwd(q64, k64, off, dscore.astype(np.float64))
+    gq, gk = dQr.cpu().numpy(), dKr.cpu().numpy()
+    print(f"dQr rel {_rel(gq, rq):.2e}  dKr rel {_rel(gk, rk):.2e}", flush=True)
+    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk))
+    assert _rel(gq, rq) <= GRAD_TOL
+    assert _rel(gk, rk) <= GRAD_TOL
+
+
+def test_route_bwd_zero_vectors(torch_mod, msa, ctxs):
+    """A zero routing-key row and a zero query head: the clamped norm is a
+    constant there (the oracle's reading), so the gradient is k^/eps or
+    q^/eps-scaled and finite."""
+    torch = torch_mod
+    B, Tq, Hq, Hkv, d = 1, 2, 4, 2, 64
+    off = np.array([0, 3, 5], dtype=np.int64)
+    Qr = msa_synth.normal_f32(7, 1, (B, Tq, Hq, d)).astype(np.float32)
+    Kr = msa_synth.normal_f32(7, 2, (5, Hkv, d)).astype(np.float32)
+    Qr[0, 1, 3] = 0.0
+    Kr[4, 1] = 0.0
+    for k in range(5):                          # chunk k aligned with token k % 2 to give margins
+        Kr[k] += 3.0 * Qr[0, k % 2].reshape(Hkv, Hq // Hkv, d).sum(axis=1) * (k + 1) / 5
+    Kr[4, 1] = 0.0
+    assert _margins_ok(Qr.astype(np.float64), Kr.astype(np.float64), off)
+    dscore = np.array([[0.7, -1.3]], dtype=np.float32)
+    dQr = torch.empty((B, Tq, Hq, d), dtype=torch.float32, device="cuda")
+    dKr = torch.empty((5, Hkv, d), dtype=torch.float32, device="cuda")
+    ws = msa.workspace(msa.msa_route_bwd_workspace_size(B, Tq, Hq, Hkv, 5, 2))
+    msa.msa_route_bwd(ctxs[64], W.dev_f32(Qr), W.dev_f32(Kr), torch.from_numpy(off).cuda(),
+                      torch.from_numpy(dscore).cuda(), dQr, dKr, ws)
+    torch.cuda.synchronize()
+    rq, rk = oracle.route_score_bwd(Qr.astype(np.float64), Kr.astype(np.float64), off, dscore.astype(np.float64))
+    gq, gk = dQr.cpu().numpy(), dKr.cpu().numpy()
+    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk))
+    assert _rel(gq, rq) <= GRAD_TOL and _rel(gk, rk) <= GRAD_TOL
+
+
+def test_route_bwd_is_deterministic(torch_mod, msa, ctxs):
+    torch = torch_mod
+    off = np.concatenate([[0], np.cumsum([3, 9, 1, 4] * 20)]).astype(np.int64)
+    N = int(off[-1])
+    Qr = W.dev_bf16(msa_synth.normal_bf16(13, 1, (3, 16, 32, 128)))
+    Kr = W.dev_bf16(msa_synth.normal_bf16(13, 2, (N, 8, 128)))
+    dscore = torch.from_numpy(msa_synth.normal_f32(13, 3, (3, 80)).astype(np.float32)).cuda()
+    ws = msa.workspace(msa.msa_route_bwd_workspace_size(3, 16, 32, 8, N, 80))
+    outs = []
+    for _ in range(2):
+        dQr = torch.empty((3, 16, 32, 128), dtype=torch.float32, device="cuda")
+        dKr = torch.empty((N, 8, 128), dtype=torch.float32, device="cuda")
+        msa.msa_route_bwd(ctxs[128], Qr, Kr, torch.from_numpy(off).cuda(), dscore, dQr, dKr, ws)
+        outs.append((dQr.cpu().numpy(), dKr.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
