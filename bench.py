@@ -84,12 +84,13 @@ def parse():
                    help="chunk rows per layer in the oracle sample (0: the whole layer)")
     p.add_argument("--cpu-sample-layers", type=int, default=4, help="routing layers in the oracle sample")
     p.add_argument("--workload", choices=["decode100m", "chunk100m", "reuse100m", "prefill8k", "batch32", "encode10m",
-                                          "train8k", "hbmcopy"],
+                                          "train8k", "routebwd1m", "hbmcopy"],
                    default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
                         "prefill8k / batch32: extra measurements on the 10M-token bank; "
                         "encode10m: the offline encode of one layer of the 10M-token bank; "
                         "train8k: forward (saving log-sum-exp) + backward of the prefill-shaped attention; "
+                        "routebwd1m: routing forward + document-score backward on the 1M-token memory; "
                         "hbmcopy: a plain 4 GiB device-to-device copy, the known-size kernel that "
                         "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--gen-tokens", type=int, default=64, help="reuse100m: tokens generated after assembly")
@@ -588,6 +589,63 @@ def run_train8k(args, torch, msa, msa_synth, device_fill, W):
     }
 
 
+def run_routebwd1m(args, torch, msa, msa_synth, device_fill, W):
+    """The routing layer's training pass on the 1M-token memory of 2,000
+    documents (lengths uniform in [128, 1024], chunk 64): a 256-token query
+    routed with top-16 (forward, document scores kept), then the backward of
+    the document scores (dQr, dK̄r) from a dense dscore over all documents,
+    as an auxiliary routing loss over the batch's documents gives."""
+    seed, T, k = args.seed, 256, 16
+    lens = msa_synth.uniform_lengths(seed, 2000, 128, 1024)
+    coff = msa_synth.prefix_offsets([(int(x) + CHUNK - 1) // CHUNK for x in lens])
+    n_docs, N = len(lens), int(coff[-1])
+    Qr = torch.empty((1, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    Kr = torch.empty((N, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    device_fill.fill_counter_bf16(Qr, seed, 730, 0)
+    device_fill.fill_counter_bf16(Kr, seed, 731, 0)
+    dscore = torch.from_numpy(msa_synth.normal_f32(seed, 732, (1, n_docs)).astype(np.float32)).cuda()
+    ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
+    coff_dev = torch.from_numpy(np.asarray(coff, dtype=np.int64)).cuda()
+    ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    doc_sc = torch.empty((1, n_docs), dtype=torch.float32, device="cuda")
+    ws_r = msa.workspace(msa.msa_route_workspace_size(1, 1, T, Hq, Hkv, N, n_docs, k))
+    ws_b = msa.workspace(msa.msa_route_bwd_workspace_size(1, T, Hq, Hkv, N, n_docs))
+    dQr = torch.empty((1, T, Hq, D), dtype=torch.float32, device="cuda")
+    dKr = torch.empty((N, Hkv, D), dtype=torch.float32, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    f_s, f_e, b_e = ev(), ev(), ev()
+    t_f, t_b = [], []
+    for it in range(args.warmup + args.steps):
+        torch.cuda.synchronize()
+        f_s.record()
+        msa.msa_route(ctx, Qr, Kr, coff_dev, k, ids, ws_r, out_doc=doc_sc)
+        f_e.record()
+        msa.msa_route_bwd(ctx, Qr, Kr, coff_dev, dscore, dQr, dKr, ws_b)
+        b_e.record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            t_f.append(f_s.elapsed_time(f_e) / 1e3)
+            t_b.append(f_e.elapsed_time(b_e) / 1e3)
+    finite = bool(torch.isfinite(dQr).all()) and bool(torch.isfinite(dKr).all())
+    tf, tb = float(np.mean(t_f)), float(np.mean(t_b))
+    # the backward's dominant cost: every (token, chunk) score again, in fp32 on the
+    # vector units (group-folded: Hkv * D multiply-adds per pair)
+    flop = 2.0 * T * N * Hkv * D
+    ctx.close()
+    return {
+        "metric": "routing-score training pass (document-score backward, 256-token query, 1M-token memory)",
+        "value": round(flop / tb / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round((tf + tb) * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 inputs, fp32 arithmetic", "data": "synthetic",
+        "config": {"workload": "msa_route (top-16) then msa_route_bwd with a dense dscore over all documents",
+                   "n_docs": n_docs, "chunk_rows": N, "tokens": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D},
+        "fwd_ms": round(tf * 1e3, 4), "bwd_ms": round(tb * 1e3, 4), "outputs_finite": finite,
+        "roofline": {"bound": "alu", "achieved": round(flop / tb / 1e12, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(flop / tb / 1e12 / 157.3, 4), "traffic": None,
+                     "kernel": "msa_route_bwd (all kernels)", "flop_per_launch": flop},
+    }
+
+
 def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
     """Offline encode of one layer of the 10M-token bank: raw K, V, Kr
     [10M, 8, 128] bf16 (61.4 GB) pooled into KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128]
@@ -770,7 +828,8 @@ def main():
     msa.lib()
     if args.workload not in ("decode100m", "chunk100m"):
         fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "encode10m": run_encode10m,
-              "hbmcopy": run_hbmcopy, "reuse100m": run_reuse100m, "train8k": run_train8k}[args.workload]
+              "hbmcopy": run_hbmcopy, "reuse100m": run_reuse100m, "train8k": run_train8k,
+              "routebwd1m": run_routebwd1m}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
         print(json.dumps(out), flush=True)
         ok = out.get("planted_recovered", out.get("planted_recovered_all", out.get(

@@ -21,13 +21,12 @@
 // Kernels:
 //   route_prep (route_scan.hip)  U[b,t,g] = sum_{h in g} q^_h, fp32.
 //   rbwd_knorm     |K̄r[n, g]| for every chunk row and KV head.
-//   rbwd_argmax    one workgroup per (b, doc) with a non-zero gradient: the
-//                  doc's unit keys, up to 64 KB at a time, in LDS; each wave
-//                  keeps one token's U in registers and scores it against
-//                  every staged chunk (the group fold of the forward, fp32);
-//                  the best (score, then lowest chunk, then lowest token) is
-//                  one 64-bit key per wave, merged across waves.  It then
-//                  writes the per-head cosines at the arg max.
+//   rbwd_chunkmax  every (token, chunk) score (the group fold of the forward,
+//                  U . k^ / Hq, in fp32 on the vector units) and, per chunk,
+//                  the best token as one 64-bit key (score, then lowest token).
+//   rbwd_docmax    per (b, doc) with a non-zero gradient: the best chunk key
+//                  (lowest chunk among equal scores), then the per-head
+//                  cosines at the arg max.
 //   rbwd_dq        one workgroup per (b, t): the documents whose arg max token
 //                  is t, in document order, summed into dQr[b, t].
 //   rbwd_dk        one workgroup per document: for each of its chunks, the
@@ -42,7 +41,6 @@ namespace msa {
 namespace {
 
 constexpr float kEps = 1e-8f;
-constexpr int kStageFloats = 16384;          // LDS floats of staged unit keys (64 KB)
 
 // Monotone map of a float to an unsigned integer (finite inputs).
 __device__ __forceinline__ uint32_t order32(float f) {
@@ -64,68 +62,142 @@ __global__ __launch_bounds__(64) void rbwd_knorm_kernel(const T* __restrict__ Kr
     if (lane == 0) knorm[row] = sqrtf(s);
 }
 
-template <typename T, int RPL>   // RPL = Hkv * D / 64 elements of a row per lane
-__global__ __launch_bounds__(256) void rbwd_argmax_kernel(
+// Per chunk row n and query b: the best token, as the key
+// order32(score) << 32 | (2^32 - 1 - t) (higher score, then lower t, wins).
+// A workgroup takes 32 chunk rows and 256 tokens at a time; wave w owns chunk
+// rows 8w .. 8w+7 and lane l the tokens l, l+64, l+128, l+192, so each thread
+// keeps a 4 x 8 block of scores.  The contraction over the Hkv * D elements
+// runs through LDS 32 elements at a time; per 4 elements a thread makes four
+// 16-byte token loads (distinct rows, conflict-free) and eight broadcast
+// unit-key loads for 128 fp32 multiply-adds.
+constexpr int kCB = 32;                       // chunk rows per workgroup (8 per wave)
+constexpr int kEB = 32;                       // contraction elements per LDS stage
+constexpr int kUS = kEB + 4;                  // padded row of the token stage
+
+template <typename T>
+__global__ __launch_bounds__(256) void rbwd_chunkmax_kernel(
+    const float* __restrict__ U, int Tq, int Hq, const T* __restrict__ Kr, int64_t N, int hkv, int D,
+    const float* __restrict__ knorm, unsigned long long* __restrict__ ckey) {
+    __shared__ __attribute__((aligned(16))) float sU[256 * kUS];
+    __shared__ __attribute__((aligned(16))) float sK[kCB * kEB];
+    const int64_t n0 = int64_t(blockIdx.x) * kCB;
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int RW = hkv * D;
+    const int nb = int(N - n0 < kCB ? N - n0 : kCB);
+    const float inv_hq = 1.f / float(Hq);
+    unsigned long long best = 0ull;           // lane j < 8: running best of chunk n0 + 8 wave + j
+    for (int t0 = 0; t0 < Tq; t0 += 256) {
+        float acc[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+        for (int e0 = 0; e0 < RW; e0 += kEB) {
+            __syncthreads();                   // every thread done with the previous stage
+            for (int i = tid; i < 256 * kEB; i += 256) {
+                const int r = i / kEB, c = i % kEB;
+                sU[r * kUS + c] = (t0 + r < Tq) ? U[(b * Tq + t0 + r) * int64_t(RW) + e0 + c] : 0.f;
+            }
+            for (int i = tid; i < kCB * kEB; i += 256) {
+                const int j = i / kEB, c = i % kEB;
+                float v = 0.f;
+                if (j < nb) {
+                    const int64_t n = n0 + j;
+                    v = Elem<T>::load(Kr, n * RW + e0 + c) / fmaxf(knorm[n * hkv + (e0 + c) / D], kEps);
+                }
+                sK[i] = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < kEB; c += 4) {
+                float4 u[4], k[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const float4*>(sU + (lane + 64 * i) * kUS + c);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) k[j] = *reinterpret_cast<const float4*>(sK + (8 * wave + j) * kEB + c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                    {
+                        acc[i][j] = fmaf(u[i].x, k[j].x, acc[i][j]);
+                        acc[i][j] = fmaf(u[i].y, k[j].y, acc[i][j]);
+                        acc[i][j] = fmaf(u[i].z, k[j].z, acc[i][j]);
+                        acc[i][j] = fmaf(u[i].w, k[j].w, acc[i][j]);
+                    }
+            }
+        }
+        // best token of each of the wave's chunks over this block of tokens
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            unsigned long long key = 0ull;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + lane + 64 * i;
+                if (t < Tq) {
+                    const unsigned long long kk =
+                        (static_cast<unsigned long long>(order32(acc[i][j] * inv_hq)) << 32) | (0xFFFFFFFFu - uint32_t(t));
+                    key = kk > key ? kk : key;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const unsigned long long other = __shfl_xor(key, o);
+                key = other > key ? other : key;
+            }
+            if (lane == j) best = key > best ? key : best;
+        }
+    }
+    const int j = 8 * wave + lane;
+    if (lane < 8 && j < nb) ckey[b * N + n0 + j] = best;
+}
+
+// Per (b, doc) with a non-zero gradient: the arg max over the document's
+// chunks (the first chunk among equal scores) of the per-chunk best keys,
+// then the per-head cosines there.
+template <typename T>
+__global__ __launch_bounds__(64) void rbwd_docmax_kernel(
     const T* __restrict__ Qr, int Tq, int Hq, const T* __restrict__ Kr, int64_t N, int hkv, int D,
     const int64_t* __restrict__ chunk_off, int64_t n_docs, const float* __restrict__ dscore,
-    const float* __restrict__ U, const float* __restrict__ knorm, int2* __restrict__ arg,
+    const unsigned long long* __restrict__ ckey, const float* __restrict__ knorm, int2* __restrict__ arg,
     float* __restrict__ cosv) {
-    __shared__ float sk[kStageFloats];
-    __shared__ unsigned long long s_best[4];
     const int64_t doc = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int lane = threadIdx.x;
     const int64_t bd = b * n_docs + doc;
     int64_t n_lo = chunk_off[doc], n_hi = chunk_off[doc + 1];
     n_lo = n_lo < 0 ? 0 : (n_lo > N ? N : n_lo);
     n_hi = n_hi < n_lo ? n_lo : (n_hi > N ? N : n_hi);
-    const int64_t nc = n_hi - n_lo;
-    if (dscore[bd] == 0.f || nc == 0) {
-        if (tid == 0) arg[bd] = make_int2(-1, -1);
+    if (dscore[bd] == 0.f || n_hi == n_lo) {
+        if (lane == 0) arg[bd] = make_int2(-1, -1);
         return;
     }
-    const int RW = hkv * D;
-    const int CB = kStageFloats / RW;         // chunks staged at a time
-    const float inv_hq = 1.f / float(Hq);
-    unsigned long long best = 0ull;
-    for (int64_t c0 = 0; c0 < nc; c0 += CB) {
-        const int cbn = int(nc - c0 < CB ? nc - c0 : CB);
-        __syncthreads();                       // every wave done with the previous chunks
-        for (int e = tid; e < cbn * RW; e += 256) {
-            const int j = e / RW, r = e % RW;
-            const int64_t n = n_lo + c0 + j;
-            const float nk = fmaxf(knorm[n * hkv + r / D], kEps);
-            sk[e] = Elem<T>::load(Kr, n * RW + r) / nk;
-        }
-        __syncthreads();
-        for (int t = wave; t < Tq; t += 4) {
-            float u[RPL];
-            const float* ur = U + (b * Tq + t) * int64_t(RW);
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) u[i] = ur[lane + 64 * i];
-            for (int j = 0; j < cbn; ++j) {
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) s += u[i] * sk[j * RW + lane + 64 * i];
-                s = wave_sum(s) * inv_hq;
-                const uint32_t idx = uint32_t((c0 + j) * Tq + t);
-                const unsigned long long key =
-                    (static_cast<unsigned long long>(order32(s)) << 32) | (0xFFFFFFFFu - idx);
-                best = key > best ? key : best;
-            }
+    // lane-strided scan, then a wave max of (score, -chunk, -token)
+    unsigned long long hi = 0ull;             // order32(score) << 32 | ~n_local
+    uint32_t tok = 0;
+    for (int64_t n = n_lo + lane; n < n_hi; n += kWave) {
+        const unsigned long long k = ckey[b * N + n];
+        const unsigned long long key = (k & 0xFFFFFFFF00000000ull) | (0xFFFFFFFFu - uint32_t(n - n_lo));
+        if (key > hi) {
+            hi = key;
+            tok = 0xFFFFFFFFu - uint32_t(k & 0xFFFFFFFFull);
         }
     }
-    if (lane == 0) s_best[wave] = best;
-    __syncthreads();
-    unsigned long long k = s_best[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) k = s_best[w] > k ? s_best[w] : k;
-    const uint32_t idx = 0xFFFFFFFFu - uint32_t(k & 0xFFFFFFFFull);
-    const int64_t n = n_lo + idx / uint32_t(Tq);
-    const int t = int(idx % uint32_t(Tq));
-    if (tid == 0) arg[bd] = make_int2(int(n), t);
-    // cosines of every head at the arg max: wave w takes heads w, w+4, ...
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long ok = __shfl_xor(hi, o);
+        const uint32_t ot = __shfl_xor(tok, o);
+        if (ok > hi) {
+            hi = ok;
+            tok = ot;
+        }
+    }
+    const int64_t n = n_lo + (0xFFFFFFFFu - uint32_t(hi & 0xFFFFFFFFull));
+    const int t = int(tok);
+    if (lane == 0) arg[bd] = make_int2(int(n), t);
     const int G = Hq / hkv;
-    for (int h = wave; h < Hq; h += 4) {
+    for (int h = 0; h < Hq; ++h) {
         const int g = h / G;
         float qq = 0.f, qk = 0.f;
         for (int c = lane; c < D; c += kWave) {
@@ -254,7 +326,7 @@ __global__ __launch_bounds__(256) void rbwd_dk_kernel(
 }
 
 struct RbwdLayout {
-    size_t u, kn, arg, cos, total;
+    size_t u, kn, arg, cos, ck, total;
 };
 
 RbwdLayout rbwd_layout(int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int64_t n_docs) {
@@ -263,7 +335,8 @@ RbwdLayout rbwd_layout(int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int
     l.kn = align256(size_t(N) * Hkv * sizeof(float));
     l.arg = align256(size_t(B) * n_docs * sizeof(int2));
     l.cos = align256(size_t(B) * n_docs * Hq * sizeof(float));
-    l.total = l.u + l.kn + l.arg + l.cos;
+    l.ck = align256(size_t(B) * N * sizeof(unsigned long long));
+    l.total = l.u + l.kn + l.arg + l.cos + l.ck;
     return l;
 }
 
@@ -276,6 +349,7 @@ hipError_t launch_rbwd_t(const RouteBwdArgs& a, hipStream_t st) {
     float* knorm = reinterpret_cast<float*>(w + l.u);
     int2* arg = a.arg_out ? reinterpret_cast<int2*>(a.arg_out) : reinterpret_cast<int2*>(w + l.u + l.kn);
     float* cosv = reinterpret_cast<float*>(w + l.u + l.kn + l.arg);
+    unsigned long long* ckey = reinterpret_cast<unsigned long long*>(w + l.u + l.kn + l.arg + l.cos);
     const T* Qr = static_cast<const T*>(r.Qr);
     const T* Kr = static_cast<const T*>(r.Krbar);
     hipError_t err = launch_route_prep(r, U, st);
@@ -283,21 +357,11 @@ hipError_t launch_rbwd_t(const RouteBwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((rbwd_knorm_kernel<T>), dim3(unsigned(r.N * r.Hkv)), dim3(64), 0, st, Kr, r.N, r.Hkv, r.D,
                        knorm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int rpl = r.Hkv * r.D / 64;
-    const dim3 grid(unsigned(r.n_docs), unsigned(r.B));
-#define MSA_RBWD_ARGMAX(RPL)                                                                                  \
-    hipLaunchKernelGGL((rbwd_argmax_kernel<T, RPL>), grid, dim3(256), 0, st, Qr, r.Tq, r.Hq, Kr, r.N, r.Hkv, \
-                       r.D, r.chunk_off, r.n_docs, a.dscore, U, knorm, arg, cosv)
-    switch (rpl) {
-        case 1: MSA_RBWD_ARGMAX(1); break;
-        case 2: MSA_RBWD_ARGMAX(2); break;
-        case 4: MSA_RBWD_ARGMAX(4); break;
-        case 8: MSA_RBWD_ARGMAX(8); break;
-        case 16: MSA_RBWD_ARGMAX(16); break;
-        case 32: MSA_RBWD_ARGMAX(32); break;
-        default: return hipErrorInvalidValue;
-    }
-#undef MSA_RBWD_ARGMAX
+    hipLaunchKernelGGL((rbwd_chunkmax_kernel<T>), dim3(unsigned(ceil_div(r.N, int64_t(kCB))), unsigned(r.B)),
+                       dim3(256), 0, st, U, r.Tq, r.Hq, Kr, r.N, r.Hkv, r.D, knorm, ckey);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((rbwd_docmax_kernel<T>), dim3(unsigned(r.n_docs), unsigned(r.B)), dim3(64), 0, st, Qr, r.Tq,
+                       r.Hq, Kr, r.N, r.Hkv, r.D, r.chunk_off, r.n_docs, a.dscore, ckey, knorm, arg, cosv);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const size_t dq_lds = size_t(r.Hkv * r.D + 2 * r.Hq) * sizeof(float);
     hipLaunchKernelGGL((rbwd_dq_kernel<T>), dim3(unsigned(r.Tq), unsigned(r.B)), dim3(256), dq_lds, st, Qr, r.Tq,
