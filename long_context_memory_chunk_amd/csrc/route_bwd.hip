@@ -22,14 +22,14 @@
 //   route_prep (route_scan.hip)  U[b,t,g] = sum_{h in g} q^_h, fp32.
 //   rbwd_knorm     |K̄r[n, g]| for every chunk row and KV head.
 //   rbwd_chunkmax  every (token, chunk) score (the group fold of the forward,
-//                  U . k^ / Hq, in fp32 on the vector units) and, per chunk,
+//                  U . k^ / Hq, in fp32 on the matrix cores) and, per chunk,
 //                  the best token as one 64-bit key (score, then lowest token).
 //   rbwd_docmax    per (b, doc) with a non-zero gradient: the best chunk key
 //                  (lowest chunk among equal scores), then the per-head
 //                  cosines at the arg max.
 //   rbwd_dq        one workgroup per (b, t): the documents whose arg max token
 //                  is t, in document order, summed into dQr[b, t].
-//   rbwd_dk        one workgroup per document: for each of its chunks, the
+//   rbwd_dk        one workgroup per document, one wave per chunk row: the
 //                  queries whose arg max chunk it is, in query order, summed
 //                  into dK̄r[n] (zero rows for chunks that got nothing).
 // Every sum runs in a fixed order (no atomics): the result does not depend on
@@ -48,57 +48,68 @@ __device__ __forceinline__ uint32_t order32(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// |K̄r[n, g]| for every (chunk row, KV head): 16 lanes per row, 16 rows per
+// workgroup.
 template <typename T>
-__global__ __launch_bounds__(64) void rbwd_knorm_kernel(const T* __restrict__ Kr, int64_t N, int hkv, int D,
-                                                        float* __restrict__ knorm) {
-    const int64_t row = blockIdx.x;          // (n, g)
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void rbwd_knorm_kernel(const T* __restrict__ Kr, int64_t rows, int D,
+                                                         float* __restrict__ knorm) {
+    const int64_t row = int64_t(blockIdx.x) * 16 + threadIdx.x / 16;
+    const int sub = threadIdx.x % 16;
     float s = 0.f;
-    for (int c = lane; c < D; c += kWave) {
-        const float x = Elem<T>::load(Kr, row * D + c);
-        s += x * x;
-    }
-    s = wave_sum(s);
-    if (lane == 0) knorm[row] = sqrtf(s);
+    if (row < rows)
+        for (int c = sub; c < D; c += 16) {
+            const float x = Elem<T>::load(Kr, row * D + c);
+            s += x * x;
+        }
+    s = group_sum<16>(s);
+    if (row < rows && sub == 0) knorm[row] = sqrtf(s);
 }
 
 // Per chunk row n and query b: the best token, as the key
 // order32(score) << 32 | (2^32 - 1 - t) (higher score, then lower t, wins).
-// A workgroup takes 32 chunk rows and 256 tokens at a time; wave w owns chunk
-// rows 8w .. 8w+7 and lane l the tokens l, l+64, l+128, l+192, so each thread
-// keeps a 4 x 8 block of scores.  The contraction over the Hkv * D elements
-// runs through LDS 32 elements at a time; per 4 elements a thread makes four
-// 16-byte token loads (distinct rows, conflict-free) and eight broadcast
-// unit-key loads for 128 fp32 multiply-adds.
-constexpr int kCB = 32;                       // chunk rows per workgroup (8 per wave)
+// The scores U . k^ are a dense contraction (tokens x chunks over Hkv * D),
+// run on the matrix cores in fp32 (v_mfma_f32_32x32x2_f32: fp32 products and
+// sums, the precision of the vector path).  A workgroup takes 32 chunk rows
+// and 256 tokens at a time, wave w the tokens 64w .. 64w+63 as two 32-row
+// tiles; the contraction runs through LDS 32 elements at a time.  Two
+// consecutive products take the elements e0 .. e0+3 with lane half u holding
+// e0 + 2u and e0 + 2u + 1 (one 8-byte read per operand), the same pairing for
+// both operands.
+constexpr int kCB = 32;                       // chunk rows per workgroup
 constexpr int kEB = 32;                       // contraction elements per LDS stage
-constexpr int kUS = kEB + 4;                  // padded row of the token stage
+constexpr int kSS = kEB + 2;                  // padded LDS row (conflict-free 8-byte reads)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <typename T>
 __global__ __launch_bounds__(256) void rbwd_chunkmax_kernel(
     const float* __restrict__ U, int Tq, int Hq, const T* __restrict__ Kr, int64_t N, int hkv, int D,
     const float* __restrict__ knorm, unsigned long long* __restrict__ ckey) {
-    __shared__ __attribute__((aligned(16))) float sU[256 * kUS];
-    __shared__ __attribute__((aligned(16))) float sK[kCB * kEB];
+    __shared__ __attribute__((aligned(16))) float sU[256 * kSS];
+    __shared__ __attribute__((aligned(16))) float sK[kCB * kSS];
+    __shared__ unsigned long long s_key[4][kCB];
     const int64_t n0 = int64_t(blockIdx.x) * kCB;
     const int64_t b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid % kWave;
+    const int tid = threadIdx.x, lane = tid % kWave, half = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int RW = hkv * D;
     const int nb = int(N - n0 < kCB ? N - n0 : kCB);
     const float inv_hq = 1.f / float(Hq);
-    unsigned long long best = 0ull;           // lane j < 8: running best of chunk n0 + 8 wave + j
+    unsigned long long best = 0ull;           // thread j < kCB: running best of chunk n0 + j
     for (int t0 = 0; t0 < Tq; t0 += 256) {
-        float acc[4][8];
+        f32x16 acc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+            for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
         for (int e0 = 0; e0 < RW; e0 += kEB) {
-            __syncthreads();                   // every thread done with the previous stage
-            for (int i = tid; i < 256 * kEB; i += 256) {
-                const int r = i / kEB, c = i % kEB;
-                sU[r * kUS + c] = (t0 + r < Tq) ? U[(b * Tq + t0 + r) * int64_t(RW) + e0 + c] : 0.f;
+            __syncthreads();                   // every wave done with the previous stage
+            for (int i = tid; i < 256 * (kEB / 4); i += 256) {
+                const int r = i / (kEB / 4), c = (i % (kEB / 4)) * 4;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t0 + r < Tq) v = *reinterpret_cast<const float4*>(U + (b * Tq + t0 + r) * int64_t(RW) + e0 + c);
+                *reinterpret_cast<float2*>(sU + r * kSS + c) = make_float2(v.x, v.y);
+                *reinterpret_cast<float2*>(sU + r * kSS + c + 2) = make_float2(v.z, v.w);
             }
             for (int i = tid; i < kCB * kEB; i += 256) {
                 const int j = i / kEB, c = i % kEB;
@@ -107,73 +118,67 @@ __global__ __launch_bounds__(256) void rbwd_chunkmax_kernel(
                     const int64_t n = n0 + j;
                     v = Elem<T>::load(Kr, n * RW + e0 + c) / fmaxf(knorm[n * hkv + (e0 + c) / D], kEps);
                 }
-                sK[i] = v;
+                sK[j * kSS + c] = v;
             }
             __syncthreads();
 #pragma unroll
             for (int c = 0; c < kEB; c += 4) {
-                float4 u[4], k[8];
+                const float2 kb = *reinterpret_cast<const float2*>(sK + (lane % 32) * kSS + c + 2 * half);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const float4*>(sU + (lane + 64 * i) * kUS + c);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) k[j] = *reinterpret_cast<const float4*>(sK + (8 * wave + j) * kEB + c);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                    {
-                        acc[i][j] = fmaf(u[i].x, k[j].x, acc[i][j]);
-                        acc[i][j] = fmaf(u[i].y, k[j].y, acc[i][j]);
-                        acc[i][j] = fmaf(u[i].z, k[j].z, acc[i][j]);
-                        acc[i][j] = fmaf(u[i].w, k[j].w, acc[i][j]);
-                    }
+                for (int m = 0; m < 2; ++m) {
+                    const float2 ua =
+                        *reinterpret_cast<const float2*>(sU + (64 * wave + 32 * m + lane % 32) * kSS + c + 2 * half);
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(ua.x, kb.x, acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(ua.y, kb.y, acc[m], 0, 0, 0);
+                }
             }
         }
-        // best token of each of the wave's chunks over this block of tokens
+        // best token of each chunk (the lane's column) over this block of tokens
+        unsigned long long key = 0ull;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            unsigned long long key = 0ull;
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + lane + 64 * i;
+            for (int i = 0; i < 16; ++i) {
+                const int t = t0 + 64 * wave + 32 * m + (i / 4) * 8 + half * 4 + (i % 4);
                 if (t < Tq) {
                     const unsigned long long kk =
-                        (static_cast<unsigned long long>(order32(acc[i][j] * inv_hq)) << 32) | (0xFFFFFFFFu - uint32_t(t));
+                        (static_cast<unsigned long long>(order32(acc[m][i] * inv_hq)) << 32) | (0xFFFFFFFFu - uint32_t(t));
                     key = kk > key ? kk : key;
                 }
             }
+        const unsigned long long other = __shfl_xor(key, 32);
+        key = other > key ? other : key;
+        if (lane < kCB) s_key[wave][lane] = key;
+        __syncthreads();
+        if (tid < kCB) {
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const unsigned long long other = __shfl_xor(key, o);
-                key = other > key ? other : key;
-            }
-            if (lane == j) best = key > best ? key : best;
+            for (int w = 0; w < 4; ++w) best = s_key[w][tid] > best ? s_key[w][tid] : best;
         }
     }
-    const int j = 8 * wave + lane;
-    if (lane < 8 && j < nb) ckey[b * N + n0 + j] = best;
+    if (tid < nb) ckey[b * N + n0 + tid] = best;
 }
 
 // Per (b, doc) with a non-zero gradient: the arg max over the document's
 // chunks (the first chunk among equal scores) of the per-chunk best keys,
 // then the per-head cosines there.
 template <typename T>
-__global__ __launch_bounds__(64) void rbwd_docmax_kernel(
+__global__ __launch_bounds__(256) void rbwd_docmax_kernel(
     const T* __restrict__ Qr, int Tq, int Hq, const T* __restrict__ Kr, int64_t N, int hkv, int D,
     const int64_t* __restrict__ chunk_off, int64_t n_docs, const float* __restrict__ dscore,
     const unsigned long long* __restrict__ ckey, const float* __restrict__ knorm, int2* __restrict__ arg,
     float* __restrict__ cosv) {
     const int64_t doc = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int64_t bd = b * n_docs + doc;
     int64_t n_lo = chunk_off[doc], n_hi = chunk_off[doc + 1];
     n_lo = n_lo < 0 ? 0 : (n_lo > N ? N : n_lo);
     n_hi = n_hi < n_lo ? n_lo : (n_hi > N ? N : n_hi);
     if (dscore[bd] == 0.f || n_hi == n_lo) {
-        if (lane == 0) arg[bd] = make_int2(-1, -1);
+        if (threadIdx.x == 0) arg[bd] = make_int2(-1, -1);
         return;
     }
-    // lane-strided scan, then a wave max of (score, -chunk, -token)
+    // lane-strided scan, then a wave max of (score, -chunk, -token) (every wave
+    // finds the same arg max)
     unsigned long long hi = 0ull;             // order32(score) << 32 | ~n_local
     uint32_t tok = 0;
     for (int64_t n = n_lo + lane; n < n_hi; n += kWave) {
@@ -195,9 +200,9 @@ __global__ __launch_bounds__(64) void rbwd_docmax_kernel(
     }
     const int64_t n = n_lo + (0xFFFFFFFFu - uint32_t(hi & 0xFFFFFFFFull));
     const int t = int(tok);
-    if (lane == 0) arg[bd] = make_int2(int(n), t);
+    if (threadIdx.x == 0) arg[bd] = make_int2(int(n), t);
     const int G = Hq / hkv;
-    for (int h = 0; h < Hq; ++h) {
+    for (int h = wave; h < Hq; h += 4) {
         const int g = h / G;
         float qq = 0.f, qk = 0.f;
         for (int c = lane; c < D; c += kWave) {
@@ -280,46 +285,62 @@ __global__ __launch_bounds__(256) void rbwd_dq_kernel(
     }
 }
 
+// One workgroup per document, one wave per chunk row of it (waves stride
+// the rows): the queries whose arg max chunk is the row, in query order.
 template <typename T>
 __global__ __launch_bounds__(256) void rbwd_dk_kernel(
     const T* __restrict__ Kr, int64_t N, int hkv, int D, int Tq, int Hq, const int64_t* __restrict__ chunk_off,
     int64_t n_docs, int64_t B, const float* __restrict__ dscore, const float* __restrict__ U,
     const float* __restrict__ knorm, const int2* __restrict__ arg, const float* __restrict__ cosv,
     float* __restrict__ dKr) {
-    extern __shared__ float smem[];
-    const int RW = hkv * D;
-    float* A = smem;                          // [RW]: sum of w sum_{h in g} q^_h
-    float* C = smem + RW;                     // [hkv]: sum of w sum_{h in g} c_h
     const int64_t doc = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     int64_t n_lo = chunk_off[doc], n_hi = chunk_off[doc + 1];
     n_lo = n_lo < 0 ? 0 : (n_lo > N ? N : n_lo);
     n_hi = n_hi < n_lo ? n_lo : (n_hi > N ? N : n_hi);
+    const int RW = hkv * D;
     const int G = Hq / hkv;
     const float inv_hq = 1.f / float(Hq);
-    for (int64_t n = n_lo; n < n_hi; ++n) {
-        __syncthreads();
-        for (int e = tid; e < RW; e += 256) A[e] = 0.f;
-        for (int g = tid; g < hkv; g += 256) C[g] = 0.f;
-        __syncthreads();
+    constexpr int kMaxPer = 32;                // elements per lane: RW <= 2048
+    const int per = RW / kWave;
+    for (int64_t n = n_lo + wave; n < n_hi; n += 4) {
+        float acc[kMaxPer];
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) acc[i] = 0.f;
+        bool any = false;
         for (int64_t b = 0; b < B; ++b) {
             const int2 a = arg[b * n_docs + doc];
             if (a.x != int(n)) continue;
+            any = true;
             const float w = dscore[b * n_docs + doc] * inv_hq;
             const float* ur = U + (b * Tq + a.y) * int64_t(RW);
-            for (int e = tid; e < RW; e += 256) A[e] += w * ur[e];
-            for (int g = tid; g < hkv; g += 256) {
+#pragma unroll
+            for (int i = 0; i < kMaxPer; ++i)
+                if (i < per) acc[i] += w * ur[lane + kWave * i];
+        }
+        if (!any) {                            // no gradient reaches this row
+#pragma unroll
+            for (int i = 0; i < kMaxPer; ++i)
+                if (i < per) dKr[n * RW + lane + kWave * i] = 0.f;
+            continue;
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            if (i >= per) break;
+            const int e = lane + kWave * i, g = e / D;
+            // the same queries' w sum_{h in g} c_h
+            float c = 0.f;
+            for (int64_t b = 0; b < B; ++b) {
+                const int2 a = arg[b * n_docs + doc];
+                if (a.x != int(n)) continue;
                 float cs = 0.f;
                 for (int h = g * G; h < (g + 1) * G; ++h) cs += cosv[(b * n_docs + doc) * Hq + h];
-                C[g] += w * cs;
+                c += dscore[b * n_docs + doc] * inv_hq * cs;
             }
-        }
-        __syncthreads();
-        for (int e = tid; e < RW; e += 256) {
-            const float nk = knorm[n * hkv + e / D];
+            const float nk = knorm[n * hkv + g];
             float d;
-            if (nk > kEps) d = (A[e] - C[e / D] * Elem<T>::load(Kr, n * RW + e) / nk) / nk;
-            else d = A[e] / kEps;
+            if (nk > kEps) d = (acc[i] - c * Elem<T>::load(Kr, n * RW + e) / nk) / nk;
+            else d = acc[i] / kEps;
             dKr[n * RW + e] = d;
         }
     }
@@ -354,22 +375,21 @@ hipError_t launch_rbwd_t(const RouteBwdArgs& a, hipStream_t st) {
     const T* Kr = static_cast<const T*>(r.Krbar);
     hipError_t err = launch_route_prep(r, U, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((rbwd_knorm_kernel<T>), dim3(unsigned(r.N * r.Hkv)), dim3(64), 0, st, Kr, r.N, r.Hkv, r.D,
-                       knorm);
+    hipLaunchKernelGGL((rbwd_knorm_kernel<T>), dim3(unsigned(ceil_div(r.N * r.Hkv, int64_t(16)))), dim3(256), 0, st,
+                       Kr, r.N * r.Hkv, r.D, knorm);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL((rbwd_chunkmax_kernel<T>), dim3(unsigned(ceil_div(r.N, int64_t(kCB))), unsigned(r.B)),
                        dim3(256), 0, st, U, r.Tq, r.Hq, Kr, r.N, r.Hkv, r.D, knorm, ckey);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((rbwd_docmax_kernel<T>), dim3(unsigned(r.n_docs), unsigned(r.B)), dim3(64), 0, st, Qr, r.Tq,
+    hipLaunchKernelGGL((rbwd_docmax_kernel<T>), dim3(unsigned(r.n_docs), unsigned(r.B)), dim3(256), 0, st, Qr, r.Tq,
                        r.Hq, Kr, r.N, r.Hkv, r.D, r.chunk_off, r.n_docs, a.dscore, ckey, knorm, arg, cosv);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const size_t dq_lds = size_t(r.Hkv * r.D + 2 * r.Hq) * sizeof(float);
     hipLaunchKernelGGL((rbwd_dq_kernel<T>), dim3(unsigned(r.Tq), unsigned(r.B)), dim3(256), dq_lds, st, Qr, r.Tq,
                        r.Hq, Kr, r.Hkv, r.D, r.n_docs, a.dscore, knorm, arg, cosv, a.dQr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const size_t dk_lds = size_t(r.Hkv * r.D + r.Hkv) * sizeof(float);
-    hipLaunchKernelGGL((rbwd_dk_kernel<T>), dim3(unsigned(r.n_docs)), dim3(256), dk_lds, st, Kr, r.N, r.Hkv, r.D,
-                       r.Tq, r.Hq, r.chunk_off, r.n_docs, r.B, a.dscore, U, knorm, arg, cosv, a.dKr);
+    hipLaunchKernelGGL((rbwd_dk_kernel<T>), dim3(unsigned(r.n_docs)), dim3(256), 0, st, Kr, r.N,
+                       r.Hkv, r.D, r.Tq, r.Hq, r.chunk_off, r.n_docs, r.B, a.dscore, U, knorm, arg, cosv, a.dKr);
     return hipGetLastError();
 }
 
