@@ -33,34 +33,35 @@
 //   read below hits distinct LDS banks across each 16 lanes, and a tile is
 //   staged into LDS as one flat 8 KB copy.
 //
-//   bwd_dkdv    a workgroup (8 waves) owns 128 keys of one (b, KV head).  Waves
-//               0..3 form dV and waves 4..7 dK, wave w taking keys
-//               32 (w % 4) .. +31, so a SIMD runs one wave of each role and
-//               each wave holds only its role's accumulators (32 x 128 fp32)
-//               next to its keys' K (and, for dK, V) as matrix-core operands:
-//               everything stays in the 256 registers of two waves per SIMD.
-//               The workgroup walks the query tiles that can see its keys from
-//               the last one down, the G query heads of a tile together (so the
-//               workgroups of one KV head running at the same time read the
-//               same tiles, from L2), each staged in LDS by direct
-//               global->LDS copies one tile ahead.  Per 32 x 32 block a wave
-//               runs S = Q K^T (and, for dK, dP = dO V^T) on
-//               v_mfma_f32_32x32x16_bf16 (keys along the accumulator's
-//               columns), forms P (or dS) in registers, then dV += P^T dO (or
-//               dK += dS^T Q) against the transposed tile.  A k-step takes its
-//               16 queries in the order the accumulator holds them ({16k + 4u
-//               .. +3, 16k + 8 + 4u .. +3} for lane half u), which is two
-//               8-byte units of a transposed row, so P and dS need no shuffle.
+//   bwd_dkdv    a workgroup (8 waves) owns 128 keys of one (b, KV head); wave
+//               w takes keys 32 (w % 4) .. +31, waves 0..3 forming dV and waves
+//               4..7 dK, so a SIMD runs one wave of each role and each wave
+//               keeps only its accumulators (32 x 128 fp32) and one operand
+//               (K or V of its keys) in registers.  The workgroup walks the
+//               query tiles that can see its keys in pairs, from the last pair
+//               down, the G heads of a pair together (so the workgroups of one
+//               KV head running at the same time read the same tiles, from
+//               L2); a pair is staged in LDS by direct global->LDS copies one
+//               pair ahead.  Per pair, in two phases split by a barrier: the
+//               dV wave forms S = Q K^T of both tiles on
+//               v_mfma_f32_32x32x16_bf16 (two interleaved chains, keys along
+//               the accumulator's columns), P = exp2(S log2 e - lse), and hands
+//               P (bf16) to the dK wave of the same keys through LDS while that
+//               wave forms dP = dO V^T; then the dV wave runs dV += P^T dO and
+//               the dK wave dS = P (dP - D), dK += dS^T Q, against the
+//               transposed tiles.  A k-step takes its 16 queries in the order
+//               the accumulator holds them ({16k + 4u .. +3, 16k + 8 + 4u ..
+//               +3} for lane half u), which is two 8-byte units of a transposed
+//               row, so P and dS need no shuffle.
 //   bwd_dq      a workgroup (4 waves) owns 32-token query tiles of up to four
 //               query heads of one KV group (for G < 4, several tiles of each
 //               head), so every staged key tile serves all four waves.  Each
 //               wave keeps its Q and dO as operands and walks the key tiles its
 //               tokens can see: S^T = K Q^T and dP^T = V dO^T (tokens along the
 //               columns), then dQ^T += K^T dS^T.
-// S is formed twice in bwd_dkdv (once per role) and dQ apart from dK/dV (S and
-// dP again), so that no gradient is accumulated with atomics: every output
-// element is written once, in bf16, and the result does not depend on
-// scheduling.  Workgroups take the
+// dQ is computed apart from dK/dV (S and dP again), so that no gradient is
+// accumulated with atomics: every output element is written once, in bf16,
+// and the result does not depend on scheduling.  Workgroups take the
 // heaviest tiles first; when B * Hkv is a multiple of the 8 XCDs, all
 // workgroups of one (b, KV head) share an XCD and its L2.
 #include "launch.hpp"
@@ -78,7 +79,6 @@ constexpr int kTile = RB * DH / 8;           // 16-byte units of a tile: 512 (8 
 constexpr int kStat = 16;                    // 16-byte units of a query tile's statistics (64 floats)
 constexpr int kKeysWg = 128;                 // keys per bwd_dkdv workgroup (4 waves x 32)
 constexpr int kStageQ = 4 * kTile + kStat;   // one bwd_dkdv stage: Q, Q^T, dO, dO^T, statistics
-constexpr int kStagesQ = 2;                  // bwd_dkdv: tile it in use while tile it+1 arrives
 constexpr int kStageK = 3 * kTile;           // one bwd_dq stage: K, K^T, V
 constexpr int PST = DH + 8;                  // LDS staging row stride (bf16) of the prep kernels
 constexpr float kLog2e = 1.4426950408889634f;
@@ -241,7 +241,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const u32x4* __restrict__ VB, const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows, int Tq,
     int Hq, int hkv, int L, int q_offset, const float2* __restrict__ rope, int max_pos, int nqb, int nkb,
     int64_t B, uint16_t* __restrict__ dKVmem, uint16_t* __restrict__ dKl, uint16_t* __restrict__ dVl) {
-    __shared__ __attribute__((aligned(16))) u32x4 sbuf[kStagesQ * kStageQ];
+    // two stages of a tile pair, then P of the pair as packed bf16 operands
+    // ([4 quarters][2 tiles][2 operands][64 lanes])
+    __shared__ __attribute__((aligned(16))) u32x4 sbuf[2 * 2 * kStageQ + 4 * 2 * 2 * kWave];
     const int64_t n_bg = B * hkv;
     const int kt = int(blockIdx.x / n_bg);          // key tiles in order: the first (heaviest) first
     const int64_t bg = blockIdx.x % n_bg;
@@ -258,22 +260,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     if (k0 >= n_keys) return;                       // the whole workgroup: past this query's keys
     const int G = Hq / hkv;
     const int64_t shift = M + (L - Tq);             // token i sees keys 0 .. shift + i
-    const int qb0 = k0 <= shift ? 0 : int((k0 - shift) / RB);
-    const int n_it = G * (nqb - qb0);
+    const int qb0 = k0 <= shift ? 0 : int((k0 - shift) / RB);   // the first query tile seeing the keys
+    // the walk: pairs of query tiles (nqb-1, nqb-2), (nqb-3, nqb-4), ... down to
+    // qb0, the G heads of a pair together
+    const int n_it = G * ((nqb - qb0 + 1) / 2);
     const int64_t kw0 = k0 + 32 * kq;               // the wave's first key
     const int qbw = kw0 <= shift ? 0 : int((kw0 - shift) / RB);   // the wave's first query tile
-    const int wave_its = G * (nqb - qbw);           // the wave works on the first wave_its tiles of the walk
+    const int wave_its = qbw > nqb - 1 ? 0 : G * ((nqb - 1 - qbw) / 2 + 1);   // pairs whose first tile it sees
     const int64_t kcol = kw0 + lane % 32;           // this lane's key (a column of S)
 
-    // K (both roles, for S) and V (dK role, for dP) of the wave's 32 keys as B operands
-    bf16x8 kf[8], vf[8];
+    // the wave's 32 keys as B operands: K in the dV role (for S), V in the dK
+    // role (for dP)
+    bf16x8 kvf[8];
     {
         const int64_t tk = (bg * nkb + kt * 4 + kq) * kTile;
+        const u32x4* src = kside ? VB : KB;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            kf[ks] = __builtin_bit_cast(bf16x8, KB[tk + row_unit(lane % 32, 2 * ks + half)]);
-            vf[ks] = kside ? __builtin_bit_cast(bf16x8, VB[tk + row_unit(lane % 32, 2 * ks + half)]) : kf[ks];
-        }
+        for (int ks = 0; ks < 8; ++ks) kvf[ks] = __builtin_bit_cast(bf16x8, src[tk + row_unit(lane % 32, 2 * ks + half)]);
     }
     f32x16 acc[4];                                  // dV (waves 0..3) or dK (waves 4..7)
 #pragma unroll
@@ -282,78 +285,139 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
 
     const uint32_t lds0 = lds_addr(sbuf);
-    // walk order: query tiles from the last down to qb0, the G heads of a tile
-    // together, so the workgroups of one (b, KV head) running at the same time
-    // read the same tiles and share them in L2
+    const int64_t qbase = (b * Hq + int64_t(g) * G) * nqb;
+    int hh_c = 0, qa_c = nqb - 1;                   // cursor of the next pair to copy
     auto dma = [&](int it) {
-        const int h = g * G + it % G, qb = nqb - 1 - it / G;
-        const int64_t qt = (b * Hq + h) * nqb + qb;
-        const uint32_t sb = lds0 + uint32_t(it % kStagesQ) * kStageQ * 16;
-        if (wave == 0 && lane < kStat)
-            lds_copy16(ST + qt * kStat + lane, __builtin_amdgcn_readfirstlane(sb + 4 * kTile * 16));
+        const uint32_t sb = lds0 + uint32_t(it & 1) * 2 * kStageQ * 16;
         const u32x4* srcs[4] = {QB, QT, OB, OT};
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            lds_copy16(srcs[tt] + qt * kTile + wave * 64 + lane,
-                       __builtin_amdgcn_readfirstlane(sb + (tt * kTile + wave * 64) * 16));
+        for (int t = 0; t < 2; ++t) {
+            const int qb = qa_c - t;
+            if (qb < qb0) break;                    // the last pair may hold one tile
+            const int64_t qt = qbase + int64_t(hh_c) * nqb + qb;
+            const uint32_t st = sb + uint32_t(t) * kStageQ * 16;
+            if (wave == t && lane < kStat)
+                lds_copy16(ST + qt * kStat + lane, __builtin_amdgcn_readfirstlane(st + 4 * kTile * 16));
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                lds_copy16(srcs[tt] + qt * kTile + wave * 64 + lane,
+                           __builtin_amdgcn_readfirstlane(st + (tt * kTile + wave * 64) * 16));
+        }
+        if (++hh_c == G) {
+            hh_c = 0;
+            qa_c -= 2;
+        }
     };
+    u32x4* pbuf = sbuf + 2 * 2 * kStageQ + kq * 2 * 2 * kWave;   // this quarter's P: [2 tiles][2 operands][64]
 
-    dma(0);
-    for (int it = 0; it < n_it; ++it) {
-        MSA_WAIT_VMCNT(0);
-        __syncthreads();                            // tile it in LDS; every wave done with tile it - 1
-        if (it + 1 < n_it) dma(it + 1);
-        if (it >= wave_its) continue;               // no token of this tile sees the wave's keys
-        const u32x4* sQ = sbuf + (it % kStagesQ) * kStageQ;
-        const u32x4* sQT = sQ + kTile;
-        const u32x4* sO = sQ + 2 * kTile;
-        const u32x4* sOT = sQ + 3 * kTile;
-        const float* sst = reinterpret_cast<const float*>(sQ + 4 * kTile);
-        const int i0 = (nqb - 1 - it / G) * RB;
-        // every token of the tile sees every key of the wave (rows past Tq have P = 0 anyway)
+    // P (or dS) of one tile from its scores, keys past a token's causal edge
+    // masked only on tiles that cross the wave's keys (rows past Tq have
+    // lse = +inf, so P = 0 there anyway)
+    auto probs = [&](const f32x16& sc, const float* sst, int i0, float* p) {
+        int64_t need = kcol - shift - i0;           // the token row from which this lane's key is visible
+        need = need < -1 ? -1 : (need > RB ? RB : need);
+        const int thr = int(need) - 4 * half;       // visible iff (i/4)*8 + i%4 >= thr
         const bool full = shift + i0 >= kw0 + 31;
-
-        // S = Q K^T (both roles), dP = dO V^T (dK role)
-        f32x16 sc, dp;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, sQ[row_unit(lane % 32, 2 * ks + half)]);
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sc, 0, 0, 0);
-        }
-        if (kside) {
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 oa = __builtin_bit_cast(bf16x8, sO[row_unit(lane % 32, 2 * ks + half)]);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
-            }
-        }
-        // P (dV role) or dS = P (dP - D) (dK role), packed as A operands
-        float w[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float4 l4 = *reinterpret_cast<const float4*>(sst + 8 * j + 4 * half);
-            float4 d4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kside) d4 = *reinterpret_cast<const float4*>(sst + 32 + 8 * j + 4 * half);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * j + e;
                 float pv = __builtin_amdgcn_exp2f(sc[i] * kLog2e - lv[e]);
-                if (!full && kcol > shift + i0 + acc_row(i, half)) pv = 0.f;
-                w[i] = kside ? pv * (dp[i] - dd[e]) : pv;
+                if (!full) pv = ((i / 4) * 8 + (i % 4) >= thr) ? pv : 0.f;
+                p[i] = pv;
             }
         }
-        const bf16x8 wa[2] = {pack_operand(w), pack_operand(w + 8)};
-        // dV += P^T dO or dK += dS^T Q, against the transposed tile
-        const u32x4* tt = kside ? sQT : sOT;
+    };
+
+    // Per pair, in two phases split by a barrier: the dV waves form S and P of
+    // both tiles (two interleaved chains) and hand P to the dK waves of the
+    // same keys through LDS while those form dP; then the dV waves run
+    // dV += P^T dO and the dK waves dS = P (dP - D), dK += dS^T Q.  S and the
+    // exponentials are computed once; each wave runs 32 products per pair.
+    dma(0);
+    int hh = 0, ia = (nqb - 1) * RB;                // head and first token of the pair's first tile
+    for (int it = 0; it < n_it; ++it) {
+        MSA_WAIT_VMCNT(0);
+        __syncthreads();                            // pair it in LDS; every wave done with pair it - 1
+        if (it + 1 < n_it) dma(it + 1);
+        const int iA = ia, iB = ia - RB;
+        if (++hh == G) {
+            hh = 0;
+            ia -= 2 * RB;
+        }
+        const bool act = it < wave_its;
+        const bool bv = act && iB >= qbw * RB;      // the pair's second tile exists and is seen
+        const u32x4* sA = sbuf + (it & 1) * 2 * kStageQ;
+        const u32x4* sB = sA + kStageQ;
+        f32x16 xa, xb;                              // S (dV role) or dP (dK role) of the two tiles
+        if (act) {
+            const int off = kside ? 2 * kTile : 0;  // dO rows for dP, Q rows for S
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int i = 0; i < 16; ++i) xa[i] = xb[i] = 0.f;
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-                acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[kk], tr_operand(tt, n * 32 + lane % 32, kk, half),
-                                                                 acc[n], 0, 0, 0);
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, sA[off + row_unit(lane % 32, 2 * ks + half)]);
+                xa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kvf[ks], xa, 0, 0, 0);
+                if (bv) {
+                    const bf16x8 a2 = __builtin_bit_cast(bf16x8, sB[off + row_unit(lane % 32, 2 * ks + half)]);
+                    xb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, kvf[ks], xb, 0, 0, 0);
+                }
+            }
+        }
+        if (!kside && act) {
+            float p[16];
+            probs(xa, reinterpret_cast<const float*>(sA + 4 * kTile), iA, p);
+            pbuf[lane] = pack8(p);
+            pbuf[kWave + lane] = pack8(p + 8);
+            if (bv) {
+                probs(xb, reinterpret_cast<const float*>(sB + 4 * kTile), iB, p);
+                pbuf[2 * kWave + lane] = pack8(p);
+                pbuf[3 * kWave + lane] = pack8(p + 8);
+            }
+        }
+        __syncthreads();                            // P of the pair visible to the dK waves
+        if (!act) continue;
+        if (kside) {
+            auto dk_tile = [&](const u32x4* sT, const f32x16& dp, const u32x4* pt) {
+                const float* sst = reinterpret_cast<const float*>(sT + 4 * kTile);
+                const u32x4 p0 = pt[lane], p1 = pt[kWave + lane];
+                float ds[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(sst + 32 + 8 * j + 4 * half);
+                    const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * j + e;
+                        ds[i] = elem(i < 8 ? p0 : p1, i % 8) * (dp[i] - dd[e]);
+                    }
+                }
+                const bf16x8 da[2] = {pack_operand(ds), pack_operand(ds + 8)};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int n = 0; n < 4; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            da[kk], tr_operand(sT + kTile, n * 32 + lane % 32, kk, half), acc[n], 0, 0, 0);
+            };
+            dk_tile(sA, xa, pbuf);
+            if (bv) dk_tile(sB, xb, pbuf + 2 * kWave);
+        } else {
+            auto dv_tile = [&](const u32x4* sT, const u32x4* pt) {
+                const bf16x8 pa[2] = {__builtin_bit_cast(bf16x8, pt[lane]), __builtin_bit_cast(bf16x8, pt[kWave + lane])};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int n = 0; n < 4; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            pa[kk], tr_operand(sT + 3 * kTile, n * 32 + lane % 32, kk, half), acc[n], 0, 0, 0);
+            };
+            dv_tile(sA, pbuf);
+            if (bv) dv_tile(sB, pbuf + 2 * kWave);
+        }
     }
 
     // ---- store: register i holds key kw0 + acc_row(i, half), column n*32 + lane%32
