@@ -33,7 +33,7 @@ from .route import (cosine, chunk_scores, chunk_scores_loops, doc_scores,
 from .gather import gather_rows
 from .attention import sparse_attn, sparse_attn_loops
 from .backward import (sparse_attn_lse, sparse_attn_bwd, sparse_attn_bwd_sampled, doc_score_argmax,
-                       route_score_bwd)
+                       route_score_bwd, encode_pool_bwd)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_to_f64",
@@ -44,4 +44,5 @@ __all__ = [
     "gather_rows",
     "sparse_attn", "sparse_attn_loops",
     "sparse_attn_lse", "sparse_attn_bwd", "sparse_attn_bwd_sampled", "doc_score_argmax", "route_score_bwd",
+    "encode_pool_bwd",
 ]

@@ -36,6 +36,10 @@ Readings taken where the pages are silent:
   constant and contributes no derivative.
 * The saved forward statistic of a query row is the natural-log
   log-sum-exp of its visible scaled logits.
+* Pooling (neo-ai.one article, アーキテクチャ: chunk means of the documents'
+  K/V/Kr, keys rotated at document-local positions): a chunk mean passes
+  1/count of its gradient to each of its rows; a key row's share is turned
+  back by its document-local angle.
 
 Parity status: pinned (tests/test_oracle_backward.py): every element of every
 gradient against central finite differences of the pinned forward oracles on
@@ -44,12 +48,14 @@ so the rotated key gradients of a query row sum to 0); the value-gradient sum
 (rows of P sum to 1); the bilinear identity <Q, dQ> = <K, dK> over all keys;
 the scale invariance of the cosine (<q, dq> = 0, <k, dk> = 0); log-sum-exp
 closed forms (Q = 0 gives log of the visible count; it reproduces the forward
-output).
+output); the pooling backward against finite differences of encode_pool and
+by its chunk sums (the rows of a chunk sum back to the pooled gradient).
 """
 
 import numpy as np
 
 from .attention import sparse_attn
+from .encode import chunk_offsets
 from .rope import rope
 from .route import EPS
 
@@ -258,3 +264,27 @@ def sparse_attn_loss(Q, mem_K, mem_V, mem_off, K_loc, V_loc, k_off, scale, theta
     """sum(dO * O): the scalar whose gradient sparse_attn_bwd returns."""
     O = sparse_attn(Q, mem_K, mem_V, mem_off, K_loc, V_loc, k_off, scale, theta)
     return float(np.sum(np.asarray(dO, dtype=np.float64) * O))
+
+
+def encode_pool_bwd(dKbar, dVbar, dKrbar, doc_tok_off, chunk_len, theta):
+    """Gradients of sum(dKbar * Kbar + dVbar * Vbar + dKrbar * Krbar) for
+    (Kbar, Vbar, Krbar) = encode_pool(K, V, Kr, ...): (dK, dV, dKr), each
+    float64 [T, Hkv, d]."""
+    dKbar = np.asarray(dKbar, dtype=np.float64)
+    dVbar = np.asarray(dVbar, dtype=np.float64)
+    dKrbar = np.asarray(dKrbar, dtype=np.float64)
+    doc_tok_off = np.asarray(doc_tok_off, dtype=np.int64)
+    off = chunk_offsets(doc_tok_off, chunk_len)
+    T = int(doc_tok_off[-1])
+    shape = (T,) + dKbar.shape[1:]
+    dK, dV, dKr = np.zeros(shape), np.zeros(shape), np.zeros(shape)
+    for doc in range(len(doc_tok_off) - 1):
+        s, e = int(doc_tok_off[doc]), int(doc_tok_off[doc + 1])
+        j = np.arange(e - s)                          # document-local positions
+        row = int(off[doc]) + j // chunk_len          # the chunk row of each token
+        cnt = np.minimum((j // chunk_len) * chunk_len + chunk_len, e - s) - (j // chunk_len) * chunk_len
+        w = (1.0 / cnt)[:, None, None]
+        dK[s:e] = rope(dKbar[row] * w, -j[:, None], theta)
+        dV[s:e] = dVbar[row] * w
+        dKr[s:e] = dKrbar[row] * w
+    return dK, dV, dKr

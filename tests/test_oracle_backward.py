@@ -234,3 +234,38 @@ def test_route_gradient_of_a_zero_key_row():
     np.testing.assert_allclose(dQr[0, 0, 0], 0.5 * (kq - cos0 * q0 / np.linalg.norm(q0)) / np.linalg.norm(q0),
                                rtol=1e-10)
     np.testing.assert_allclose(dQr[0, 0, 1], 0.0, atol=0)
+
+
+@pytest.mark.parametrize("chunk_len,lens", [(3, (5, 1, 7)), (1, (2, 3)), (4, (4, 8))])
+def test_encode_pool_gradients_match_finite_differences(chunk_len, lens):
+    rng = np.random.default_rng(40 + chunk_len)
+    tok = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, H, d = int(tok[-1]), 2, 8
+    K, V, Kr = (rng.standard_normal((T, H, d)) for _ in range(3))
+    N = int(oracle.chunk_offsets(tok, chunk_len)[-1])
+    gK, gV, gR = (rng.standard_normal((N, H, d)) for _ in range(3))
+    dK, dV, dKr = bw.encode_pool_bwd(gK, gV, gR, tok, chunk_len, THETA)
+
+    def loss():
+        kb, vb, rb = oracle.encode_pool(K, V, Kr, tok, chunk_len, THETA)
+        return float(np.sum(gK * kb) + np.sum(gV * vb) + np.sum(gR * rb))
+
+    np.testing.assert_allclose(dK, _fd(loss, K), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dV, _fd(loss, V), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dKr, _fd(loss, Kr), rtol=1e-6, atol=1e-8)
+
+
+def test_encode_pool_gradient_rows_sum_to_the_pooled_gradient():
+    rng = np.random.default_rng(8)
+    tok = np.array([0, 10, 13], dtype=np.int64)
+    gK, gV, gR = (rng.standard_normal((5, 2, 8)) for _ in range(3))   # chunks 4: 3 + 2 = 5 rows
+    dK, dV, dKr = bw.encode_pool_bwd(gK, gV, gR, tok, 4, THETA)
+    off = oracle.chunk_offsets(tok, 4)
+    for doc in range(2):
+        s, e = tok[doc], tok[doc + 1]
+        for c, r0 in enumerate(range(s, e, 4)):
+            r1 = min(r0 + 4, e)
+            np.testing.assert_allclose(dV[r0:r1].sum(axis=0), gV[off[doc] + c], rtol=1e-12)
+            np.testing.assert_allclose(dKr[r0:r1].sum(axis=0), gR[off[doc] + c], rtol=1e-12)
+            rot = oracle.rope(dK[r0:r1], (np.arange(r0, r1) - s)[:, None], THETA)   # back to rotated space
+            np.testing.assert_allclose(rot.sum(axis=0), gK[off[doc] + c], rtol=1e-12, atol=1e-14)
