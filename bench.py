@@ -672,6 +672,19 @@ def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
     ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     nbytes = 3 * T * ROW_KR + N * (ROW_KV + ROW_KR)
     finite = bool(torch.isfinite(KVbar).all()) and bool(torch.isfinite(Krbar).all())
+    # the backward of the pooling (msa_encode_pool_bwd): the pooled rows taken as
+    # their own gradients, sent back to every token (written over K, V, Kr)
+    bwd = lambda: msa.msa_encode_pool_bwd(ctx, KVbar, Krbar, tok_d, coff_d, K, V, Kr, CHUNK)
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        bwd()
+        b.record()
+    torch.cuda.synchronize()
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    finite = finite and bool(torch.isfinite(K[:1_000_000]).all())
     ctx.close()
     return {"metric": "offline encode GB/s (doc-wise RoPE + chunk mean-pool of K, V, Kr)",
             "value": round(nbytes / (ms / 1e3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -681,6 +694,9 @@ def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
                                    "KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128], chunk 64",
                        "tokens": T, "n_docs": len(lens), "chunk_rows": N, "max_doc_tokens": int(lens.max())},
             "encode_kernel_ms": round(ms, 4), "outputs_finite": finite,
+            "pool_bwd_kernel_ms": round(bwd_ms, 4),
+            "pool_bwd_GBps": round(nbytes / (bwd_ms / 1e3) / 1e9, 1),
+            "pool_bwd_frac": round(nbytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "traffic": None, "kernel": "encode_pool_kernel", "bytes_per_launch": nbytes}}

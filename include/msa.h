@@ -136,6 +136,31 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt,
                            void* KVbar, void* Krbar, hipStream_t stream);
 
 /*
+ * msa_encode_pool_bwd -- gradients of msa_encode_pool with respect to the
+ * document tokens' K, V and Kr, given the gradients of the pooled rows.
+ * (Training: [neo] アーキテクチャ pools each document's K/V/Kr by chunk means
+ * with document-wise RoPE; [rev] 核心能力 › 端到端可训练框架: the memory is
+ * trained end to end, so the gradients of the pooled rows reach the tokens.)
+ * For document d with tokens [s, e) and its chunk j of rows [r0, r1):
+ *     dK[r]  = RoPE^-1(dK̄[j] / (r1 - r0), r - s)   (rotation back by -angle)
+ *     dV[r]  = dV̄[j] / (r1 - r0)
+ *     dKr[r] = dK̄r[j] / (r1 - r0)
+ *   dKVbar         device [N][2][Hkv][d] of dt (dK̄ then dV̄ per row, the
+ *                  layout of msa_encode_pool's KVbar).
+ *   dKrbar         device [N][Hkv][d] of dt.
+ *   doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv, chunk_len  as for
+ *                  msa_encode_pool.
+ *   dK, dV, dKr    device [T][Hkv][d] of dt (written for every token of a
+ *                  document; rows outside every document untouched).
+ * fp32 arithmetic, one rounding to dt on store.
+ */
+msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt,
+                               const void* dKVbar, const void* dKrbar,
+                               const int64_t* doc_tok_off, const int64_t* doc_chunk_off,
+                               int64_t n_docs, int64_t T, int64_t N, int Hkv, int chunk_len,
+                               void* dK, void* dV, void* dKr, hipStream_t stream);
+
+/*
  * msa_route -- stage 2a (online): cosine routing + document top-k.
  * ([neo] アーキテクチャ: cosine similarity, mean over heads, then max over
  * tokens, top-k documents; [blog] 稀疏注意力机制; [rev] 核心模块.)

@@ -24,7 +24,7 @@ MSA_MAX_TOPK = 64
 EXPORTS = [
     "msa_abi_version", "msa_last_error", "msa_status_string",
     "msa_ctx_create", "msa_ctx_destroy", "msa_chunk_offsets",
-    "msa_encode_pool", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
+    "msa_encode_pool", "msa_encode_pool_bwd", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
     "msa_route_bwd_workspace_size", "msa_route_bwd",
     "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
     "msa_sparse_attn_workspace_size", "msa_sparse_attn",
@@ -54,6 +54,7 @@ _SIGS = {
     "msa_ctx_destroy": (I32, [P]),
     "msa_chunk_offsets": (I32, [P, I64, I32, P]),
     "msa_encode_pool": (I32, [P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, P, P]),
+    "msa_encode_pool_bwd": (I32, [P, I32, P, P, P, P, I64, I64, I64, I32, I32, P, P, P, P]),
     "msa_route_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I64, I32]),
     "msa_route": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, I32, P, P, P, P, P, SZ, P]),
     "msa_route_time_next": (I32, [P, P, P]),
@@ -189,6 +190,16 @@ def msa_encode_pool(ctx, K, V, Kr, doc_tok_off, doc_chunk_off, KVbar, Krbar, chu
     _check(lib().msa_encode_pool(ctx.handle, _dtype(K), _ptr(K), _ptr(V), _ptr(Kr), _ptr(doc_tok_off),
                                  _ptr(doc_chunk_off), doc_tok_off.numel() - 1, T, N, Hkv, chunk_len,
                                  _ptr(KVbar), _ptr(Krbar), _stream(stream)))
+
+
+def msa_encode_pool_bwd(ctx, dKVbar, dKrbar, doc_tok_off, doc_chunk_off, dK, dV, dKr, chunk_len, stream=None):
+    """dKVbar [N, 2, Hkv, d], dKrbar [N, Hkv, d]; offsets int64 device [n_docs+1];
+    dK, dV, dKr [T, Hkv, d] outputs."""
+    T, Hkv, d = dK.shape
+    N = dKrbar.shape[0]
+    _check(lib().msa_encode_pool_bwd(ctx.handle, _dtype(dK), _ptr(dKVbar), _ptr(dKrbar), _ptr(doc_tok_off),
+                                     _ptr(doc_chunk_off), doc_tok_off.numel() - 1, T, N, Hkv, chunk_len,
+                                     _ptr(dK), _ptr(dV), _ptr(dKr), _stream(stream)))
 
 
 # ---------------------------------------------------------------- stage 2

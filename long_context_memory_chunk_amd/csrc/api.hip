@@ -227,6 +227,33 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt, const void* K, const void
     return ok();
 }
 
+msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt, const void* dKVbar, const void* dKrbar,
+                               const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs, int64_t T,
+                               int64_t N, int Hkv, int chunk_len, void* dK, void* dV, void* dKr,
+                               hipStream_t stream) {
+    const char* fn = "msa_encode_pool_bwd";
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+    if (!dtype_ok(dt)) return fail(MSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dt));
+    if (n_docs < 0 || T < 0 || N < 0) return fail(MSA_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (Hkv < 1) return fail(MSA_ERR_INVALID_ARG, "%s: Hkv < 1", fn);
+    if (chunk_len < 1) return fail(MSA_ERR_INVALID_ARG, "%s: chunk_len < 1", fn);
+    if (n_docs > 0x7FFFFFFF) return fail(MSA_ERR_UNSUPPORTED, "%s: n_docs > 2^31-1", fn);
+    if (n_docs > T || n_docs > N || N > T)
+        return fail(MSA_ERR_INVALID_ARG, "%s: need n_docs <= N <= T (%lld, %lld, %lld)", fn, (long long)n_docs,
+                    (long long)N, (long long)T);
+    if (n_docs > 0 && (!dKVbar || !dKrbar || !doc_tok_off || !doc_chunk_off || !dK || !dV || !dKr))
+        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (n_docs > 0 && (!aligned16(dKVbar) || !aligned16(dKrbar) || !aligned16(dK) || !aligned16(dV) ||
+                       !aligned16(dKr)))
+        return fail(MSA_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", fn);
+    DeviceGuard dg(ctx->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_encode_pool_bwd: hipSetDevice");
+    hipError_t e = msa::launch_encode_bwd(ctx, dt, dKVbar, dKrbar, doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv,
+                                          chunk_len, dK, dV, dKr, stream);
+    if (e != hipSuccess) return hip_fail(e, "msa_encode_pool_bwd: launch");
+    return ok();
+}
+
 size_t msa_route_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int64_t N,
                                 int64_t n_docs, int top_k) {
     if (B < 1 || Tq < 1 || Hkv < 1 || N < 0 || n_docs < 1 || top_k < 1) return 0;

@@ -151,6 +151,108 @@ __global__ __launch_bounds__(256) void encode_pool_kernel(
     }
 }
 
+// 16-byte streaming store of VEC floats converted to T (the token-row
+// gradients are written once and not read again here).
+template <typename T> struct St16;
+template <> struct St16<float> {
+    __device__ __forceinline__ static void put(float* p, const float* in) {
+        const u32x4 v = {__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                         __float_as_uint(in[3])};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    }
+};
+template <> struct St16<bf16_t> {
+    __device__ __forceinline__ static void put(bf16_t* p, const float* in) {
+        const u32x4 v = {pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]), pack_bf16x2(in[4], in[5]),
+                         pack_bf16x2(in[6], in[7])};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    }
+};
+
+// Backward of the pooling: every token row of a chunk gets 1/count of the
+// chunk's gradient, the key part turned back by the row's document-local
+// angle.  Same mapping as the forward (one wave per chunk, a lane owning a
+// 16-byte slot of each RoPE half): the pooled gradient row is read once and
+// the chunk's token rows are written.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void encode_bwd_kernel(
+    const T* __restrict__ dKVbar, const T* __restrict__ dKrbar, const int64_t* __restrict__ tok_off,
+    const int64_t* __restrict__ chunk_off, int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
+    const float2* __restrict__ rope_cs, int max_pos, T* __restrict__ dK, T* __restrict__ dV,
+    T* __restrict__ dKr) {
+    constexpr int VEC = Vec16<T>::kN;
+    constexpr int HALF = D / 2;
+    constexpr int SLOTS_PER_HEAD = HALF / VEC;
+    const int lane = threadIdx.x % kWave;
+    const int slots = hkv * SLOTS_PER_HEAD;
+    const int64_t row_elems = int64_t(hkv) * D;
+    const int64_t n_waves = int64_t(gridDim.x) * (blockDim.x / kWave);
+
+    for (int64_t n = int64_t(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave; n < N;
+         n += n_waves) {
+        const int64_t doc = doc_of_chunk(chunk_off, n_docs, n);
+        int64_t s = tok_off[doc], e = tok_off[doc + 1];
+        s = s < 0 ? 0 : (s > T_rows ? T_rows : s);
+        e = e < s ? s : (e > T_rows ? T_rows : e);
+        const int64_t j = n - chunk_off[doc];
+        const int64_t r0 = s + j * chunk_len;
+        if (j < 0 || r0 >= e) continue;         // inconsistent offsets: nothing is written
+        const int64_t r1 = (r0 + chunk_len < e) ? r0 + chunk_len : e;
+        const float inv = 1.f / float(r1 - r0);
+
+        for (int slot = lane; slot < slots; slot += kWave) {
+            const int h = slot / SLOTS_PER_HEAD;
+            const int i0 = (slot % SLOTS_PER_HEAD) * VEC;
+            float k1[VEC], k2[VEC], v1[VEC], v2[VEC], q1[VEC], q2[VEC];
+            const T* kv = dKVbar + n * 2 * row_elems + int64_t(h) * D + i0;
+            const T* kr = dKrbar + n * row_elems + int64_t(h) * D + i0;
+            Vec16<T>::load(kv, k1);
+            Vec16<T>::load(kv + HALF, k2);
+            Vec16<T>::load(kv + row_elems, v1);
+            Vec16<T>::load(kv + row_elems + HALF, v2);
+            Vec16<T>::load(kr, q1);
+            Vec16<T>::load(kr + HALF, q2);
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) {
+                k1[u] *= inv; k2[u] *= inv;
+                v1[u] *= inv; v2[u] *= inv;
+                q1[u] *= inv; q2[u] *= inv;
+            }
+            for (int64_t r = r0; r < r1; ++r) {
+                int pos = int(r - s);
+                pos = pos < max_pos ? pos : max_pos - 1;
+                const float2* cs = rope_cs + int64_t(pos) * HALF + i0;
+                float a[VEC], bb[VEC];
+#pragma unroll
+                for (int w = 0; w < VEC; ++w) {
+                    const float2 t = cs[w];
+                    a[w] = k1[w] * t.x + k2[w] * t.y;     // the transpose of the rotation
+                    bb[w] = k2[w] * t.x - k1[w] * t.y;
+                }
+                const int64_t o = r * row_elems + int64_t(h) * D + i0;
+                St16<T>::put(dK + o, a);
+                St16<T>::put(dK + o + HALF, bb);
+                St16<T>::put(dV + o, v1);
+                St16<T>::put(dV + o + HALF, v2);
+                St16<T>::put(dKr + o, q1);
+                St16<T>::put(dKr + o + HALF, q2);
+            }
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_typed(const msa_ctx* ctx, const void* dKVbar, const void* dKrbar, const int64_t* tok_off,
+                            const int64_t* chunk_off, int64_t n_docs, int64_t T_rows, int64_t N, int hkv,
+                            int chunk_len, void* dK, void* dV, void* dKr, hipStream_t st) {
+    const int64_t blocks = ceil_div(N, int64_t(4));
+    const unsigned grid = unsigned(blocks < (int64_t(1) << 30) ? blocks : (int64_t(1) << 30));
+    hipLaunchKernelGGL((encode_bwd_kernel<T, D>), dim3(grid), dim3(256), 0, st, static_cast<const T*>(dKVbar),
+                       static_cast<const T*>(dKrbar), tok_off, chunk_off, n_docs, T_rows, N, hkv, chunk_len,
+                       ctx->rope_cs, ctx->max_pos, static_cast<T*>(dK), static_cast<T*>(dV), static_cast<T*>(dKr));
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const msa_ctx* ctx, const void* K, const void* V, const void* Kr,
                         const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs,
@@ -185,6 +287,27 @@ hipError_t launch_encode(const msa_ctx* ctx, msa_dtype dt, const void* K, const 
                                         chunk_len, KVbar, Krbar, st);
     return launch_typed<float, 64>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N, hkv,
                                    chunk_len, KVbar, Krbar, st);
+}
+
+}  // namespace msa
+
+namespace msa {
+
+hipError_t launch_encode_bwd(const msa_ctx* ctx, msa_dtype dt, const void* dKVbar, const void* dKrbar,
+                             const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs, int64_t T_rows,
+                             int64_t N, int hkv, int chunk_len, void* dK, void* dV, void* dKr, hipStream_t st) {
+    if (n_docs == 0 || N == 0) return hipSuccess;
+    if (dt == MSA_BF16)
+        return ctx->head_dim == 128
+                   ? launch_bwd_typed<bf16_t, 128>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
+                                                   chunk_len, dK, dV, dKr, st)
+                   : launch_bwd_typed<bf16_t, 64>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
+                                                  chunk_len, dK, dV, dKr, st);
+    return ctx->head_dim == 128
+               ? launch_bwd_typed<float, 128>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
+                                              chunk_len, dK, dV, dKr, st)
+               : launch_bwd_typed<float, 64>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
+                                             chunk_len, dK, dV, dKr, st);
 }
 
 }  // namespace msa

@@ -260,3 +260,35 @@ def test_sparse_attn_bwd_full_size_sampled(torch_mod, msa, ctx128):
     for name, got, ref in (("dQ", got_q, rq), ("dK", allk[key_rows], rk), ("dV", allv[key_rows], rv)):
         print(f"\n{name}: rel max err {_rel(got, ref):.3e}", flush=True)
         assert _rel(got, ref) <= GRAD_TOL, name
+
+
+ENC_CASES = [
+    # dtype, d, Hkv, chunk_len, document lengths
+    ("f32", 64, 2, 16, [256] * 64),                          # the tiny fp32 bank
+    ("bf16", 128, 8, 64, list(range(128, 1024, 37))),       # Qwen-shaped, ragged last chunks
+    ("bf16", 128, 8, 5, [1, 2, 5, 6, 13, 4, 9]),            # short documents, partial chunks
+    ("f32", 128, 4, 1, [3, 1, 7]),                           # chunk 1: one row per token
+]
+
+
+@pytest.mark.parametrize("dtype,d,Hkv,chunk_len,lens", ENC_CASES)
+def test_encode_pool_bwd_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, chunk_len, lens):
+    torch = torch_mod
+    ctx = ctx128 if d == 128 else ctx64
+    tok = msa_synth.prefix_offsets(lens)
+    coff = msa_synth.prefix_offsets([(n + chunk_len - 1) // chunk_len for n in lens])
+    T, N = int(tok[-1]), int(coff[-1])
+    gKV = W.draw(111, 1, (N, 2, Hkv, d), dtype)
+    gR = W.draw(111, 2, (N, Hkv, d), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = [torch.full((T, Hkv, d), float("nan"), dtype=tdt, device="cuda") for _ in range(3)]
+    msa.msa_encode_pool_bwd(ctx, W.dev(gKV, dtype), W.dev(gR, dtype), torch.from_numpy(tok).cuda(),
+                            torch.from_numpy(coff).cuda(), *out, chunk_len)
+    torch.cuda.synchronize()
+    g = W.widen(gKV, dtype)
+    ref = oracle.encode_pool_bwd(g[:, 0], g[:, 1], W.widen(gR, dtype), tok, chunk_len, ctx.rope_theta)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for name, t, r in zip(("dK", "dV", "dKr"), out, ref):
+        got = W.widen(W.host_bits(t), dtype)
+        assert np.all(np.isfinite(got)), name
+        assert W.rel_row_err(got, r) <= tol, (name, W.rel_row_err(got, r))
