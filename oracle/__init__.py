@@ -32,8 +32,8 @@ from .route import (cosine, chunk_scores, chunk_scores_loops, doc_scores,
                     topk_docs, route, EPS)
 from .gather import gather_rows
 from .attention import sparse_attn, sparse_attn_loops
-from .backward import (sparse_attn_lse, sparse_attn_bwd, sparse_attn_bwd_sampled, doc_score_argmax,
-                       route_score_bwd, encode_pool_bwd)
+from .backward import (sparse_attn_lse, sparse_attn_bwd, sparse_attn_bwd_sampled, pair_scores,
+                       doc_score_argmax, route_score_bwd, encode_pool_bwd)
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f32_to_f64",
@@ -43,6 +43,7 @@ __all__ = [
     "route", "EPS",
     "gather_rows",
     "sparse_attn", "sparse_attn_loops",
-    "sparse_attn_lse", "sparse_attn_bwd", "sparse_attn_bwd_sampled", "doc_score_argmax", "route_score_bwd",
+    "sparse_attn_lse", "sparse_attn_bwd", "sparse_attn_bwd_sampled", "pair_scores", "doc_score_argmax",
+    "route_score_bwd",
     "encode_pool_bwd",
 ]

@@ -187,29 +187,40 @@ def sparse_attn_bwd_sampled(Q, mem_K, mem_V, K_loc, V_loc, k_off, scale, theta, 
     return dq, dk, dv
 
 
-def doc_score_argmax(Qr, Krbar, doc_chunk_off, eps=EPS):
-    """Document scores with the (chunk, token) that attains each.
-
-    Returns score [B, n_docs], arg_chunk [B, n_docs] (global chunk row),
-    arg_tok [B, n_docs]; ties go to the lowest chunk, then the lowest token."""
+def pair_scores(Qr, Krbar, eps=EPS):
+    """s[b, n, t] = (1/Hq) sum_h cos(Qr[b,t,h], K̄r[n, h // G]): the score of
+    every (chunk, token) pair, head sum in head order."""
     Qr = np.asarray(Qr, dtype=np.float64)
     Kr = np.asarray(Krbar, dtype=np.float64)
-    off = np.asarray(doc_chunk_off, dtype=np.int64)
     B, T, Hq, d = Qr.shape
     Hkv = Kr.shape[1]
     G = Hq // Hkv
     nq = np.maximum(np.sqrt(np.sum(Qr * Qr, axis=-1, keepdims=True)), eps)
     nk = np.maximum(np.sqrt(np.sum(Kr * Kr, axis=-1, keepdims=True)), eps)
     Qn, Kn = Qr / nq, Kr / nk
+    out = np.empty((B, Kr.shape[0], T))
+    for b in range(B):
+        s = np.zeros((Kr.shape[0], T))
+        for h in range(Hq):
+            s += Kn[:, h // G, :] @ Qn[b, :, h, :].T
+        out[b] = s / Hq
+    return out
+
+
+def doc_score_argmax(Qr, Krbar, doc_chunk_off, eps=EPS):
+    """Document scores with the (chunk, token) that attains each.
+
+    Returns score [B, n_docs], arg_chunk [B, n_docs] (global chunk row),
+    arg_tok [B, n_docs]; ties go to the lowest chunk, then the lowest token."""
+    off = np.asarray(doc_chunk_off, dtype=np.int64)
+    S = pair_scores(Qr, Krbar, eps)
+    B, _, T = S.shape
     n_docs = len(off) - 1
     score = np.empty((B, n_docs))
     arg_c = np.empty((B, n_docs), dtype=np.int64)
     arg_t = np.empty((B, n_docs), dtype=np.int64)
     for b in range(B):
-        s = np.zeros((Kr.shape[0], T))                          # s[n, t], head sum in head order
-        for h in range(Hq):
-            s += Kn[:, h // G, :] @ Qn[b, :, h, :].T
-        s /= Hq
+        s = S[b]
         for doc in range(n_docs):
             blk = s[off[doc]:off[doc + 1]]
             flat = int(np.argmax(blk))                          # first max in (chunk, token) order

@@ -43,13 +43,8 @@ def ctxs(msa):
         v.close()
 
 
-def _scores_all(Qr, Kr):
-    """s[b, n, t]: the oracle's score of every (chunk, token) pair."""
-    return np.stack([oracle.chunk_scores(Qr[:, t:t + 1], Kr) for t in range(Qr.shape[1])], axis=2)
-
-
 def _margins_ok(Qr, Kr, off):
-    s = _scores_all(Qr, Kr)
+    s = oracle.pair_scores(Qr, Kr)
     for doc in range(len(off) - 1):
         blk = s[:, off[doc]:off[doc + 1], :].reshape(s.shape[0], -1)
         if blk.shape[1] > 1:
@@ -154,3 +149,47 @@ def test_route_bwd_is_deterministic(torch_mod, msa, ctxs):
         msa.msa_route_bwd(ctxs[128], Qr, Kr, torch.from_numpy(off).cuda(), dscore, dQr, dKr, ws)
         outs.append((dQr.cpu().numpy(), dKr.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_route_bwd_full_size_routebwd1m(torch_mod, msa, ctxs):
+    """The shape and inputs the bench's routing training pass times: a
+    256-token query over the 1M-token memory of 2,000 documents (lengths
+    uniform in [128, 1024], chunk 64, 19,254 chunk rows), dense dscore.
+    Documents whose best two (chunk, token) scores are within 1e-4 (by the
+    oracle) get dscore = 0, so every remaining arg max is unique."""
+    from msa_synth import device as device_fill
+    torch = torch_mod
+    seed, T, Hq, Hkv, d = 0, 256, 32, 8, 128
+    lens = msa_synth.uniform_lengths(seed, 2000, 128, 1024)
+    coff = msa_synth.prefix_offsets([(int(x) + 63) // 64 for x in lens])
+    n_docs, N = len(lens), int(coff[-1])
+    Qr_d = torch.empty((1, T, Hq, d), dtype=torch.bfloat16, device="cuda")
+    Kr_d = torch.empty((N, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    device_fill.fill_counter_bf16(Qr_d, seed, 730, 0)
+    device_fill.fill_counter_bf16(Kr_d, seed, 731, 0)
+    q64 = W.widen(W.counter_bf16_threads(seed, 730, 0, T * Hq * d).reshape(1, T, Hq, d), "bf16")
+    k64 = W.widen(W.counter_bf16_threads(seed, 731, 0, N * Hkv * d).reshape(N, Hkv, d), "bf16")
+    dscore = msa_synth.normal_f32(seed, 732, (1, n_docs)).astype(np.float32)
+    # margins from the oracle's score of every (chunk, token) pair
+    s = oracle.pair_scores(q64, k64)[0]                                                       # [N, T]
+    for doc in range(n_docs):
+        blk = np.sort(s[coff[doc]:coff[doc + 1]].ravel())
+        if blk[-1] - blk[-2] <= 1e-4:
+            dscore[0, doc] = 0.0
+    live = dscore[0] != 0
+    print(f"\nfull-size route bwd: {int(live.sum())} of {n_docs} documents carry a gradient", flush=True)
+    assert live.sum() > 0.9 * n_docs
+    dQr = torch.empty((1, T, Hq, d), dtype=torch.float32, device="cuda")
+    dKr = torch.empty((N, Hkv, d), dtype=torch.float32, device="cuda")
+    arg = torch.empty((1, n_docs, 2), dtype=torch.int32, device="cuda")
+    ws = msa.workspace(msa.msa_route_bwd_workspace_size(1, T, Hq, Hkv, N, n_docs))
+    msa.msa_route_bwd(ctxs[128], Qr_d, Kr_d, torch.from_numpy(coff).cuda(), torch.from_numpy(dscore).cuda(),
+                      dQr, dKr, ws, out_arg=arg)
+    torch.cuda.synchronize()
+    _, ac, at = oracle.doc_score_argmax(q64, k64, coff)
+    got = arg.cpu().numpy()
+    assert np.array_equal(got[0, live, 0], ac[0, live]) and np.array_equal(got[0, live, 1], at[0, live])
+    rq, rk = oracle.route_score_bwd(q64, k64, coff, dscore.astype(np.float64))
+    gq, gk = dQr.cpu().numpy(), dKr.cpu().numpy()
+    print(f"dQr rel {_rel(gq, rq):.2e}  dKr rel {_rel(gk, rk):.2e}", flush=True)
+    assert _rel(gq, rq) <= GRAD_TOL and _rel(gk, rk) <= GRAD_TOL

@@ -170,6 +170,15 @@ def test_doc_score_argmax_matches_forward_scores():
             np.testing.assert_allclose(one[0, 0], score[b, doc], rtol=1e-12)
 
 
+def test_pair_scores_reduce_to_the_forward_chunk_scores():
+    rng = np.random.default_rng(6)
+    Qr, Kr, off = _route_case(rng, B=2, T=4, lens=(3, 2))
+    S = bw.pair_scores(Qr, Kr)
+    np.testing.assert_allclose(S.max(axis=2), oracle.chunk_scores(Qr, Kr), rtol=1e-14)
+    for t in range(4):
+        np.testing.assert_allclose(S[:, :, t], oracle.chunk_scores_loops(Qr[:, t:t + 1], Kr), rtol=1e-12)
+
+
 def test_doc_score_argmax_ties_go_to_lowest_chunk_then_token():
     rng = np.random.default_rng(4)
     Qr, Kr, off = _route_case(rng, B=1, T=3, lens=(4,))
