@@ -292,3 +292,45 @@ def test_encode_pool_bwd_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, ch
         got = W.widen(W.host_bits(t), dtype)
         assert np.all(np.isfinite(got)), name
         assert W.rel_row_err(got, r) <= tol, (name, W.rel_row_err(got, r))
+
+
+def test_backward_validation_errors(torch_mod, msa, ctx128):
+    """Bad arguments are refused before anything is enqueued."""
+    torch = torch_mod
+    x = _inputs(121, "bf16", 128, 32, 8, 1, 8, 16, [4])
+    dev = {k: W.dev_bf16(x[k]) for k in ("Q", "KV", "Kl", "Vl", "dO")}
+    mo = torch.tensor([0, 4], dtype=torch.int64, device="cuda")
+    O = torch.empty_like(dev["Q"])
+    lse = torch.empty((1, 8, 32), dtype=torch.float32, device="cuda")
+    ws_f = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, 8, 32, 8, 4, 16))
+    with pytest.raises(msa.MsaError) as e:                       # lse missing
+        msa.msa_sparse_attn_lse(ctx128, dev["Q"], dev["KV"], mo, 4, dev["Kl"], dev["Vl"], 16, 0.088, O, None, ws_f)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    msa.msa_sparse_attn_lse(ctx128, dev["Q"], dev["KV"], mo, 4, dev["Kl"], dev["Vl"], 16, 0.088, O, lse, ws_f)
+    g = [torch.empty_like(dev[k]) for k in ("Q", "KV", "Kl", "Vl")]
+    need = msa.msa_sparse_attn_bwd_workspace_size(1, 1, 8, 32, 8, 4, 16)
+    small = msa.workspace(need - 256)
+    with pytest.raises(msa.MsaError) as e:                       # workspace too small
+        msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, 4, dev["Kl"], dev["Vl"], 16, 0.088, O, dev["dO"],
+                                lse, *g, small)
+    assert e.value.status == msa.MSA_ERR_WORKSPACE
+    ws = msa.workspace(need)
+    with pytest.raises(msa.MsaError) as e:                       # Tq > L
+        msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, 4, dev["Kl"][:, :4].contiguous(),
+                                dev["Vl"][:, :4].contiguous(), 16, 0.088, O, dev["dO"], lse, g[0], g[1],
+                                g[2][:, :4].contiguous(), g[3][:, :4].contiguous(), ws)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    with pytest.raises(msa.MsaError) as e:                       # dO missing
+        msa.msa_sparse_attn_bwd(ctx128, dev["Q"], dev["KV"], mo, 4, dev["Kl"], dev["Vl"], 16, 0.088, O, None,
+                                lse, *g, ws)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    # pooling backward: more chunk rows than tokens
+    gkv = torch.zeros((10, 2, 8, 128), dtype=torch.bfloat16, device="cuda")
+    gr = torch.zeros((10, 8, 128), dtype=torch.bfloat16, device="cuda")
+    out = [torch.empty((5, 8, 128), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    tok = torch.tensor([0, 5], dtype=torch.int64, device="cuda")
+    coff = torch.tensor([0, 10], dtype=torch.int64, device="cuda")
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_encode_pool_bwd(ctx128, gkv, gr, tok, coff, *out, 1)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    torch.cuda.synchronize()

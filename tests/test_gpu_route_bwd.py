@@ -193,3 +193,26 @@ def test_route_bwd_full_size_routebwd1m(torch_mod, msa, ctxs):
     gq, gk = dQr.cpu().numpy(), dKr.cpu().numpy()
     print(f"dQr rel {_rel(gq, rq):.2e}  dKr rel {_rel(gk, rk):.2e}", flush=True)
     assert _rel(gq, rq) <= GRAD_TOL and _rel(gk, rk) <= GRAD_TOL
+
+
+def test_route_bwd_validation_errors(torch_mod, msa, ctxs):
+    torch = torch_mod
+    Qr = torch.zeros((1, 2, 32, 128), dtype=torch.bfloat16, device="cuda")
+    Kr = torch.zeros((6, 8, 128), dtype=torch.bfloat16, device="cuda")
+    off = torch.tensor([0, 3, 6], dtype=torch.int64, device="cuda")
+    ds = torch.ones((1, 2), dtype=torch.float32, device="cuda")
+    dQ = torch.empty((1, 2, 32, 128), dtype=torch.float32, device="cuda")
+    dK = torch.empty((6, 8, 128), dtype=torch.float32, device="cuda")
+    ws = msa.workspace(msa.msa_route_bwd_workspace_size(1, 2, 32, 8, 6, 2))
+    with pytest.raises(msa.MsaError) as e:                       # Hq % Hkv
+        msa.msa_route_bwd(ctxs[128], Qr[:, :, :30].contiguous(), Kr, off, ds, dQ[:, :, :30].contiguous(), dK, ws)
+    assert e.value.status == msa.MSA_ERR_INVALID_ARG
+    with pytest.raises(msa.MsaError) as e:                       # workspace too small
+        msa.msa_route_bwd(ctxs[128], Qr, Kr, off, ds, dQ, dK, msa.workspace(256))
+    assert e.value.status == msa.MSA_ERR_WORKSPACE
+    Kr12 = torch.zeros((6, 12, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(msa.MsaError) as e:                       # Hkv * d not a power of two
+        msa.msa_route_bwd(ctxs[128], Qr[:, :, :24].contiguous(), Kr12, off, ds, dQ[:, :, :24].contiguous(),
+                          torch.empty((6, 12, 128), dtype=torch.float32, device="cuda"), ws)
+    assert e.value.status == msa.MSA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
