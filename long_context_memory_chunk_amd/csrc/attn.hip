@@ -14,9 +14,9 @@
 // Three kernels compute it; launch_attn takes the first that applies:
 //   attn_prefill_kernel (attn_mfma.hip)  bf16, d = 128, long query blocks:
 //                                        matrix cores.
-//   attn_decode_kernel (below)           bf16, d = 128, G in {1, 2, 4}:
-//                                        decode and short queries, laid out
-//                                        for HBM bandwidth.
+//   attn_decode_mfma_kernel              bf16, d = 128, G in {1, 2, 4, 8}:
+//     (attn_decode_mfma.hip)             decode and short queries, scores on
+//                                        the matrix cores, P . V on v_dot2.
 //   attn_split_kernel                    any dtype, d in {64, 128}, any G.
 // The last two write partial (m, l, o) per key split; attn_combine merges
 // them exactly.  Every path can also write each row's log-sum-exp (the
@@ -35,6 +35,7 @@
 #include "attn_mfma.hpp"
 
 namespace msa {
+
 namespace {
 
 constexpr int kSplit = 256;
@@ -233,276 +234,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     if (tid < G) part_ml[(bt * Hq + g * G + tid) * P + p] = make_float2(s_m[tid], s_l[tid]);
 }
 
-// ---------------------------------------------------------------- bf16, d = 128
-//
-// attn_decode_kernel: the same key space and mask as attn_split_kernel, laid
-// out for HBM bandwidth.  A workgroup (4 waves) owns NC consecutive 64-key
-// chunks of one (b, i, kv head g) and the G query heads that read g; wave w
-// takes keys 16w .. 16w+15 of every chunk.  16 lanes hold one key: lane c of
-// the 16 owns bytes 16c .. 16c+15 of the 256-byte row, so one wave instruction
-// reads four whole rows; a lane's keys in a chunk are its key slot s = lane /
-// 16 plus 4 it, it = 0 .. 3.  The next chunk's K rows are loaded while this
-// chunk is used (two register buffers), and its V rows as soon as this
-// chunk's P.V is done.  A local key's RoPE pair
-// (i, i + 64) sits in lanes c and c + 8 of the same row of 16 lanes and is
-// exchanged with DPP row_ror:8; a lane's local keys in a chunk are 4 positions
-// apart, so its cos/sin advance by the fixed rotation of 4 positions (angle
-// addition) from the table value at its first local key of the chunk.  The G
-// dot products are summed over the 16 lanes with DPP.  Each wave keeps an
-// online softmax in registers (log2 domain, scale and log2(e) folded into the
-// query; the running max is raised only past m + 2^8 = kLazy); the slots and
-// the waves are merged once, at the end, into one partial (m, l, o) per
-// workgroup, which attn_combine_kernel merges with the others.
-
-__device__ __forceinline__ uint32_t ror8_16(uint32_t v) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));   // row_ror:8
-}
-
-constexpr int kDecodeChunk = 64;             // keys per chunk
-constexpr float kDecodeLazy = 8.f;           // log2 units: raise the running max only past m + 8
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int G>
-__global__ __launch_bounds__(256, 2) void attn_decode_kernel(
-    const bf16_t* __restrict__ Q, int Tq, int Hq, int hkv, const bf16_t* __restrict__ KVmem,
-    const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows,
-    const bf16_t* __restrict__ Kl, const bf16_t* __restrict__ Vl, int L, int q_offset, float qscale,
-    const float2* __restrict__ rope_cs, int max_pos, int P, int NC,
-    float* __restrict__ part_o, float2* __restrict__ part_ml) {
-    constexpr int D = 128, CK = kDecodeChunk, NIT = 4;
-    __shared__ float red[4][G][D];
-    __shared__ float s_m[4][G], s_l[4][G];
-
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int slot = lane / 16, c = lane % 16;
-    const float sgn = (c & 8) ? 1.f : -1.f;      // first half: x1 c - x2 s; second: x2 c + x1 s
-    const int p = blockIdx.x, g = blockIdx.y;
-    const int64_t bt = blockIdx.z;
-    const int64_t b = bt / Tq;
-    const int i = int(bt % Tq);
-
-    int64_t r0 = mem_off[b], r1 = mem_off[b + 1];
-    r0 = r0 < 0 ? 0 : (r0 > cap ? cap : r0);
-    r1 = r1 < r0 ? r0 : (r1 > cap ? cap : r1);
-    if (r1 - r0 > max_rows) r1 = r0 + max_rows;
-    const int64_t M = r1 - r0;
-    const int64_t total = M + int64_t(L - Tq) + i + 1;
-    const int64_t row_elems = int64_t(hkv) * D;
-    const int64_t hrow = bt * Hq + int64_t(g) * G;   // first query head row of this group
-    const int64_t n_chunks = (total + CK - 1) / CK;
-    const int64_t cb = int64_t(p) * NC;
-    const int64_t ce = (cb + NC < n_chunks) ? cb + NC : n_chunks;
-
-    if (cb >= ce) {                              // no keys here: an empty partial
-        for (int idx = tid; idx < G * D; idx += 256) part_o[((hrow + idx / D) * P + p) * D + idx % D] = 0.f;
-        if (tid < G) part_ml[(hrow + tid) * P + p] = make_float2(-INFINITY, 0.f);
-        return;
-    }
-
-    // ---- this lane's 8 elements of the G rotated, scaled query heads
-    float q[G][8];
-    float2 step[8];
-    {
-        u32x4 qw[G];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) qw[hh] = *reinterpret_cast<const u32x4*>(Q + (hrow + hh) * D + c * 8);
-        int pos_q = q_offset + (L - Tq) + i;
-        pos_q = pos_q < max_pos ? pos_q : max_pos - 1;
-        const float2* cs_q = rope_cs + int64_t(pos_q) * (D / 2) + (c % 8) * 8;
-        const float2* st = rope_cs + int64_t(4 < max_pos ? 4 : max_pos - 1) * (D / 2) + (c % 8) * 8;
-        float2 cq[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { cq[e] = cs_q[e]; step[e] = st[e]; }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const u32x4 w = qw[hh];
-            const u32x4 pw = {ror8_16(w[0]), ror8_16(w[1]), ror8_16(w[2]), ror8_16(w[3])};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-                const float px = (e & 1) ? bf16_hi(pw[e / 2]) : bf16_lo(pw[e / 2]);
-                q[hh][e] = (x * cq[e].x + sgn * px * cq[e].y) * qscale;
-            }
-        }
-    }
-
-    // ---- chunk loads: the K rows of this lane's 4 keys (keys past the end load
-    // the last valid key, in bounds, and are masked) with the cos/sin of its
-    // first local key in the chunk, two buffers deep; and the V rows, one
-    // buffer, loaded as soon as the previous chunk's P.V has used them
-    struct Buf {
-        u32x4 k[NIT];
-        float2 seed[8];
-    };
-    u32x4 vbuf[NIT];
-    auto key_ptr = [&](int64_t key, bool value) {
-        key = key < total ? key : total - 1;
-        return (key >= M) ? (value ? Vl : Kl) + ((b * L + (key - M)) * hkv + g) * D
-                          : KVmem + (r0 + key) * 2 * row_elems + (value ? row_elems : 0) + int64_t(g) * D;
-    };
-    auto load_k = [&](int64_t cidx, Buf& bf) {
-        const int64_t kb = cidx * CK + wave * 16 + slot;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-            bf.k[it] = *reinterpret_cast<const u32x4*>(key_ptr(kb + 4 * it, false) + c * 8);
-        const int64_t fl = (M > kb) ? (M - kb + 3) / 4 : 0;          // first it with key >= M
-        int64_t pos = int64_t(q_offset) + kb + 4 * fl - M;
-        pos = pos < 0 ? 0 : (pos < max_pos ? pos : max_pos - 1);
-        const float2* cs = rope_cs + pos * (D / 2) + (c % 8) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bf.seed[e] = cs[e];
-    };
-    auto load_v = [&](int64_t cidx) {
-        const int64_t kb = cidx * CK + wave * 16 + slot;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-            vbuf[it] = *reinterpret_cast<const u32x4*>(key_ptr(kb + 4 * it, true) + c * 8);
-    };
-
-    float m[G], l[G], o[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
-    }
-
-    auto process = [&](int64_t cidx, const Buf& bf, bool next) {
-        const int64_t kb = cidx * CK + wave * 16 + slot;
-        const int64_t fl = (M > kb) ? (M - kb + 3) / 4 : 0;
-        float2 rot[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rot[e] = bf.seed[e];
-        float lg[G][NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const bool valid = kb + 4 * it < total;
-            const u32x4 w = bf.k[it];
-            float y[8];
-            if (it >= fl) {                      // local key: rotate
-                if (it > fl) {                   // advance cos/sin by 4 positions
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float2 r = rot[e];
-                        rot[e] = make_float2(r.x * step[e].x - r.y * step[e].y, r.y * step[e].x + r.x * step[e].y);
-                    }
-                }
-                const u32x4 pw = {ror8_16(w[0]), ror8_16(w[1]), ror8_16(w[2]), ror8_16(w[3])};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-                    const float px = (e & 1) ? bf16_hi(pw[e / 2]) : bf16_lo(pw[e / 2]);
-                    y[e] = x * rot[e].x + sgn * px * rot[e].y;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d += y[e] * q[hh][e];
-                d = group_sum<16>(d);
-                lg[hh][it] = valid ? d : -INFINITY;
-            }
-        }
-        // online softmax per head over the wave's 16 keys (the max is the same in
-        // every lane); the probabilities replace the logits in place
-        float (&pr)[G][NIT] = lg;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float mx = fmaxf(fmaxf(lg[hh][0], lg[hh][1]), fmaxf(lg[hh][2], lg[hh][3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            if (mx > m[hh] + kDecodeLazy) {
-                const float corr = (m[hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[hh] - mx);
-                l[hh] *= corr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[hh][e] *= corr;
-                m[hh] = mx;
-            }
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                pr[hh][it] = (lg[hh][it] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lg[hh][it] - m[hh]);   // same element
-                l[hh] += pr[hh][it];
-            }
-        }
-        // P.V in the same layout
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const u32x4 w = vbuf[it];
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[hh][e] += pr[hh][it] * v[e];
-        }
-        if (next) load_v(cidx + 1);
-    };
-
-    // ---- chunks cb .. ce-1, the next one's loads in flight behind this one
-    Buf A, Bb;
-    load_k(cb, A);
-    load_v(cb);
-    for (int64_t cc = cb; cc < ce; cc += 2) {
-        if (cc + 1 < ce) load_k(cc + 1, Bb);
-        process(cc, A, cc + 1 < ce);
-        if (cc + 1 >= ce) break;
-        if (cc + 2 < ce) load_k(cc + 2, A);
-        process(cc + 1, Bb, cc + 2 < ce);
-    }
-
-    // ---- merge the four key slots of each wave (same m), then the waves
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        l[hh] += __shfl_xor(l[hh], 16);
-        l[hh] += __shfl_xor(l[hh], 32);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = o[hh][e];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            o[hh][e] = v;
-        }
-    }
-    if (slot == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[wave][hh][c * 8 + e] = o[hh][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int hh = idx / D, dd = idx % D;
-        const float mw = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = (s_m[w][hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][hh] - mw);
-            acc += f * red[w][hh][dd];
-        }
-        part_o[((hrow + hh) * P + p) * D + dd] = acc;
-    }
-    if (tid < G) {
-        const float mw = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
-        float lsum = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            lsum += (s_m[w][tid] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][tid] - mw) * s_l[w][tid];
-        // the combine takes m in natural-log units
-        part_ml[(hrow + tid) * P + p] = make_float2(mw == -INFINITY ? -INFINITY : mw * kLn2, lsum);
-    }
-}
-
 // Merges the P partial (m, l, o) of one output row: the partials' weights
 // exp(m_p - m) and the weighted row sums are computed in parallel (weights
 // kept in LDS), then each thread sums its dimension over the partials with
@@ -554,12 +285,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     if (lse != nullptr && dd == 0) lse[row] = m + logf(l);
 }
 
-// Chunks per workgroup of attn_decode_kernel: about four workgroups per CU,
-// counted from the largest key count a query may have, each taking as many
-// chunks as that allows (at most 16), so its set-up and merge are spread over
-// several chunks.  (Measured on the 32-query batch: 4 per CU 108.6 us, 8 per
-// CU 113.9 us, 16 per CU 124.3 us; the kernel is bound by its per-key vector
-// work, so more workgroups only add set-up.)
+// Chunks per workgroup of attn_decode_mfma_kernel (128 keys each): enough
+// for one workgroup per resident slot (two per CU) over the largest key count
+// a query may have, so each workgroup streams for long and its set-up and
+// merge are spread over many chunks.  (Measured on 32 decode queries with
+// 1,000-2,048 memory rows and 2,048 local keys: 105 us at two workgroups per
+// CU, 113 us at four, 124 us at eight.)
+constexpr int kDecodeWgsPerCu = 2;
+
 struct DecodePlan {
     int nc, P;
 };
@@ -567,15 +300,14 @@ struct DecodePlan {
 DecodePlan decode_plan(int64_t B, int Tq, int Hkv, int64_t max_rows, int L, int num_cus) {
     const int64_t chunks = ceil_div(max_rows + L, int64_t(kDecodeChunk));
     const int64_t total = B * Tq * Hkv * chunks;
-    int64_t nc = total / (int64_t(num_cus) * 4);
-    nc = nc < 1 ? 1 : (nc > 16 ? 16 : nc);
-    if (nc > chunks) nc = chunks;
+    int64_t nc = ceil_div(total, int64_t(num_cus) * kDecodeWgsPerCu);
+    nc = nc < 1 ? 1 : (nc > chunks ? chunks : nc);
     return DecodePlan{int(nc), int(ceil_div(chunks, nc))};
 }
 
 bool decode_applicable(msa_dtype dt, int D, int Hq, int Hkv, int64_t max_rows, int L) {
     const int G = Hq / Hkv;
-    return dt == MSA_BF16 && D == 128 && (G == 1 || G == 2 || G == 4) &&
+    return dt == MSA_BF16 && D == 128 && (G == 1 || G == 2 || G == 4 || G == 8) &&
            max_rows + L <= int64_t(kDecodeChunk) * kMaxParts;     // at most kMaxParts partials per row
 }
 
@@ -602,27 +334,12 @@ hipError_t launch_split_g(const AttnArgs& a, float* part_o, float2* part_ml, int
     return hipGetLastError();
 }
 
-template <int G>
-hipError_t launch_decode_g(const AttnArgs& a, float* part_o, float2* part_ml, DecodePlan pl, hipStream_t st) {
-    hipLaunchKernelGGL((attn_decode_kernel<G>), dim3(unsigned(pl.P), unsigned(a.Hkv), unsigned(a.B * a.Tq)),
-                       dim3(256), 0, st, static_cast<const bf16_t*>(a.Q), a.Tq, a.Hq, a.Hkv,
-                       static_cast<const bf16_t*>(a.KVmem), a.mem_off, a.mem_rows_cap, a.max_rows,
-                       static_cast<const bf16_t*>(a.K_local), static_cast<const bf16_t*>(a.V_local), a.L,
-                       a.q_offset, a.scale * kLog2e, a.rope_cs, a.max_pos, pl.P, pl.nc, part_o, part_ml);
-    hipError_t err = hipGetLastError();
+hipError_t launch_decode(const AttnArgs& a, float* part_o, float2* part_ml, DecodePlan pl, hipStream_t st) {
+    hipError_t err = launch_decode_mfma(a, part_o, part_ml, pl.P, pl.nc, st);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
                        part_o, part_ml, pl.P, static_cast<bf16_t*>(a.O), a.lse);
     return hipGetLastError();
-}
-
-hipError_t launch_decode(const AttnArgs& a, float* part_o, float2* part_ml, DecodePlan pl, hipStream_t st) {
-    switch (a.Hq / a.Hkv) {
-        case 1: return launch_decode_g<1>(a, part_o, part_ml, pl, st);
-        case 2: return launch_decode_g<2>(a, part_o, part_ml, pl, st);
-        case 4: return launch_decode_g<4>(a, part_o, part_ml, pl, st);
-        default: return hipErrorNotSupported;
-    }
 }
 
 template <typename T, int D>

@@ -412,6 +412,10 @@ ATTN_CASES = [
     ("bf16", 128, 64, 8, 2, 1, 700, [90, 200], 16),   # G = 8 decode
     ("bf16", 128, 32, 8, 4, 1, 8192, [500, 0, 1000, 37], 16),  # several 64-key chunks per workgroup
     ("bf16", 128, 32, 8, 2, 1, 1, [0, 5], 16),        # one local key; one query sees only it
+    ("bf16", 128, 8, 8, 2, 1, 400, [37, 130], 16),    # decode, G = 1
+    ("bf16", 128, 16, 8, 3, 2, 333, [64, 95, 1], 16), # G = 2, two tokens, blocks across the memory end
+    ("bf16", 128, 32, 8, 2, 63, 700, [300, 129], 16), # 63 tokens: the longest query on the decode kernel
+    ("bf16", 128, 64, 8, 3, 3, 2000, [1000, 31, 0], 16),  # G = 8, several chunks per workgroup
     ("f32", 64, 4, 2, 2, 1, 1, [0, 3], 4),            # the same on the generic kernel
 ]
 
@@ -455,6 +459,38 @@ def test_sparse_attn_is_deterministic(torch_mod, msa, ctx128):
         msa.msa_sparse_attn(ctx128, Q, KV, mo, 300, Kl, Vl, 16, W.scale_of(128), O, ws)
         outs.append(W.host_bits(O))
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_sparse_attn_running_max_rises_every_block(torch_mod, msa, ctx128):
+    """Memory keys whose scores grow by far more than the lazy-rescale margin
+    from one 32-key block to the next (K row r of KV head g is 0.5 r times the
+    unit direction of query head g G, rotated at the query's position), so the
+    running max of every head is raised, and the output accumulated so far
+    rescaled, block after block."""
+    torch = torch_mod
+    Hq, Hkv, d, L, qoff, rows = 32, 8, 128, 40, 16, 600
+    G = Hq // Hkv
+    Q = W.draw(83, 1, (1, 1, Hq, d), "bf16")
+    q = W.widen(Q, "bf16")[0, 0]
+    rq = oracle.rope(q, np.full(Hq, qoff + L - 1), ctx128.rope_theta)
+    unit = rq / np.linalg.norm(rq, axis=-1, keepdims=True)
+    kv = np.empty((rows, 2, Hkv, d))
+    kv[:, 0] = 0.5 * np.arange(rows, dtype=np.float64)[:, None, None] * unit[::G][None]
+    kv[:, 1] = W.widen(W.draw(83, 2, (rows, Hkv, d), "bf16"), "bf16")
+    KV = oracle.f64_to_bf16_bits(kv)
+    Kl = W.draw(83, 3, (1, L, Hkv, d), "bf16")
+    Vl = W.draw(83, 4, (1, L, Hkv, d), "bf16")
+    mem_off = np.array([0, rows], dtype=np.int64)
+    O = torch.full((1, 1, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, 1, Hq, Hkv, rows, L))
+    msa.msa_sparse_attn(ctx128, W.dev(Q, "bf16"), W.dev(KV, "bf16"), torch.from_numpy(mem_off).cuda(), rows,
+                        W.dev(Kl, "bf16"), W.dev(Vl, "bf16"), qoff, W.scale_of(d), O, ws)
+    torch.cuda.synchronize()
+    kvw = W.widen(KV, "bf16")
+    ref = oracle.sparse_attn(q[None, None], kvw[:, 0], kvw[:, 1], mem_off, W.widen(Kl, "bf16"),
+                             W.widen(Vl, "bf16"), qoff, W.scale_of(d), ctx128.rope_theta)
+    got = W.widen(W.host_bits(O), "bf16")
+    assert np.max(np.abs(got - ref)) <= 2e-2
 
 
 # ---------------------------------------------------------------- validation with a context
