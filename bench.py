@@ -821,7 +821,7 @@ def run_reuse100m(args, torch, msa, msa_synth, device_fill, W):
         "planted_recovered_all_layers": recovered,
         "roofline": {"bound": "hbm", "achieved": round(tok_bytes / per_tok / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(roof / per_tok, 4), "traffic": None,
-                     "kernel": "one generated token (18 x attn_decode_kernel + attn_combine)",
+                     "kernel": "one generated token (18 x attn_decode_mfma_kernel + attn_combine)",
                      "bytes_per_launch": tok_bytes},
     }
 
