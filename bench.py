@@ -84,7 +84,7 @@ def parse():
                    help="chunk rows per layer in the oracle sample (0: the whole layer)")
     p.add_argument("--cpu-sample-layers", type=int, default=4, help="routing layers in the oracle sample")
     p.add_argument("--workload", choices=["decode100m", "chunk100m", "reuse100m", "prefill8k", "batch32", "encode10m",
-                                          "train8k", "routebwd1m", "hbmcopy"],
+                                          "train8k", "routebwd1m", "hbmcopy", "probes"],
                    default="decode100m",
                    help="decode100m: the routed decode step on the 100M-token bank (default, the metric); "
                         "prefill8k / batch32: extra measurements on the 10M-token bank; "
@@ -92,7 +92,8 @@ def parse():
                         "train8k: forward (saving log-sum-exp) + backward of the prefill-shaped attention; "
                         "routebwd1m: routing forward + document-score backward on the 1M-token memory; "
                         "hbmcopy: a plain 4 GiB device-to-device copy, the known-size kernel that "
-                        "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE)")
+                        "calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE); "
+                        "probes: measured streaming-read, device-copy and pinned host <-> device bandwidth")
     p.add_argument("--gen-tokens", type=int, default=64, help="reuse100m: tokens generated after assembly")
     p.add_argument("--gather", choices=["batch", "loop"], default="batch",
                    help="msa_gather submission: one hipMemcpyBatchAsync, or one hipMemcpyAsync per copy")
@@ -726,6 +727,50 @@ def run_hbmcopy(args, torch, msa, msa_synth, device_fill, W):
             "copy_checked": same}
 
 
+def run_probes(args, torch, msa, msa_synth, device_fill, W):
+    """Measured ceilings beside the spec figures (8 TB/s HBM, about 64 GB/s
+    PCIe per direction): a streaming read of a 4 GiB device tensor (a bf16
+    matrix-vector product over it, [2^20 x 2048] times a vector, which reads the
+    matrix once: the best reader among torch's reductions and BLAS calls here),
+    a 4 GiB device-to-device copy, and 1 GiB copies between pinned host memory
+    and the device in each direction."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps / 1e3
+    n = 2 << 30                                  # bf16 elements: 4 GiB
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    device_fill.fill_counter_bf16(x, args.seed, 1, 0)
+    y = torch.empty_like(x)
+    A = x.view(1 << 20, 2048)
+    vec = torch.ones(2048, dtype=torch.bfloat16, device="cuda")
+    read_s = timed(lambda: torch.mv(A, vec), 10)
+    copy_s = timed(lambda: y.copy_(x), 10)
+    same = bool(torch.equal(x[:1 << 20], y[:1 << 20]))
+    del y
+    m = 1 << 30                                  # bytes: 1 GiB each way
+    host = torch.empty(m, dtype=torch.uint8, pin_memory=True)
+    host.copy_(x.view(torch.uint8)[:m].cpu())
+    dev = torch.empty(m, dtype=torch.uint8, device="cuda")
+    h2d_s = timed(lambda: dev.copy_(host, non_blocking=True), 5)
+    d2h_s = timed(lambda: host.copy_(dev, non_blocking=True), 5)
+    same = same and bool(torch.equal(dev[:1 << 20], x.view(torch.uint8)[:1 << 20]))
+    return {"metric": "bandwidth probes (streaming read, device copy, pinned host <-> device)",
+            "value": round(2 * n / read_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 1,
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "4 GiB device tensor read and copied, 1 GiB pinned host copies"},
+            "read_GBps": round(2 * n / read_s / 1e9, 1), "read_frac_of_8TBps": round(2 * n / read_s / 8e12, 4),
+            "device_copy_GBps": round(4 * n / copy_s / 1e9, 1),
+            "h2d_GBps": round(m / h2d_s / 1e9, 1), "d2h_GBps": round(m / d2h_s / 1e9, 1),
+            "copy_checked": same}
+
+
 def run_reuse100m(args, torch, msa, msa_synth, device_fill, W):
     """Route once, then decode many tokens (the pages' pipeline: documents are
     selected when the context is assembled, then generation reuses them).
@@ -845,7 +890,7 @@ def main():
     if args.workload not in ("decode100m", "chunk100m"):
         fn = {"prefill8k": run_prefill8k, "batch32": run_batch32, "encode10m": run_encode10m,
               "hbmcopy": run_hbmcopy, "reuse100m": run_reuse100m, "train8k": run_train8k,
-              "routebwd1m": run_routebwd1m}[args.workload]
+              "routebwd1m": run_routebwd1m, "probes": run_probes}[args.workload]
         out = fn(args, torch, msa, msa_synth, device_fill, W)
         print(json.dumps(out), flush=True)
         ok = out.get("planted_recovered", out.get("planted_recovered_all", out.get(
