@@ -76,6 +76,20 @@ def test_ctx_create_rejects_unsupported_head_dim_before_touching_hip():
     assert e.value.status == msa.MSA_ERR_INVALID_ARG
 
 
+def test_hip_runtime_failure_maps_to_msa_err_hip():
+    """With no GPU visible the HIP runtime itself fails (hipGetDeviceCount):
+    the call returns MSA_ERR_HIP with the failing call and HIP's error named,
+    and no exception crosses the ABI.  On a machine with a GPU the same
+    context is created; the test needs the GPU-less case."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the HIP runtime does not fail here")
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_ctx_create(0, 128, 1e6, 1024)
+    assert e.value.status == msa.MSA_ERR_HIP
+    assert "hipGetDeviceCount" in str(e.value)
+
+
 def test_calls_without_context_fail_cleanly():
     L = msa.lib()
     assert L.msa_encode_pool(None, 1, *([None] * 5), 1, 1, 1, 1, 1, None, None, None) == 1
