@@ -445,6 +445,47 @@ def test_sparse_attn_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B,
     assert np.max(np.abs(got - ref)) <= tol
 
 
+def _random_attn_cases(n, seed):
+    """Seeded shapes for the decode / short-query kernel: G in {1, 2, 4, 8},
+    1-5 query tokens, ragged memory rows (some queries without any), local
+    lengths from Tq to 700 and offsets k, so blocks start on every alignment
+    against the memory/local boundary and the end."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        G = (1, 2, 4, 8)[k % 4]
+        Hkv = int(rng.choice([1, 2, 8]))
+        B = int(rng.integers(1, 5))
+        Tq = int(rng.integers(1, 6))
+        L = int(rng.integers(Tq, 701))
+        rows = [int(r) if rng.random() > 0.2 else 0 for r in rng.integers(0, 500, size=B)]
+        qoff = int(rng.integers(0, 64))
+        cases.append((G * Hkv, Hkv, B, Tq, L, rows, qoff))
+    return cases
+
+
+@pytest.mark.parametrize("Hq,Hkv,B,Tq,L,rows,qoff", _random_attn_cases(12, 2024))
+def test_sparse_attn_random_decode_shapes(torch_mod, msa, ctx128, Hq, Hkv, B, Tq, L, rows, qoff):
+    torch = torch_mod
+    d = 128
+    mem_off = msa_synth.prefix_offsets(rows)
+    M = int(mem_off[-1])
+    Q = W.draw(91, 1, (B, Tq, Hq, d), "bf16")
+    KV = W.draw(91, 2, (max(M, 1), 2, Hkv, d), "bf16")
+    Kl = W.draw(91, 3, (B, L, Hkv, d), "bf16")
+    Vl = W.draw(91, 4, (B, L, Hkv, d), "bf16")
+    O = torch.full((B, Tq, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = msa.workspace(msa.msa_sparse_attn_workspace_size(1, B, Tq, Hq, Hkv, max(max(rows), 1), L))
+    msa.msa_sparse_attn(ctx128, W.dev(Q, "bf16"), W.dev(KV, "bf16"), torch.from_numpy(mem_off).cuda(),
+                        max(max(rows), 1), W.dev(Kl, "bf16"), W.dev(Vl, "bf16"), qoff, W.scale_of(d), O, ws)
+    torch.cuda.synchronize()
+    kv = W.widen(KV, "bf16")
+    ref = oracle.sparse_attn(W.widen(Q, "bf16"), kv[:, 0], kv[:, 1], mem_off, W.widen(Kl, "bf16"),
+                             W.widen(Vl, "bf16"), qoff, W.scale_of(d), ctx128.rope_theta)
+    got = W.widen(W.host_bits(O), "bf16")
+    assert np.max(np.abs(got - ref)) <= 2e-2
+
+
 def test_sparse_attn_is_deterministic(torch_mod, msa, ctx128):
     torch = torch_mod
     Q = W.dev_bf16(msa_synth.normal_bf16(81, 1, (1, 1, 32, 128)))
