@@ -188,6 +188,7 @@ ROUTE_CASES = [
     ("bf16", 128, 32, 8, 1, 256, 250, 8, 16),    # matrix cores: 256-token query, token max
     ("bf16", 128, 16, 4, 2, 128, 100, 12, 5),    # matrix cores: 4 KV heads, 2 queries
     ("bf16", 128, 16, 16, 6, 1, 90, 4, 7),       # matrix cores: 16 KV heads
+    ("bf16", 128, 16, 4, 2, 512, 300, 6, 12),    # one GEMM: two 512-token queries, 4 KV heads
 ]
 
 
