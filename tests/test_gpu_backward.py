@@ -118,11 +118,28 @@ BWD_CASES = [
 ]
 
 
+def _random_bwd_cases(n, seed):
+    """Seeded shapes: G cycling through 1, 2, 4 and 8, 1-2 queries of 1-150
+    tokens, ragged memory rows (some queries without any), local lengths up to
+    400 and offsets k, so query and key tiles end at every alignment."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        G = (1, 2, 4, 8)[k % 4]
+        Hkv = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        Tq = int(rng.integers(1, 151))
+        L = int(rng.integers(Tq, 401))
+        rows = [int(r) if rng.random() > 0.25 else 0 for r in rng.integers(0, 300, size=B)]
+        cases.append((G * Hkv, Hkv, B, Tq, L, rows, int(rng.integers(0, 41))))
+    return cases
+
+
 def _rel(got, ref):
     return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-@pytest.mark.parametrize("Hq,Hkv,B,Tq,L,rows,qoff", BWD_CASES)
+@pytest.mark.parametrize("Hq,Hkv,B,Tq,L,rows,qoff", BWD_CASES + _random_bwd_cases(8, 77))
 def test_sparse_attn_bwd_parity(torch_mod, msa, ctx128, Hq, Hkv, B, Tq, L, rows, qoff):
     torch = torch_mod
     d = 128
