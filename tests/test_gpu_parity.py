@@ -211,6 +211,41 @@ def test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B
         _check_valid_topk(ids[b], sc[b], D_ref[b], tol)
 
 
+def _random_route_cases(n, seed):
+    """Seeded shapes cycling through the four chunk-score paths: the streaming
+    scan (B*Tq <= 4), the matrix cores on a decode batch, 128- and 256-token
+    query blocks (token tiles, the one-GEMM path), and query blocks of any
+    length or head dim (generic scan, fp32 among them); KV heads 1-16, group
+    sizes 1-8, ragged documents of 1-19 chunks, k up to 64."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = i % 4
+        Hkv = int(rng.choice([1, 2, 4, 8, 16]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        dtype, d = "bf16", 128
+        if kind == 0:
+            B, Tq = int(rng.integers(1, 5)), 1
+        elif kind == 1:
+            B, Tq = int(rng.integers(5, 41)), 1
+        elif kind == 2:
+            B, Tq = int(rng.integers(1, 3)), int(rng.choice([128, 256]))
+        else:
+            B, Tq = int(rng.integers(1, 4)), int(rng.integers(2, 20))
+            dtype = str(rng.choice(["bf16", "f32"]))
+            d = int(rng.choice([64, 128]))
+        n_docs = int(rng.integers(1, 400))
+        k = int(rng.integers(1, min(n_docs, 64) + 1))
+        cases.append((dtype, d, G * Hkv, Hkv, B, Tq, n_docs, int(rng.integers(1, 20)), k))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,n_docs,maxc,k", _random_route_cases(16, 502))
+def test_route_parity_random_shapes(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, n_docs, maxc,
+                                    k):
+    test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, n_docs, maxc, k)
+
+
 @pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16), (32, 1), (1, 256)])
 def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
     Hq, Hkv, d, k = 32, 8, 128, 16
