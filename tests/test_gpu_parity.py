@@ -133,6 +133,38 @@ def test_encode_pool_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, c, len
             assert W.rel_row_err(got, ref) <= 2 ** -8 + 1e-5
 
 
+def _random_encode_cases(n, seed):
+    """Seeded layouts: either dtype and head dim, 1-16 KV heads, chunk lengths
+    1-64, and 1-40 documents whose lengths mix single tokens, lengths one off
+    a chunk multiple and long documents (below the RoPE table of each head
+    dim: 4096 positions for d = 64, 16384 for d = 128)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ("bf16", "f32")[i % 2]
+        d = (128, 128, 64)[i % 3]
+        Hkv = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        c = int(rng.choice([1, int(rng.integers(2, 64)), 64]))
+        lens = []
+        for _ in range(int(rng.integers(1, 41))):
+            kind = rng.integers(0, 4)
+            if kind == 0:
+                lens.append(1)
+            elif kind == 1:
+                lens.append(max(1, c * int(rng.integers(1, 9)) + int(rng.choice([-1, 0, 1]))))
+            elif kind == 2:
+                lens.append(int(rng.integers(2, 300)))
+            else:
+                lens.append(int(rng.integers(300, 4000 if d == 64 else 9000)))
+        cases.append((dtype, d, Hkv, c, lens))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,d,Hkv,c,lens", _random_encode_cases(10, 404))
+def test_encode_pool_random_layouts(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, c, lens):
+    test_encode_pool_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, c, lens)
+
+
 # ---------------------------------------------------------------- stage 2a
 
 def _bank(dtype, N, Hkv, d, seed):
