@@ -669,6 +669,60 @@ def test_gather_device_matches_oracle_and_host_gather(torch_mod, msa, ctx128):
         assert np.array_equal(got[mo_np[b]:mo_np[b + 1]], ref)
 
 
+def _random_gather_cases(n, seed):
+    """Seeded layouts: rows of 256 B to 8 KiB (K and V of 1-8 heads, d 64 or
+    128, bf16 or fp32 elements; the copy is byte-level), 1-200 documents of
+    1-20 chunk rows, 1-4 queries, k up to 64, ids in random order with a run
+    of consecutive ids in some rows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        row_elems = 2 * int(rng.choice([1, 2, 4, 8])) * int(rng.choice([64, 128])) * int(rng.choice([1, 2]))
+        n_docs = int(rng.integers(1, 201))
+        B = int(rng.integers(1, 5))
+        k = int(rng.integers(1, min(n_docs, 64) + 1))
+        cases.append((row_elems, n_docs, int(rng.integers(1, 21)), B, k, 900 + i))
+    return cases
+
+
+@pytest.mark.parametrize("row_elems,n_docs,maxc,B,k,seed", _random_gather_cases(10, 63))
+def test_gather_random_layouts(torch_mod, msa, ctx128, row_elems, n_docs, maxc, B, k, seed):
+    torch = torch_mod
+    rng = np.random.default_rng(seed)
+    coff = msa_synth.prefix_offsets(rng.integers(1, maxc + 1, size=n_docs))
+    N = int(coff[-1])
+    bank = msa_synth.counter_bf16(seed, 8, 0, N * row_elems).reshape(N, row_elems)
+    host = torch.empty((N, row_elems), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = np.stack([rng.permutation(n_docs)[:k] for _ in range(B)]).astype(np.int32)
+    for b in range(0, B, 2):                       # a run of consecutive documents
+        if k >= 3 and n_docs >= k:
+            start = int(rng.integers(0, n_docs - k + 1))
+            ids[b] = np.arange(start, start + k, dtype=np.int32)[rng.permutation(k)]
+    cap = int(sum(np.diff(coff)[ids[b]].sum() for b in range(B)))
+    row_bytes = row_elems * 2
+    dst = torch.zeros((cap, row_elems), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    msa.msa_gather_device(ctx128, host, row_bytes, N, torch.from_numpy(coff).cuda(),
+                          torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
+    dst2 = torch.zeros_like(dst)
+    mo_h = torch.zeros(B + 1, dtype=torch.int64, pin_memory=True)
+    side = torch.cuda.Stream()
+    msa.msa_gather(host, row_bytes, N, coff, ids, k, dst2, cap, mo_h, side=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    mo_np = mo.cpu().numpy()
+    assert np.array_equal(mo_np, mo_h.numpy())
+    got, got2 = W.host_bits(dst), W.host_bits(dst2)
+    for b in range(B):
+        ref, m = oracle.gather_rows(bank, coff, ids[b])
+        assert mo_np[b + 1] - mo_np[b] == m
+        assert np.array_equal(got[mo_np[b]:mo_np[b + 1]], ref)
+        assert np.array_equal(got2[mo_np[b]:mo_np[b + 1]], ref)
+    assert mo_np[B] == cap
+
+
 def test_gather_device_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, ctx128):
     torch = torch_mod
     coff = np.array([0, 3, 5, 9, 10], dtype=np.int64)
