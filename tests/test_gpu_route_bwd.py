@@ -69,7 +69,26 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,lens,zero_docs", CASES)
+def _random_cases(n, seed):
+    """Seeded shapes: either dtype and head dim, KV heads 1-16 with group
+    sizes 1-8, 1-3 queries of 1-16 tokens, 1-60 documents of 1-20 chunks, and
+    a few documents whose score gradient is zero."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ("bf16", "f32")[i % 2]
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8, 16]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        n_docs = int(rng.integers(1, 61))
+        lens = [int(x) for x in rng.integers(1, 21, size=n_docs)]
+        zero = sorted(int(x) for x in rng.choice(n_docs, size=int(rng.integers(0, min(3, n_docs) + 1)),
+                                                   replace=False))
+        cases.append((dtype, d, G * Hkv, Hkv, int(rng.integers(1, 4)), int(rng.integers(1, 17)), lens, zero))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv,B,Tq,lens,zero_docs", CASES + _random_cases(8, 31))
 def test_route_bwd_parity(torch_mod, msa, ctxs, dtype, d, Hq, Hkv, B, Tq, lens, zero_docs):
     torch = torch_mod
     off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
