@@ -7,6 +7,11 @@ in host memory and are fetched on demand.
 Reading taken: the selected documents' rows are concatenated in ascending doc
 id order (attention is invariant to the order of memory rows, so one canonical
 order is fixed for comparisons).  Pure indexing; no arithmetic.
+
+Parity status: pinned (tests/test_oracle_gather.py): hand-written layouts whose
+rows name their own index (ids out of order, adjacent documents, one-chunk
+documents, the first and last document, no document) against the row lists
+written out by hand.
 """
 
 import numpy as np

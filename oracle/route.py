@@ -36,14 +36,6 @@ import numpy as np
 EPS = 1e-8
 
 
-def cosine(q, k, eps=EPS):
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    nq = np.maximum(np.sqrt(np.sum(q * q, axis=-1)), eps)
-    nk = np.maximum(np.sqrt(np.sum(k * k, axis=-1)), eps)
-    return np.sum(q * k, axis=-1) / (nq * nk)
-
-
 def _unit(x, eps=EPS):
     n = np.maximum(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)), eps)
     return x / n

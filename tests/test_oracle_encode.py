@@ -113,3 +113,8 @@ def test_chunk_mean_equals_pooled_v():
     _, Vb, Rb = oracle.encode_pool(K, V, Kr, off, 64, 1e4)
     assert np.array_equal(oracle.chunk_mean(V, off, 64), Vb)
     assert np.array_equal(oracle.chunk_mean(Kr, off, 64), Rb)
+
+
+def test_chunk_counts_are_ceilings():
+    assert oracle.chunk_counts([1, 16, 17, 32, 33, 64], 16).tolist() == [1, 1, 2, 2, 3, 4]
+    assert oracle.chunk_counts([5, 1, 7], 1).tolist() == [5, 1, 7]

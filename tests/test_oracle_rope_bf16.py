@@ -88,3 +88,18 @@ def test_rope_preserves_norm_and_relative_positions():
         b = oracle.rope(q, m + delta, 1e6) @ oracle.rope(k, n + delta, 1e6)
         assert abs(a - b) < 1e-10
         assert abs(np.linalg.norm(oracle.rope(q, m, 1e6)) - np.linalg.norm(q)) < 1e-12
+
+
+def test_f32_widening_is_exact():
+    # values with all 24 significand bits in use, and extremes of the range
+    x = np.array([1 + 2.0 ** -23, -(2.0 ** 127) * (2 - 2.0 ** -23), 2.0 ** -149, 0.1], dtype=np.float32)
+    w = oracle.f32_to_f64(x)
+    assert w.dtype == np.float64
+    assert w[0] == 1 + 2.0 ** -23 and w[1] == -(2.0 ** 127) * (2 - 2.0 ** -23) and w[2] == 2.0 ** -149
+    assert w[3] == 0.100000001490116119384765625          # float32(0.1), not 0.1
+
+
+def test_rope_angles_closed_form():
+    # d = 4, theta = 100: inverse frequencies 1 and 1/10
+    ang = oracle.rope_angles(np.array([0, 3, 7]), 4, 100.0)
+    np.testing.assert_allclose(ang, [[0.0, 0.0], [3.0, 0.3], [7.0, 0.7]], rtol=1e-15, atol=0)
