@@ -652,13 +652,13 @@ def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
     [10M, 8, 128] bf16 (61.4 GB) pooled into KV̄ [N, 2, 8, 128] and K̄r [N, 8, 128]
     (0.96 GB) with document-wise RoPE; every launch times the whole layer."""
     lens, tok, (K, V, Kr) = encode_10m_inputs(args.seed, torch, msa_synth, device_fill)
-    coff = msa.msa_chunk_offsets(tok, CHUNK)
+    coff, max_len = msa.msa_chunk_offsets(tok, CHUNK, with_max_len=True)
     T, N = int(tok[-1]), int(coff[-1])
     KVbar = torch.empty((N, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
     Krbar = torch.empty((N, Hkv, D), dtype=torch.bfloat16, device="cuda")
     tok_d, coff_d = torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda()
     ctx = msa.msa_ctx_create(0, D, 1e6, 16384)
-    enc = lambda: msa.msa_encode_pool(ctx, K, V, Kr, tok_d, coff_d, KVbar, Krbar, CHUNK)
+    enc = lambda: msa.msa_encode_pool(ctx, K, V, Kr, tok_d, coff_d, KVbar, Krbar, CHUNK, max_len)
     for _ in range(args.warmup):
         enc()
     torch.cuda.synchronize()
@@ -675,7 +675,7 @@ def run_encode10m(args, torch, msa, msa_synth, device_fill, W):
     finite = bool(torch.isfinite(KVbar).all()) and bool(torch.isfinite(Krbar).all())
     # the backward of the pooling (msa_encode_pool_bwd): the pooled rows taken as
     # their own gradients, sent back to every token (written over K, V, Kr)
-    bwd = lambda: msa.msa_encode_pool_bwd(ctx, KVbar, Krbar, tok_d, coff_d, K, V, Kr, CHUNK)
+    bwd = lambda: msa.msa_encode_pool_bwd(ctx, KVbar, Krbar, tok_d, coff_d, K, V, Kr, CHUNK, max_len)
     for _ in range(args.warmup):
         bwd()
     torch.cuda.synchronize()

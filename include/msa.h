@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 #define MSA_MAX_TOPK 64
 
 typedef enum msa_status {
@@ -103,9 +103,12 @@ msa_status msa_ctx_destroy(msa_ctx* ctx);
  *   doc_tok_off      host int64[n_docs+1], doc_tok_off[0] == 0, strictly
  *                    increasing (every document has >= 1 token).
  *   doc_chunk_off    host int64[n_docs+1] output.
+ *   max_doc_len      host output or NULL: the longest document's length in
+ *                    tokens (0 when n_docs == 0), the value msa_encode_pool
+ *                    and msa_encode_pool_bwd take as max_doc_len.
  */
 msa_status msa_chunk_offsets(const int64_t* doc_tok_off, int64_t n_docs, int chunk_len,
-                             int64_t* doc_chunk_off);
+                             int64_t* doc_chunk_off, int64_t* max_doc_len);
 
 /*
  * msa_encode_pool -- stage 1 (offline): document-wise RoPE + chunk mean.
@@ -125,15 +128,21 @@ msa_status msa_chunk_offsets(const int64_t* doc_tok_off, int64_t n_docs, int chu
  *   KVbar          device [N][2][Hkv][d] of dt: row n holds K̄ then V̄, so a
  *                  document's pooled content is one contiguous span.
  *   Krbar          device [N][Hkv][d] of dt.
+ *   max_doc_len    host: the longest document's length in tokens (from
+ *                  msa_chunk_offsets).  Document-local positions run up to
+ *                  max_doc_len - 1, so max_doc_len > the context's max_pos
+ *                  is MSA_ERR_INVALID_ARG, nothing enqueued.
  * Offsets are trusted to be consistent (use msa_chunk_offsets); if they are
  * not, outputs are unspecified but every access stays inside [0, T) rows
- * and [0, N) chunk rows.  Document-local positions must be < max_pos.
+ * and [0, N) chunk rows.  A document that the device offsets make longer
+ * than max_doc_len (a wrong max_doc_len) gets NaN in all of its pooled
+ * rows: positions are never clamped or read past the RoPE table.
  */
 msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt,
                            const void* K, const void* V, const void* Kr,
                            const int64_t* doc_tok_off, const int64_t* doc_chunk_off,
                            int64_t n_docs, int64_t T, int64_t N, int Hkv, int chunk_len,
-                           void* KVbar, void* Krbar, hipStream_t stream);
+                           int64_t max_doc_len, void* KVbar, void* Krbar, hipStream_t stream);
 
 /*
  * msa_encode_pool_bwd -- gradients of msa_encode_pool with respect to the
@@ -148,8 +157,9 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt,
  *   dKVbar         device [N][2][Hkv][d] of dt (dK̄ then dV̄ per row, the
  *                  layout of msa_encode_pool's KVbar).
  *   dKrbar         device [N][Hkv][d] of dt.
- *   doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv, chunk_len  as for
- *                  msa_encode_pool.
+ *   doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv, chunk_len, max_doc_len
+ *                  as for msa_encode_pool (the same checks; token rows of a
+ *                  document longer than max_doc_len get NaN).
  *   dK, dV, dKr    device [T][Hkv][d] of dt (written for every token of a
  *                  document; rows outside every document untouched).
  * fp32 arithmetic, one rounding to dt on store.
@@ -158,7 +168,7 @@ msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt,
                                const void* dKVbar, const void* dKrbar,
                                const int64_t* doc_tok_off, const int64_t* doc_chunk_off,
                                int64_t n_docs, int64_t T, int64_t N, int Hkv, int chunk_len,
-                               void* dK, void* dV, void* dKr, hipStream_t stream);
+                               int64_t max_doc_len, void* dK, void* dV, void* dKr, hipStream_t stream);
 
 /*
  * msa_route -- stage 2a (online): cosine routing + document top-k.

@@ -52,9 +52,9 @@ _SIGS = {
     "msa_status_string": (ctypes.c_char_p, [I32]),
     "msa_ctx_create": (I32, [I32, I32, F64, I32, ctypes.POINTER(P)]),
     "msa_ctx_destroy": (I32, [P]),
-    "msa_chunk_offsets": (I32, [P, I64, I32, P]),
-    "msa_encode_pool": (I32, [P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, P, P, P]),
-    "msa_encode_pool_bwd": (I32, [P, I32, P, P, P, P, I64, I64, I64, I32, I32, P, P, P, P]),
+    "msa_chunk_offsets": (I32, [P, I64, I32, P, P]),
+    "msa_encode_pool": (I32, [P, I32, P, P, P, P, P, I64, I64, I64, I32, I32, I64, P, P, P]),
+    "msa_encode_pool_bwd": (I32, [P, I32, P, P, P, P, I64, I64, I64, I32, I32, I64, P, P, P, P]),
     "msa_route_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I64, I32]),
     "msa_route": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, I32, P, P, P, P, P, SZ, P]),
     "msa_route_time_next": (I32, [P, P, P]),
@@ -171,35 +171,40 @@ def msa_ctx_destroy(ctx):
     ctx.close()
 
 
-def msa_chunk_offsets(doc_tok_off, chunk_len):
-    """Host helper: int64 numpy prefix sums of ceil(len / chunk_len)."""
+def msa_chunk_offsets(doc_tok_off, chunk_len, with_max_len=False):
+    """Host helper: int64 numpy prefix sums of ceil(len / chunk_len); with
+    with_max_len, also the longest document's length (msa_encode_pool's
+    max_doc_len)."""
     tok = np.ascontiguousarray(doc_tok_off, dtype=np.int64)
     out = np.empty_like(tok)
-    _check(lib().msa_chunk_offsets(_ptr(tok), len(tok) - 1, chunk_len, _ptr(out)))
-    return out
+    mx = ctypes.c_int64(0)
+    _check(lib().msa_chunk_offsets(_ptr(tok), len(tok) - 1, chunk_len, _ptr(out), ctypes.addressof(mx)))
+    return (out, mx.value) if with_max_len else out
 
 
 # ---------------------------------------------------------------- stage 1
 
-def msa_encode_pool(ctx, K, V, Kr, doc_tok_off, doc_chunk_off, KVbar, Krbar, chunk_len,
+def msa_encode_pool(ctx, K, V, Kr, doc_tok_off, doc_chunk_off, KVbar, Krbar, chunk_len, max_doc_len,
                     stream=None):
     """K, V, Kr [T, Hkv, d]; offsets int64 device tensors [n_docs+1];
-    KVbar [N, 2, Hkv, d], Krbar [N, Hkv, d] outputs."""
+    KVbar [N, 2, Hkv, d], Krbar [N, Hkv, d] outputs; max_doc_len the longest
+    document's token count (msa_chunk_offsets(..., with_max_len=True))."""
     T, Hkv, d = K.shape
     N = Krbar.shape[0]
     _check(lib().msa_encode_pool(ctx.handle, _dtype(K), _ptr(K), _ptr(V), _ptr(Kr), _ptr(doc_tok_off),
                                  _ptr(doc_chunk_off), doc_tok_off.numel() - 1, T, N, Hkv, chunk_len,
-                                 _ptr(KVbar), _ptr(Krbar), _stream(stream)))
+                                 int(max_doc_len), _ptr(KVbar), _ptr(Krbar), _stream(stream)))
 
 
-def msa_encode_pool_bwd(ctx, dKVbar, dKrbar, doc_tok_off, doc_chunk_off, dK, dV, dKr, chunk_len, stream=None):
+def msa_encode_pool_bwd(ctx, dKVbar, dKrbar, doc_tok_off, doc_chunk_off, dK, dV, dKr, chunk_len, max_doc_len,
+                        stream=None):
     """dKVbar [N, 2, Hkv, d], dKrbar [N, Hkv, d]; offsets int64 device [n_docs+1];
-    dK, dV, dKr [T, Hkv, d] outputs."""
+    dK, dV, dKr [T, Hkv, d] outputs; max_doc_len as for msa_encode_pool."""
     T, Hkv, d = dK.shape
     N = dKrbar.shape[0]
     _check(lib().msa_encode_pool_bwd(ctx.handle, _dtype(dK), _ptr(dKVbar), _ptr(dKrbar), _ptr(doc_tok_off),
                                      _ptr(doc_chunk_off), doc_tok_off.numel() - 1, T, N, Hkv, chunk_len,
-                                     _ptr(dK), _ptr(dV), _ptr(dKr), _stream(stream)))
+                                     int(max_doc_len), _ptr(dK), _ptr(dV), _ptr(dKr), _stream(stream)))
 
 
 # ---------------------------------------------------------------- stage 2

@@ -87,6 +87,20 @@ struct DeviceGuard {
     }
 };
 
+// Document-local positions run from 0 to max_doc_len - 1, and every one of
+// them must have a row in the context's RoPE table.
+msa_status check_doc_len(const char* fn, const msa_ctx* ctx, int64_t n_docs, int64_t T, int64_t max_doc_len) {
+    if (n_docs == 0) return MSA_OK;
+    if (max_doc_len < 1 || max_doc_len > T)
+        return fail(MSA_ERR_INVALID_ARG, "%s: max_doc_len %lld outside [1, T = %lld]", fn, (long long)max_doc_len,
+                    (long long)T);
+    if (max_doc_len > ctx->max_pos)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "%s: a document of %lld tokens needs RoPE positions up to %lld, but the context's "
+                    "max_pos is %d", fn, (long long)max_doc_len, (long long)(max_doc_len - 1), ctx->max_pos);
+    return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,7 +195,7 @@ msa_status msa_ctx_destroy(msa_ctx* ctx) {
 }
 
 msa_status msa_chunk_offsets(const int64_t* doc_tok_off, int64_t n_docs, int chunk_len,
-                             int64_t* doc_chunk_off) {
+                             int64_t* doc_chunk_off, int64_t* max_doc_len) {
     if (!doc_tok_off || !doc_chunk_off) return fail(MSA_ERR_INVALID_ARG, "msa_chunk_offsets: NULL pointer");
     if (n_docs < 0) return fail(MSA_ERR_INVALID_ARG, "msa_chunk_offsets: n_docs < 0");
     if (chunk_len < 1) return fail(MSA_ERR_INVALID_ARG, "msa_chunk_offsets: chunk_len < 1");
@@ -191,17 +205,20 @@ msa_status msa_chunk_offsets(const int64_t* doc_tok_off, int64_t n_docs, int chu
             return fail(MSA_ERR_INVALID_ARG, "msa_chunk_offsets: document %lld has no token",
                         (long long)d);
     doc_chunk_off[0] = 0;
+    int64_t longest = 0;
     for (int64_t d = 0; d < n_docs; ++d) {
         const int64_t len = doc_tok_off[d + 1] - doc_tok_off[d];
         doc_chunk_off[d + 1] = doc_chunk_off[d] + (len + chunk_len - 1) / chunk_len;
+        longest = std::max(longest, len);
     }
+    if (max_doc_len) *max_doc_len = longest;
     return ok();
 }
 
 msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt, const void* K, const void* V, const void* Kr,
                            const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs,
-                           int64_t T, int64_t N, int Hkv, int chunk_len, void* KVbar, void* Krbar,
-                           hipStream_t stream) {
+                           int64_t T, int64_t N, int Hkv, int chunk_len, int64_t max_doc_len, void* KVbar,
+                           void* Krbar, hipStream_t stream) {
     const char* fn = "msa_encode_pool";
     if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
     if (!dtype_ok(dt)) return fail(MSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dt));
@@ -214,6 +231,7 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt, const void* K, const void
     if (n_docs > N) return fail(MSA_ERR_INVALID_ARG, "%s: %lld documents but %lld chunk rows", fn,
                                 (long long)n_docs, (long long)N);
     if (N > T) return fail(MSA_ERR_INVALID_ARG, "%s: more chunk rows than tokens", fn);
+    if (msa_status s = check_doc_len(fn, ctx, n_docs, T, max_doc_len)) return s;
     if (n_docs > 0 && (!K || !V || !Kr || !doc_tok_off || !doc_chunk_off || !KVbar || !Krbar))
         return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (n_docs > 0 && (!aligned16(K) || !aligned16(V) || !aligned16(Kr) || !aligned16(KVbar) ||
@@ -222,15 +240,15 @@ msa_status msa_encode_pool(msa_ctx* ctx, msa_dtype dt, const void* K, const void
     DeviceGuard dg(ctx->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_encode_pool: hipSetDevice");
     hipError_t e = msa::launch_encode(ctx, dt, K, V, Kr, doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv,
-                                      chunk_len, KVbar, Krbar, stream);
+                                      chunk_len, max_doc_len, KVbar, Krbar, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_encode_pool: launch");
     return ok();
 }
 
 msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt, const void* dKVbar, const void* dKrbar,
                                const int64_t* doc_tok_off, const int64_t* doc_chunk_off, int64_t n_docs, int64_t T,
-                               int64_t N, int Hkv, int chunk_len, void* dK, void* dV, void* dKr,
-                               hipStream_t stream) {
+                               int64_t N, int Hkv, int chunk_len, int64_t max_doc_len, void* dK, void* dV,
+                               void* dKr, hipStream_t stream) {
     const char* fn = "msa_encode_pool_bwd";
     if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
     if (!dtype_ok(dt)) return fail(MSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dt));
@@ -241,6 +259,7 @@ msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt, const void* dKVbar, c
     if (n_docs > T || n_docs > N || N > T)
         return fail(MSA_ERR_INVALID_ARG, "%s: need n_docs <= N <= T (%lld, %lld, %lld)", fn, (long long)n_docs,
                     (long long)N, (long long)T);
+    if (msa_status s = check_doc_len(fn, ctx, n_docs, T, max_doc_len)) return s;
     if (n_docs > 0 && (!dKVbar || !dKrbar || !doc_tok_off || !doc_chunk_off || !dK || !dV || !dKr))
         return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
     if (n_docs > 0 && (!aligned16(dKVbar) || !aligned16(dKrbar) || !aligned16(dK) || !aligned16(dV) ||
@@ -249,7 +268,7 @@ msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt, const void* dKVbar, c
     DeviceGuard dg(ctx->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_encode_pool_bwd: hipSetDevice");
     hipError_t e = msa::launch_encode_bwd(ctx, dt, dKVbar, dKrbar, doc_tok_off, doc_chunk_off, n_docs, T, N, Hkv,
-                                          chunk_len, dK, dV, dKr, stream);
+                                          chunk_len, max_doc_len, dK, dV, dKr, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_encode_pool_bwd: launch");
     return ok();
 }

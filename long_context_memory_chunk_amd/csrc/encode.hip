@@ -16,7 +16,11 @@
 //   their loads issued first (nontemporal: the raw tensors are streamed once),
 //   which keeps enough bytes in flight per wave to cover HBM latency.  Row
 //   loads of one wave cover whole 128-byte segments.  cos/sin come from the
-//   context's table (float64 angles rounded to float32).
+//   context's table (float64 angles rounded to float32).  The host has
+//   checked that the longest document (max_doc_len) fits the table; a
+//   document the device offsets make longer than that gets NaN rows instead
+//   of clamped positions, so a wrong length is visible and never read past
+//   the table.
 #include <type_traits>
 
 #include "common.hpp"
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void encode_pool_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ Kr,
     const int64_t* __restrict__ tok_off, const int64_t* __restrict__ chunk_off, int64_t n_docs,
     int64_t T_rows, int64_t N, int hkv, int chunk_len,
-    const float2* __restrict__ rope_cs, int max_pos,
+    const float2* __restrict__ rope_cs, int64_t max_doc_len,
     T* __restrict__ KVbar, T* __restrict__ Krbar) {
     constexpr int VEC = Vec16<T>::kN;           // elements per 16-byte slot
     constexpr int HALF = D / 2;
@@ -84,6 +88,19 @@ __global__ __launch_bounds__(256) void encode_pool_kernel(
         if (j < 0 || r0 >= e) continue;         // inconsistent offsets: row n is left unwritten
         const int64_t r1 = (r0 + chunk_len < e) ? r0 + chunk_len : e;
         const float cnt = float(r1 - r0);
+        if (e - s > max_doc_len) {              // longer than the host was told: NaN, not clamped positions
+            float nan[VEC];
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) nan[u] = __builtin_nanf("");
+            for (int slot = lane; slot < 2 * slots; slot += kWave) {
+                const int64_t o = int64_t(slot) * VEC;
+                Vec16<T>::store(KVbar + n * 2 * row_elems + o, nan);
+                Vec16<T>::store(KVbar + n * 2 * row_elems + row_elems + o, nan);
+            }
+            for (int slot = lane; slot < 2 * slots; slot += kWave)
+                Vec16<T>::store(Krbar + n * row_elems + int64_t(slot) * VEC, nan);
+            continue;
+        }
 
         for (int slot = lane; slot < slots; slot += kWave) {
             const int h = slot / SLOTS_PER_HEAD;
@@ -107,9 +124,8 @@ __global__ __launch_bounds__(256) void encode_pool_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < R; ++u) {
-                    int pos = int(r + u - s);
-                    pos = pos < max_pos ? pos : max_pos - 1;
-                    const float2* cs = rope_cs + int64_t(pos) * HALF + i0;
+                    const int64_t pos = r + u - s;    // < e - s <= max_doc_len <= max_pos
+                    const float2* cs = rope_cs + pos * HALF + i0;
                     float a[VEC], b[VEC];
                     Raw16<T>::unpack(ka[u], a);
                     Raw16<T>::unpack(kb[u], b);
@@ -178,7 +194,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void encode_bwd_kernel(
     const T* __restrict__ dKVbar, const T* __restrict__ dKrbar, const int64_t* __restrict__ tok_off,
     const int64_t* __restrict__ chunk_off, int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
-    const float2* __restrict__ rope_cs, int max_pos, T* __restrict__ dK, T* __restrict__ dV,
+    const float2* __restrict__ rope_cs, int64_t max_doc_len, T* __restrict__ dK, T* __restrict__ dV,
     T* __restrict__ dKr) {
     constexpr int VEC = Vec16<T>::kN;
     constexpr int HALF = D / 2;
@@ -199,6 +215,7 @@ __global__ __launch_bounds__(256) void encode_bwd_kernel(
         if (j < 0 || r0 >= e) continue;         // inconsistent offsets: nothing is written
         const int64_t r1 = (r0 + chunk_len < e) ? r0 + chunk_len : e;
         const float inv = 1.f / float(r1 - r0);
+        const bool too_long = e - s > max_doc_len;   // NaN gradients, not clamped positions
 
         for (int slot = lane; slot < slots; slot += kWave) {
             const int h = slot / SLOTS_PER_HEAD;
@@ -218,16 +235,24 @@ __global__ __launch_bounds__(256) void encode_bwd_kernel(
                 v1[u] *= inv; v2[u] *= inv;
                 q1[u] *= inv; q2[u] *= inv;
             }
-            for (int64_t r = r0; r < r1; ++r) {
-                int pos = int(r - s);
-                pos = pos < max_pos ? pos : max_pos - 1;
-                const float2* cs = rope_cs + int64_t(pos) * HALF + i0;
-                float a[VEC], bb[VEC];
+            if (too_long) {
 #pragma unroll
-                for (int w = 0; w < VEC; ++w) {
-                    const float2 t = cs[w];
-                    a[w] = k1[w] * t.x + k2[w] * t.y;     // the transpose of the rotation
-                    bb[w] = k2[w] * t.x - k1[w] * t.y;
+                for (int u = 0; u < VEC; ++u) k1[u] = k2[u] = v1[u] = v2[u] = q1[u] = q2[u] = __builtin_nanf("");
+            }
+            for (int64_t r = r0; r < r1; ++r) {
+                float a[VEC], bb[VEC];
+                if (too_long) {
+#pragma unroll
+                    for (int w = 0; w < VEC; ++w) a[w] = bb[w] = k1[w];
+                } else {
+                    const int64_t pos = r - s;          // < e - s <= max_doc_len <= max_pos
+                    const float2* cs = rope_cs + pos * HALF + i0;
+#pragma unroll
+                    for (int w = 0; w < VEC; ++w) {
+                        const float2 t = cs[w];
+                        a[w] = k1[w] * t.x + k2[w] * t.y;     // the transpose of the rotation
+                        bb[w] = k2[w] * t.x - k1[w] * t.y;
+                    }
                 }
                 const int64_t o = r * row_elems + int64_t(h) * D + i0;
                 St16<T>::put(dK + o, a);
@@ -244,26 +269,26 @@ __global__ __launch_bounds__(256) void encode_bwd_kernel(
 template <typename T, int D>
 hipError_t launch_bwd_typed(const msa_ctx* ctx, const void* dKVbar, const void* dKrbar, const int64_t* tok_off,
                             const int64_t* chunk_off, int64_t n_docs, int64_t T_rows, int64_t N, int hkv,
-                            int chunk_len, void* dK, void* dV, void* dKr, hipStream_t st) {
+                            int chunk_len, int64_t max_doc_len, void* dK, void* dV, void* dKr, hipStream_t st) {
     const int64_t blocks = ceil_div(N, int64_t(4));
     const unsigned grid = unsigned(blocks < (int64_t(1) << 30) ? blocks : (int64_t(1) << 30));
     hipLaunchKernelGGL((encode_bwd_kernel<T, D>), dim3(grid), dim3(256), 0, st, static_cast<const T*>(dKVbar),
                        static_cast<const T*>(dKrbar), tok_off, chunk_off, n_docs, T_rows, N, hkv, chunk_len,
-                       ctx->rope_cs, ctx->max_pos, static_cast<T*>(dK), static_cast<T*>(dV), static_cast<T*>(dKr));
+                       ctx->rope_cs, max_doc_len, static_cast<T*>(dK), static_cast<T*>(dV), static_cast<T*>(dKr));
     return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const msa_ctx* ctx, const void* K, const void* V, const void* Kr,
                         const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs,
-                        int64_t T_rows, int64_t N, int hkv, int chunk_len, void* KVbar,
-                        void* Krbar, hipStream_t st) {
+                        int64_t T_rows, int64_t N, int hkv, int chunk_len, int64_t max_doc_len,
+                        void* KVbar, void* Krbar, hipStream_t st) {
     const int64_t blocks = ceil_div(N, int64_t(4));
     const unsigned grid = unsigned(blocks < (int64_t(1) << 30) ? blocks : (int64_t(1) << 30));
     hipLaunchKernelGGL((encode_pool_kernel<T, D, kEncodeUnroll>), dim3(grid), dim3(256), 0, st,
                        static_cast<const T*>(K), static_cast<const T*>(V),
                        static_cast<const T*>(Kr), tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                       chunk_len, ctx->rope_cs, ctx->max_pos, static_cast<T*>(KVbar),
+                       chunk_len, ctx->rope_cs, max_doc_len, static_cast<T*>(KVbar),
                        static_cast<T*>(Krbar));
     return hipGetLastError();
 }
@@ -273,20 +298,20 @@ hipError_t launch_typed(const msa_ctx* ctx, const void* K, const void* V, const 
 hipError_t launch_encode(const msa_ctx* ctx, msa_dtype dt, const void* K, const void* V,
                          const void* Kr, const int64_t* tok_off, const int64_t* chunk_off,
                          int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
-                         void* KVbar, void* Krbar, hipStream_t st) {
+                         int64_t max_doc_len, void* KVbar, void* Krbar, hipStream_t st) {
     if (n_docs == 0 || N == 0) return hipSuccess;
     if (dt == MSA_BF16) {
         if (ctx->head_dim == 128)
             return launch_typed<bf16_t, 128>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N,
-                                             hkv, chunk_len, KVbar, Krbar, st);
+                                             hkv, chunk_len, max_doc_len, KVbar, Krbar, st);
         return launch_typed<bf16_t, 64>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                        chunk_len, KVbar, Krbar, st);
+                                        chunk_len, max_doc_len, KVbar, Krbar, st);
     }
     if (ctx->head_dim == 128)
         return launch_typed<float, 128>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                        chunk_len, KVbar, Krbar, st);
+                                        chunk_len, max_doc_len, KVbar, Krbar, st);
     return launch_typed<float, 64>(ctx, K, V, Kr, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                   chunk_len, KVbar, Krbar, st);
+                                   chunk_len, max_doc_len, KVbar, Krbar, st);
 }
 
 }  // namespace msa
@@ -295,19 +320,20 @@ namespace msa {
 
 hipError_t launch_encode_bwd(const msa_ctx* ctx, msa_dtype dt, const void* dKVbar, const void* dKrbar,
                              const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs, int64_t T_rows,
-                             int64_t N, int hkv, int chunk_len, void* dK, void* dV, void* dKr, hipStream_t st) {
+                             int64_t N, int hkv, int chunk_len, int64_t max_doc_len, void* dK, void* dV,
+                             void* dKr, hipStream_t st) {
     if (n_docs == 0 || N == 0) return hipSuccess;
     if (dt == MSA_BF16)
         return ctx->head_dim == 128
                    ? launch_bwd_typed<bf16_t, 128>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                                   chunk_len, dK, dV, dKr, st)
+                                                   chunk_len, max_doc_len, dK, dV, dKr, st)
                    : launch_bwd_typed<bf16_t, 64>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                                  chunk_len, dK, dV, dKr, st);
+                                                  chunk_len, max_doc_len, dK, dV, dKr, st);
     return ctx->head_dim == 128
                ? launch_bwd_typed<float, 128>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                              chunk_len, dK, dV, dKr, st)
+                                              chunk_len, max_doc_len, dK, dV, dKr, st)
                : launch_bwd_typed<float, 64>(ctx, dKVbar, dKrbar, tok_off, chunk_off, n_docs, T_rows, N, hkv,
-                                             chunk_len, dK, dV, dKr, st);
+                                             chunk_len, max_doc_len, dK, dV, dKr, st);
 }
 
 }  // namespace msa

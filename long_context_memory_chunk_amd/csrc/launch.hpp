@@ -11,10 +11,11 @@ namespace msa {
 hipError_t launch_encode(const msa_ctx* ctx, msa_dtype dt, const void* K, const void* V,
                          const void* Kr, const int64_t* tok_off, const int64_t* chunk_off,
                          int64_t n_docs, int64_t T_rows, int64_t N, int hkv, int chunk_len,
-                         void* KVbar, void* Krbar, hipStream_t st);
+                         int64_t max_doc_len, void* KVbar, void* Krbar, hipStream_t st);
 hipError_t launch_encode_bwd(const msa_ctx* ctx, msa_dtype dt, const void* dKVbar, const void* dKrbar,
                              const int64_t* tok_off, const int64_t* chunk_off, int64_t n_docs, int64_t T_rows,
-                             int64_t N, int hkv, int chunk_len, void* dK, void* dV, void* dKr, hipStream_t st);
+                             int64_t N, int hkv, int chunk_len, int64_t max_doc_len, void* dK, void* dV,
+                             void* dKr, hipStream_t st);
 
 struct RouteArgs {
     msa_dtype dt;

@@ -35,7 +35,7 @@ def test_synth_library_exports():
 
 
 def test_abi_version_and_status_strings():
-    assert msa.msa_abi_version() == 1
+    assert msa.msa_abi_version() == 2
     assert msa.msa_status_string(0) == "MSA_OK"
     assert msa.msa_status_string(4) == "MSA_ERR_WORKSPACE"
     assert msa.msa_status_string(99) == "MSA_STATUS_UNKNOWN"
@@ -52,6 +52,8 @@ def test_chunk_offsets_host_helper():
     tok = np.array([0, 5, 7, 14, 78, 143], dtype=np.int64)
     assert msa.msa_chunk_offsets(tok, 2).tolist() == [0, 3, 4, 8, 40, 73]
     assert msa.msa_chunk_offsets(tok, 64).tolist() == [0, 1, 2, 3, 4, 6]
+    off, longest = msa.msa_chunk_offsets(tok, 64, with_max_len=True)
+    assert off.tolist() == [0, 1, 2, 3, 4, 6] and longest == 65      # lengths 5, 2, 7, 64, 65
 
 
 def test_chunk_offsets_rejects_empty_document_and_bad_chunk():
@@ -92,7 +94,7 @@ def test_hip_runtime_failure_maps_to_msa_err_hip():
 
 def test_calls_without_context_fail_cleanly():
     L = msa.lib()
-    assert L.msa_encode_pool(None, 1, *([None] * 5), 1, 1, 1, 1, 1, None, None, None) == 1
+    assert L.msa_encode_pool(None, 1, *([None] * 5), 1, 1, 1, 1, 1, 1, None, None, None) == 1
     assert L.msa_route(None, 1, None, 1, 1, 1, None, 1, 1, None, 1, 1, None, None, None, None,
                        None, 0, None) == 1
     assert "ctx is NULL" in msa.msa_last_error()

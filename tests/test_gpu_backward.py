@@ -300,7 +300,7 @@ def test_encode_pool_bwd_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, ch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     out = [torch.full((T, Hkv, d), float("nan"), dtype=tdt, device="cuda") for _ in range(3)]
     msa.msa_encode_pool_bwd(ctx, W.dev(gKV, dtype), W.dev(gR, dtype), torch.from_numpy(tok).cuda(),
-                            torch.from_numpy(coff).cuda(), *out, chunk_len)
+                            torch.from_numpy(coff).cuda(), *out, chunk_len, max(lens))
     torch.cuda.synchronize()
     g = W.widen(gKV, dtype)
     ref = oracle.encode_pool_bwd(g[:, 0], g[:, 1], W.widen(gR, dtype), tok, chunk_len, ctx.rope_theta)
@@ -348,6 +348,6 @@ def test_backward_validation_errors(torch_mod, msa, ctx128):
     tok = torch.tensor([0, 5], dtype=torch.int64, device="cuda")
     coff = torch.tensor([0, 10], dtype=torch.int64, device="cuda")
     with pytest.raises(msa.MsaError) as e:
-        msa.msa_encode_pool_bwd(ctx128, gkv, gr, tok, coff, *out, 1)
+        msa.msa_encode_pool_bwd(ctx128, gkv, gr, tok, coff, *out, 1, 5)
     assert e.value.status == msa.MSA_ERR_INVALID_ARG
     torch.cuda.synchronize()

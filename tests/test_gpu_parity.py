@@ -26,6 +26,7 @@ import pytest
 
 import msa_synth
 import oracle
+from tests import peaked as P
 from tests import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -116,7 +117,8 @@ def test_encode_pool_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hkv, c, len
     KVbar = torch.full((N, 2, Hkv, d), float("nan"), dtype=tdt, device="cuda")
     Krbar = torch.full((N, Hkv, d), float("nan"), dtype=tdt, device="cuda")
     msa.msa_encode_pool(ctx, W.dev(K, dtype), W.dev(V, dtype), W.dev(Kr, dtype),
-                        torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda(), KVbar, Krbar, c)
+                        torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda(), KVbar, Krbar, c,
+                        int(lens.max()))
     torch.cuda.synchronize()
     Kb, Vb, Rb = oracle.encode_pool(W.widen(K, dtype), W.widen(V, dtype), W.widen(Kr, dtype), tok, c,
                                     ctx.rope_theta)
@@ -510,7 +512,7 @@ def test_sparse_attn_parity(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B,
                              W.widen(Vl, dtype), qoff, W.scale_of(d), ctx.rope_theta)
     got = W.widen(W.host_bits(O), dtype)
     tol = 2e-2 if dtype == "bf16" else 1e-3
-    assert np.max(np.abs(got - ref)) <= tol
+    P.assert_attn_close(got, ref, tol, f"{dtype} d={d} G={Hq // Hkv} B={B} Tq={Tq} L={L} rows={rows}")
 
 
 def _random_attn_cases(n, seed):
@@ -551,7 +553,7 @@ def test_sparse_attn_random_decode_shapes(torch_mod, msa, ctx128, Hq, Hkv, B, Tq
     ref = oracle.sparse_attn(W.widen(Q, "bf16"), kv[:, 0], kv[:, 1], mem_off, W.widen(Kl, "bf16"),
                              W.widen(Vl, "bf16"), qoff, W.scale_of(d), ctx128.rope_theta)
     got = W.widen(W.host_bits(O), "bf16")
-    assert np.max(np.abs(got - ref)) <= 2e-2
+    P.assert_attn_close(got, ref, 2e-2, f"G={Hq // Hkv} B={B} Tq={Tq} L={L} rows={rows} k={qoff}")
 
 
 def test_sparse_attn_is_deterministic(torch_mod, msa, ctx128):
@@ -599,10 +601,73 @@ def test_sparse_attn_running_max_rises_every_block(torch_mod, msa, ctx128):
     ref = oracle.sparse_attn(q[None, None], kvw[:, 0], kvw[:, 1], mem_off, W.widen(Kl, "bf16"),
                              W.widen(Vl, "bf16"), qoff, W.scale_of(d), ctx128.rope_theta)
     got = W.widen(W.host_bits(O), "bf16")
-    assert np.max(np.abs(got - ref)) <= 2e-2
+    P.assert_attn_close(got, ref, 2e-2, "rising running max")
 
 
 # ---------------------------------------------------------------- validation with a context
+
+def test_encode_rejects_documents_longer_than_the_rope_table(torch_mod, msa, ctx64):
+    """ctx64 has max_pos 4096: a document of 4,097 tokens needs position 4096,
+    so both encode calls refuse it before enqueueing anything; 4,096 tokens
+    is the longest accepted."""
+    torch = torch_mod
+    for n in (4097, 4096):
+        lens = np.array([3, n], dtype=np.int64)
+        tok = msa_synth.prefix_offsets(lens)
+        coff, longest = msa.msa_chunk_offsets(tok, 16, with_max_len=True)
+        assert longest == n
+        T, N = int(tok[-1]), int(coff[-1])
+        X = torch.zeros((T, 2, 64), dtype=torch.float32, device="cuda")
+        KVbar = torch.zeros((N, 2, 2, 64), dtype=torch.float32, device="cuda")
+        Krbar = torch.zeros((N, 2, 64), dtype=torch.float32, device="cuda")
+        tok_d, coff_d = torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda()
+        if n > ctx64.max_pos:
+            with pytest.raises(msa.MsaError) as e:
+                msa.msa_encode_pool(ctx64, X, X, X, tok_d, coff_d, KVbar, Krbar, 16, longest)
+            assert e.value.status == msa.MSA_ERR_INVALID_ARG and "max_pos" in str(e.value)
+            with pytest.raises(msa.MsaError) as e:
+                msa.msa_encode_pool_bwd(ctx64, KVbar, Krbar, tok_d, coff_d, X, X, X, 16, longest)
+            assert e.value.status == msa.MSA_ERR_INVALID_ARG and "max_pos" in str(e.value)
+        else:
+            msa.msa_encode_pool(ctx64, X, X, X, tok_d, coff_d, KVbar, Krbar, 16, longest)
+            torch.cuda.synchronize()
+            assert bool(torch.isfinite(KVbar).all())
+
+
+def test_encode_marks_a_document_longer_than_max_doc_len_with_nan(torch_mod, msa, ctx128):
+    """A max_doc_len below a document's real length is a caller error the
+    host cannot see (the offsets are on the device): that document's pooled
+    rows (and its token gradients in the backward) come out NaN, the other
+    documents' rows are exact, and nothing reads past the RoPE table."""
+    torch = torch_mod
+    lens = np.array([40, 100, 17], dtype=np.int64)
+    tok = msa_synth.prefix_offsets(lens)
+    coff = msa.msa_chunk_offsets(tok, 16)
+    T, N = int(tok[-1]), int(coff[-1])
+    K, V, Kr = (W.draw(23, s, (T, 2, 128), "f32") for s in (1, 2, 3))
+    KVbar = torch.zeros((N, 2, 2, 128), dtype=torch.float32, device="cuda")
+    Krbar = torch.zeros((N, 2, 128), dtype=torch.float32, device="cuda")
+    tok_d, coff_d = torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda()
+    msa.msa_encode_pool(ctx128, W.dev_f32(K), W.dev_f32(V), W.dev_f32(Kr), tok_d, coff_d, KVbar, Krbar, 16, 50)
+    dK = torch.zeros((T, 2, 128), dtype=torch.float32, device="cuda")
+    dV, dKr = torch.zeros_like(dK), torch.zeros_like(dK)
+    msa.msa_encode_pool_bwd(ctx128, KVbar, Krbar, tok_d, coff_d, dK, dV, dKr, 16, 50)
+    torch.cuda.synchronize()
+    kv, kr = KVbar.cpu().numpy(), Krbar.cpu().numpy()
+    long_rows = slice(int(coff[1]), int(coff[2]))
+    assert np.all(np.isnan(kv[long_rows])) and np.all(np.isnan(kr[long_rows]))
+    Kb, Vb, Rb = oracle.encode_pool(W.widen(K, "f32"), W.widen(V, "f32"), W.widen(Kr, "f32"), tok, 16,
+                                    ctx128.rope_theta)
+    for rows in (slice(int(coff[0]), int(coff[1])), slice(int(coff[2]), int(coff[3]))):
+        assert W.rel_row_err(kv[rows, 0], Kb[rows]) <= 1e-5
+        assert W.rel_row_err(kv[rows, 1], Vb[rows]) <= 1e-5
+        assert W.rel_row_err(kr[rows], Rb[rows]) <= 1e-5
+    toks = slice(int(tok[1]), int(tok[2]))
+    for g in (dK, dV, dKr):
+        g = g.cpu().numpy()
+        assert np.all(np.isnan(g[toks]))
+        assert np.all(np.isfinite(g[:int(tok[1])])) and np.all(np.isfinite(g[int(tok[2]):]))
+
 
 def test_validation_errors_enqueue_nothing(torch_mod, msa, ctx128):
     torch = torch_mod

@@ -7,6 +7,7 @@ import pytest
 
 import msa_synth
 import oracle
+from tests import peaked as P
 from tests import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -50,13 +51,13 @@ def test_tiny_fp32_end_to_end(gpu, msa):
     w = W.tiny_fp32()
     ctx = msa.msa_ctx_create(0, w["d"], w["theta"], 4096)
     tok = w["tok_off"]
-    coff = msa.msa_chunk_offsets(tok, w["chunk"])
+    coff, max_len = msa.msa_chunk_offsets(tok, w["chunk"], with_max_len=True)
     N = int(coff[-1])
     KVbar = torch.empty((N, 2, w["Hkv"], w["d"]), dtype=torch.float32, device="cuda")
     Krbar = torch.empty((N, w["Hkv"], w["d"]), dtype=torch.float32, device="cuda")
     msa.msa_encode_pool(ctx, W.dev_f32(w["K"]), W.dev_f32(w["V"]), W.dev_f32(w["Kr"]),
                         torch.from_numpy(tok).cuda(), torch.from_numpy(coff).cuda(), KVbar, Krbar,
-                        w["chunk"])
+                        w["chunk"], max_len)
     ids = torch.empty((1, w["top_k"]), dtype=torch.int32, device="cuda")
     ws = msa.workspace(msa.msa_route_workspace_size(0, 1, w["Tq"], w["Hq"], w["Hkv"], N, 64, w["top_k"]))
     msa.msa_route(ctx, W.dev_f32(w["Qr"]), Krbar, torch.from_numpy(coff).cuda(), w["top_k"], ids, ws)
@@ -73,7 +74,7 @@ def test_tiny_fp32_end_to_end(gpu, msa):
     mV, _ = oracle.gather_rows(Vb, coff, ids_ref[0])
     ref = oracle.sparse_attn(w["Q"].astype(np.float64), mK, mV, [0, m], w["K_loc"].astype(np.float64),
                              w["V_loc"].astype(np.float64), w["top_k"], W.scale_of(w["d"]), w["theta"])
-    assert np.max(np.abs(O.cpu().numpy() - ref)) <= 1e-3
+    P.assert_attn_close(O.cpu().numpy(), ref, 1e-3, "tiny fp32 pipeline")
     ctx.close()
 
 
@@ -88,7 +89,7 @@ def test_qwen_bf16_layer_end_to_end(gpu, msa):
     Hq, Hkv, d, c, k = w["Hq"], w["Hkv"], w["d"], w["chunk"], w["top_k"]
     ctx = msa.msa_ctx_create(0, d, w["theta"], 16384)
     tok, T = w["tok_off"], w["T"]
-    coff = msa.msa_chunk_offsets(tok, c)
+    coff, max_len = msa.msa_chunk_offsets(tok, c, with_max_len=True)
     N = int(coff[-1])
     K = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device="cuda")
     V = torch.empty_like(K)
@@ -97,7 +98,7 @@ def test_qwen_bf16_layer_end_to_end(gpu, msa):
     KVbar = torch.empty((N, 2, Hkv, d), dtype=torch.bfloat16, device="cuda")
     Krbar = torch.empty((N, Hkv, d), dtype=torch.bfloat16, device="cuda")
     msa.msa_encode_pool(ctx, K, V, W.dev_bf16(w["Kr"]), torch.from_numpy(tok).cuda(),
-                        torch.from_numpy(coff).cuda(), KVbar, Krbar, c)
+                        torch.from_numpy(coff).cuda(), KVbar, Krbar, c, max_len)
     del K, V
     ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
     ws = msa.workspace(msa.msa_route_workspace_size(1, 1, w["Tq"], Hq, Hkv, N, w["n_docs"], k))
@@ -134,5 +135,5 @@ def test_qwen_bf16_layer_end_to_end(gpu, msa):
     ref = oracle.sparse_attn(W.widen(w["Q"], "bf16"), mK, mV, [0, len(mK)], W.widen(w["K_loc"], "bf16"),
                              W.widen(w["V_loc"], "bf16"), k, W.scale_of(d), w["theta"])
     got = W.widen(W.host_bits(O), "bf16")
-    assert np.max(np.abs(got - ref)) <= 2e-2
+    P.assert_attn_close(got, ref, 2e-2, "Qwen-shaped layer decode")
     ctx.close()
