@@ -369,6 +369,31 @@ msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * msa_sparse_attn_noalloc -- msa_sparse_attn without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus workspace), same kernels, same result
+ * bits as msa_sparse_attn.  The split partials and packed key tiles live in
+ * a library-held scratch array of MSA_NOALLOC_SCRATCH_BYTES per device, held
+ * until the process ends; its device address is taken when the first
+ * context on the device is created.  A call whose msa_sparse_attn_workspace_size
+ * exceeds that returns MSA_ERR_WORKSPACE (nothing enqueued): decode and
+ * short-prompt attention fit, a long prefill does not.  Every call on a
+ * device shares that device's array and no part of it needs to start at
+ * zero (each kernel writes what it reads); calls that can overlap on one
+ * device (other streams, other threads) race on it and must be ordered by
+ * the caller.  The call calls no hipMalloc, hipFree or allocating routine.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+msa_status msa_sparse_attn_noalloc(msa_ctx* ctx, msa_dtype dt,
+                                   const void* Q, int64_t B, int Tq, int Hq,
+                                   const void* KVmem, const int64_t* mem_off,
+                                   int64_t mem_rows_cap, int64_t max_rows_per_query,
+                                   const void* K_local, const void* V_local, int L, int Hkv,
+                                   int q_offset, float scale, void* O, hipStream_t stream);
+
+/*
  * msa_sparse_attn_lse -- msa_sparse_attn that also saves, per output row, the
  * statistic its backward recomputes the softmax from.  Same arguments, plus
  *   lse            device float [B][Tq][Hq]: natural-log log-sum-exp over the

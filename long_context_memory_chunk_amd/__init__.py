@@ -27,7 +27,7 @@ EXPORTS = [
     "msa_encode_pool", "msa_encode_pool_bwd", "msa_route_workspace_size", "msa_route", "msa_route_time_next",
     "msa_route_bwd_workspace_size", "msa_route_bwd",
     "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
-    "msa_sparse_attn_workspace_size", "msa_sparse_attn",
+    "msa_sparse_attn_workspace_size", "msa_sparse_attn", "msa_sparse_attn_noalloc",
     "msa_sparse_attn_lse", "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
 ]
 
@@ -66,6 +66,8 @@ _SIGS = {
     "msa_sparse_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
                               P, SZ, P]),
+    "msa_sparse_attn_noalloc": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
+                                      P]),
     "msa_sparse_attn_lse": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
                                   P, P, SZ, P]),
     "msa_sparse_attn_bwd_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
@@ -295,6 +297,19 @@ def msa_sparse_attn(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local
                                  _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
+
+
+def msa_sparse_attn_noalloc(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local, q_offset, scale,
+                            O, stream=None):
+    """msa_sparse_attn with the library's scratch array instead of a workspace
+    (allocates nothing; see include/msa.h for the size limit)."""
+    B, Tq, Hq, d = Q.shape
+    _, L, Hkv, _ = K_local.shape
+    cap = KVmem.shape[0] if KVmem is not None else 0
+    _check(lib().msa_sparse_attn_noalloc(ctx.handle, _dtype(Q), _ptr(Q), B, Tq, Hq, _ptr(KVmem),
+                                         _ptr(mem_off), cap, max_rows_per_query, _ptr(K_local),
+                                         _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O),
+                                         _stream(stream)))
 
 
 def msa_sparse_attn_lse(ctx, Q, KVmem, mem_off, max_rows_per_query, K_local, V_local, q_offset, scale,

@@ -10,6 +10,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -25,6 +27,16 @@ bool attn_supported_group(int Hq, int Hkv);
 namespace {
 
 thread_local std::string g_err;
+
+// Library-held scratch for msa_sparse_attn_noalloc: one array per device
+// (each device holds its own copy, at its own address, for the life of the
+// process).  Host code never uses the array's name as an address: the device
+// address is looked up once per device, with that device current, and kept
+// in g_scratch_addr (and in every context on that device).
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;
 
 // msa_gather submits its copies with hipMemcpyBatchAsync when the HIP runtime
 // loaded in the process provides it (looked up at run time: an older runtime
@@ -179,6 +191,23 @@ msa_status msa_ctx_create(int device, int head_dim, double rope_theta, int max_p
     c->rope_cs = d_table;
     c->prof_start = nullptr;
     c->prof_stop = nullptr;
+    c->scratch = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        auto it = g_scratch_addr.find(device);
+        if (it == g_scratch_addr.end()) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));   // the device is current (DeviceGuard)
+            if (e != hipSuccess || !addr) {
+                delete c;
+                (void)hipFree(d_table);
+                return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                "msa_ctx_create: hipGetSymbolAddress of the scratch array");
+            }
+            it = g_scratch_addr.emplace(device, addr).first;
+        }
+        c->scratch = it->second;
+    }
     *out = c;
     return ok();
 }
@@ -586,6 +615,27 @@ msa_status msa_sparse_attn(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B,
     return sparse_attn_fwd("msa_sparse_attn", ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap,
                            max_rows_per_query, K_local, V_local, L, Hkv, q_offset, scale, O, nullptr, workspace,
                            ws_bytes, stream);
+}
+
+msa_status msa_sparse_attn_noalloc(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,
+                                   const void* KVmem, const int64_t* mem_off, int64_t mem_rows_cap,
+                                   int64_t max_rows_per_query, const void* K_local, const void* V_local, int L,
+                                   int Hkv, int q_offset, float scale, void* O, hipStream_t stream) {
+    const char* fn = "msa_sparse_attn_noalloc";
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+    if (!ctx->scratch) return fail(MSA_ERR_INVALID_ARG, "%s: context has no scratch address", fn);
+    msa_status s = check_attn(fn, ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap, max_rows_per_query,
+                              K_local, V_local, L, Hkv, q_offset, scale);
+    if (s != MSA_OK) return s;
+    const size_t need = msa::attn_workspace(dt, B, Tq, Hq, Hkv, ctx->head_dim, max_rows_per_query, L,
+                                            ctx->num_cus);
+    if (need > MSA_NOALLOC_SCRATCH_BYTES)
+        return fail(MSA_ERR_WORKSPACE,
+                    "%s: this call needs %zu bytes of scratch, the library's array holds %zu; "
+                    "use msa_sparse_attn with a workspace", fn, need, size_t(MSA_NOALLOC_SCRATCH_BYTES));
+    return sparse_attn_fwd(fn, ctx, dt, Q, B, Tq, Hq, KVmem, mem_off, mem_rows_cap, max_rows_per_query, K_local,
+                           V_local, L, Hkv, q_offset, scale, O, nullptr, ctx->scratch, MSA_NOALLOC_SCRATCH_BYTES,
+                           stream);
 }
 
 msa_status msa_sparse_attn_lse(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_t B, int Tq, int Hq,

@@ -138,4 +138,5 @@ struct msa_ctx {
     float2* rope_cs;   // device [max_pos][head_dim/2] (cos, sin)
     hipEvent_t prof_start;   // msa_route_time_next: consumed by the next msa_route
     hipEvent_t prof_stop;
+    void* scratch;           // device address of this device's library scratch array
 };
