@@ -76,13 +76,38 @@ def _aimed(target_dir, qs, logit, scale):
     return logit * target_dir / (scale * proj)
 
 
+def aim_memory_keys(q_tok, pos, theta, G, logit=10.0):
+    """Memory keys [Hkv, d] (used as stored) whose product with the query
+    q_tok [Hq, d] rotated to global position `pos` has a mean logit of `logit`
+    over each group's heads, built on the high-frequency rotary pairs."""
+    Hq, d = q_tok.shape
+    scale = 1.0 / np.sqrt(d)
+    qrot = oracle.rope(q_tok, np.full(Hq, pos), theta)
+    dirs = _group_dir(qrot * _hf_mask(d), G)
+    return np.stack([_aimed(dirs[g], qrot[g * G:(g + 1) * G], logit, scale) for g in range(Hq // G)])
+
+
+def aim_local_keys(q_tok, back, theta, G, logit=10.0):
+    """Unrotated local keys [Hkv, d] placed `back` positions before the query
+    token q_tok [Hq, d] with a mean logit of `logit` over each group's heads
+    (back = 0: the token's own key, aligned with the unrotated query; else
+    along the high-frequency pairs of the query rotated by `back`)."""
+    Hq, d = q_tok.shape
+    scale = 1.0 / np.sqrt(d)
+    if back == 0:
+        dirs, qs = _group_dir(q_tok, G), q_tok
+    else:
+        qs = oracle.rope(q_tok, np.full(Hq, back), theta)
+        dirs = _group_dir(qs * _hf_mask(d), G)
+    return np.stack([_aimed(dirs[g], qs[g * G:(g + 1) * G], logit, scale) for g in range(Hq // G)])
+
+
 def peaked_inputs(seed, B, Tq, Hq, Hkv, d, L, rows, qoff, theta, tokens=None, logit=10.0):
     """bf16 bits of Q [B,Tq,Hq,d], KV [M,2,Hkv,d], K_loc, V_loc [B,L,Hkv,d]
     and int64 mem_off [B+1], with keys planted for the query tokens in
     `tokens` (default: the last token) of every query, each planted key at a
     mean logit of `logit` over its group's query heads.  Returns a dict."""
     G = Hq // Hkv
-    scale = 1.0 / np.sqrt(d)
     mem_off = msa_synth.prefix_offsets(rows)
     M = int(mem_off[-1])
     tokens = [Tq - 1] if tokens is None else list(tokens)
@@ -91,34 +116,26 @@ def peaked_inputs(seed, B, Tq, Hq, Hkv, d, L, rows, qoff, theta, tokens=None, lo
     Kl = msa_synth.normal_bf16(seed, 3, (B, L, Hkv, d))
     Vl = msa_synth.normal_bf16(seed, 4, (B, L, Hkv, d))
     q64 = oracle.bf16_bits_to_f64(Q)
-    hf = _hf_mask(d)
     kv64 = oracle.bf16_bits_to_f64(KV[:, 0])
     kl64 = oracle.bf16_bits_to_f64(Kl)
     for b in range(B):
         nb = int(mem_off[b + 1] - mem_off[b])
         slots = memory_plant_rows(nb)
         for n, i in enumerate(tokens):
-            pos = qoff + (L - Tq) + i
-            qrot = oracle.rope(q64[b, i], np.full(Hq, pos), theta)
-            qrel = oracle.rope(q64[b, i], np.full(Hq, LOCAL_BACK), theta)
-            dir_mem = _group_dir(qrot * hf, G)
-            dir_diag = _group_dir(q64[b, i], G)
-            dir_back = _group_dir(qrel * hf, G)
             j = (L - Tq) + i
-            for g in range(Hkv):
-                grp = slice(g * G, (g + 1) * G)
-                for s in slots[n::len(tokens)]:
-                    kv64[mem_off[b] + s, g] = _aimed(dir_mem[g], qrot[grp], logit, scale)
-                kl64[b, j, g] = _aimed(dir_diag[g], q64[b, i, grp], logit, scale)
-                if j - LOCAL_BACK >= 0:
-                    kl64[b, j - LOCAL_BACK, g] = _aimed(dir_back[g], qrel[grp], logit, scale)
+            mem = aim_memory_keys(q64[b, i], qoff + j, theta, G, logit)
+            for s in slots[n::len(tokens)]:
+                kv64[mem_off[b] + s] = mem
+            kl64[b, j] = aim_local_keys(q64[b, i], 0, theta, G, logit)
+            if j - LOCAL_BACK >= 0:
+                kl64[b, j - LOCAL_BACK] = aim_local_keys(q64[b, i], LOCAL_BACK, theta, G, logit)
     KV[:, 0] = oracle.f64_to_bf16_bits(kv64)
     Kl = oracle.f64_to_bf16_bits(kl64)
     # values scaled by 1/4 (exact in bf16) so that |O| stays near one
     KV[:, 1] = oracle.f64_to_bf16_bits(V_SCALE * oracle.bf16_bits_to_f64(KV[:, 1]))
     Vl = oracle.f64_to_bf16_bits(V_SCALE * oracle.bf16_bits_to_f64(Vl))
     return dict(Q=Q, KV=KV, Kl=Kl, Vl=Vl, mem_off=mem_off, tokens=tokens, qoff=qoff, theta=theta,
-                scale=scale)
+                scale=1.0 / np.sqrt(d))
 
 
 def oracle_out(w, qoff=None, mem_keep=None, drop_last_local=False, local_shift=0, mem_late=False):
