@@ -12,8 +12,10 @@
 // the host: gather_plan turns the device-resident ids into (source row,
 // destination row, rows) triples, and gather_copy reads the host rows over
 // PCIe with 16-byte loads (pinned host memory is mapped into the GPU's
-// address space) and writes them to HBM.  No host synchronisation is needed
-// between routing and attention.
+// address space) and writes them to HBM.  For a single query, gather_one
+// does both in one launch: every workgroup sorts the query's K ids and scans
+// their row counts itself (a few hundred bytes) and then copies its share.
+// No host synchronisation is needed between routing and attention.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -110,6 +112,55 @@ __global__ __launch_bounds__(256) void gather_copy_kernel(const u32x4* __restric
     }
 }
 
+// One query: workgroup (e, y) copies rows y, y + kCopySplit, ... of the
+// document in sorted position e; every wave of it derives (source row,
+// destination row, rows) from the ids on its own (wave-uniform results), so
+// the workgroup needs no barrier; workgroup (0, 0) also writes mem_off.
+__global__ __launch_bounds__(256) void gather_one_kernel(const u32x4* __restrict__ host, int64_t row_vecs,
+                                                         const int32_t* __restrict__ ids, int K,
+                                                         const int64_t* __restrict__ off, int64_t n_docs,
+                                                         int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
+                                                         u32x4* __restrict__ dst) {
+    const int lane = threadIdx.x % kWave;
+    const int e = blockIdx.x;
+    int32_t id = (lane < K) ? ids[lane] : 0x7FFFFFFF;
+    if (id < 0 || id >= n_docs) id = 0x7FFFFFFF;          // invalid ids copy nothing
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int32_t y = __shfl_xor(id, j);
+            const bool asc_block = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            const int32_t mn = id < y ? id : y, mx = id < y ? y : id;
+            id = (lower == asc_block) ? mn : mx;
+        }
+    }
+    int64_t src = 0, rows = 0;
+    if (id != 0x7FFFFFFF) {
+        src = off[id];
+        const int64_t end = off[id + 1];
+        if (src >= 0 && end >= src && end <= n_rows_host) rows = end - src;
+        else src = 0;
+    }
+    const int64_t dst0 = wave_excl_scan(rows, lane);
+    const int64_t total = __shfl(dst0 + rows, 63);
+    if (e == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        mem_off[0] = 0;
+        mem_off[1] = total < cap ? total : cap;
+    }
+    // this workgroup's entry, clamped to the buffer
+    const int64_t my_src = __shfl(src, e), my_dst = __shfl(dst0, e);
+    int64_t my_rows = __shfl(rows, e);
+    if (my_dst >= cap) my_rows = 0;
+    else if (my_dst + my_rows > cap) my_rows = cap - my_dst;
+    for (int64_t r = blockIdx.y; r < my_rows; r += kCopySplit) {
+        const u32x4* sp = host + (my_src + r) * row_vecs;
+        u32x4* dp = dst + (my_dst + r) * row_vecs;
+        for (int64_t v = threadIdx.x; v < row_vecs; v += 256) dp[v] = sp[v];
+    }
+}
+
 }  // namespace
 
 size_t gather_device_workspace(int64_t B) { return align256(size_t(B) * 64 * 3 * sizeof(int64_t)); }
@@ -117,6 +168,12 @@ size_t gather_device_workspace(int64_t B) { return align256(size_t(B) * 64 * 3 *
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
                                 int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
                                 int64_t cap_rows, int64_t* mem_off, void* ws, hipStream_t st) {
+    if (B == 1) {
+        hipLaunchKernelGGL(gather_one_kernel, dim3(unsigned(K), kCopySplit), dim3(256), 0, st,
+                           static_cast<const u32x4*>(host), int64_t(row_bytes / 16), ids, K, off, n_docs,
+                           n_rows_host, cap_rows, mem_off, static_cast<u32x4*>(dst));
+        return hipGetLastError();
+    }
     int64_t* plan = static_cast<int64_t*>(ws);
     hipLaunchKernelGGL(gather_plan_kernel, dim3(1), dim3(kPlanWaves * 64), 0, st, ids, int(B), K, off, n_docs,
                        n_rows_host, cap_rows, mem_off, plan);

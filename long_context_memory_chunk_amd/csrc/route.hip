@@ -17,8 +17,13 @@
 //                         coalesced chunk-score loads): every document's key
 //                         bits and each wave's largest key.
 //   topk_final            the K-th largest wave maximum bounds the K-th key
-//                         from below; only the few waves that reach it are
-//                         searched for the top k.
+//                         from below, and the wave maxima are distinct keys,
+//                         so at most K waves reach it; their documents are
+//                         read in one batched pass and the top k of the keys
+//                         at or above the bound kept.
+// (A single kernel whose last workgroup does the final step was measured
+// slower: the device-scope fences that publish every workgroup's results
+// cost more than the second launch.)
 // The top-k key is 64 bits: order-preserving bits of the fp32 document
 // score above (0xFFFFFFFF - doc id), so a larger key is a better document
 // and equal scores order by lower id, a total order.
@@ -241,22 +246,27 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(
 // One workgroup per query.  The K largest wave maxima are K distinct
 // documents, so the K-th of them (thr) is at most the K-th largest key
 // overall: every top-K document has a key >= thr and lies in a wave whose
-// maximum is >= thr.  (a) 16 waves reduce the wave maxima to their top K and
-// a pairwise merge tree combines the 16 lists (thr); (b) the waves that reach thr are listed (usually a
-// few more than K) and their documents with keys >= thr are gathered in LDS;
-// (c) wave 0 offers those to its top K.  If ties make more documents qualify
-// than the buffers hold, wave 0 offers every document of every qualifying wave
-// instead (exact, slower).
+// maximum is >= thr, and only K waves have one (the maxima are distinct).
+// (a) The wave maxima are loaded once (kept in LDS when they fit); 16 waves
+// reduce them to their top K and a pairwise merge tree combines the 16 lists
+// (thr); (b) the waves that reach thr are listed; (c) every thread reads its
+// share of those waves' document keys in one batch of loads and keeps the
+// keys >= thr in LDS; (d) wave 0 offers those to its top K.  If ties make
+// more keys qualify than the buffer holds, wave 0 offers every document of
+// the qualifying waves instead (exact, slower).
 constexpr int kFinalWaves = 16;
-constexpr int kSelCap = 1024;
-constexpr int kMaxQual = 1024;
+constexpr int kFinalThreads = kFinalWaves * 64;
+constexpr int kSelCap = 4096;
+constexpr int kWmaxLds = 4096;                   // wave maxima kept in LDS (larger banks re-read them)
+constexpr int kDocsPerThread = MSA_MAX_TOPK * kDocsPerWave / kFinalThreads;
 
-__global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const uint32_t* __restrict__ dkey, int64_t n_docs, const uint64_t* __restrict__ wmax, int W, int K,
     int32_t* __restrict__ ids, float* __restrict__ scores) {
     __shared__ uint64_t lists[kFinalWaves][64];
     __shared__ uint64_t sel[kSelCap];
-    __shared__ int qual[kMaxQual];
+    __shared__ uint64_t s_wm[kWmaxLds];
+    __shared__ int qual[MSA_MAX_TOPK];
     __shared__ int s_count, s_nq;
     __shared__ uint64_t s_thr;
     const int tid = threadIdx.x;
@@ -265,13 +275,17 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
     const int64_t b = blockIdx.x;
     const uint64_t* wm = wmax + b * W;
     const uint32_t* db = dkey + b * n_docs;
+    const bool wm_lds = W <= kWmaxLds;
 
     // (a) thr = the K-th largest wave maximum
     const int per = ((W + kFinalWaves - 1) / kFinalWaves + kWave - 1) / kWave * kWave;
     const int c0 = wave * per, c1 = (c0 + per < W) ? c0 + per : W;
     uint64_t best = 0;
-    for (int base = c0; base < c1; base += kWave)
-        best = wave_offer(best, (base + lane < c1) ? wm[base + lane] : 0, K, lane);
+    for (int base = c0; base < c1; base += kWave) {
+        const uint64_t m = (base + lane < c1) ? wm[base + lane] : 0;
+        if (wm_lds && base + lane < c1) s_wm[base + lane] = m;
+        best = wave_offer(best, m, K, lane);
+    }
     lists[wave][lane] = (lane < K) ? best : 0;
     if (tid == 0) { s_count = 0; s_nq = 0; }
     __syncthreads();
@@ -288,30 +302,37 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
     __syncthreads();
     const uint64_t thr = s_thr;
 
-    // (b) qualifying waves, then their documents at or above thr
-    for (int i = tid; i < W; i += kFinalWaves * 64) {
-        const uint64_t m = wm[i];
+    // (b) the waves that reach thr: at most K
+    for (int i = tid; i < W; i += kFinalThreads) {
+        const uint64_t m = wm_lds ? s_wm[i] : wm[i];
         if (m != 0 && m >= thr) {
             const int p = atomicAdd(&s_nq, 1);
-            if (p < kMaxQual) qual[p] = i;
+            if (p < MSA_MAX_TOPK) qual[p] = i;
         }
     }
     __syncthreads();
-    const int nq = s_nq;
-    constexpr int kWavesPerPass = kFinalWaves * 64 / kDocsPerWave;
-    if (nq <= kMaxQual) {
-        for (int q0 = 0; q0 < nq; q0 += kWavesPerPass) {
-            const int q = q0 + tid / kDocsPerWave;
-            if (q < nq) {
-                const int64_t doc = int64_t(qual[q]) * kDocsPerWave + tid % kDocsPerWave;
-                if (doc < n_docs) {
-                    const uint32_t o = db[doc];
-                    const uint64_t key = (uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(doc));
-                    if (o != 0 && key >= thr) {
-                        const int p = atomicAdd(&s_count, 1);
-                        if (p < kSelCap) sel[p] = key;
-                    }
-                }
+    const int nq = s_nq < MSA_MAX_TOPK ? s_nq : MSA_MAX_TOPK;
+
+    // (c) their document keys, one batch of loads per thread: entry e of the
+    // nq * 256 documents is thread e % 1024's load e / 1024
+    {
+        uint32_t o[kDocsPerThread];
+#pragma unroll
+        for (int u = 0; u < kDocsPerThread; ++u) {
+            const int e = u * kFinalThreads + tid;
+            int64_t doc = n_docs;
+            if (e < nq * kDocsPerWave) doc = int64_t(qual[e / kDocsPerWave]) * kDocsPerWave + e % kDocsPerWave;
+            o[u] = doc < n_docs ? db[doc] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kDocsPerThread; ++u) {
+            const int e = u * kFinalThreads + tid;
+            if (o[u] == 0u || e >= nq * kDocsPerWave) continue;
+            const int64_t doc = int64_t(qual[e / kDocsPerWave]) * kDocsPerWave + e % kDocsPerWave;
+            const uint64_t key = (uint64_t(o[u]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(doc));
+            if (key >= thr) {
+                const int p = atomicAdd(&s_count, 1);
+                if (p < kSelCap) sel[p] = key;
             }
         }
     }
@@ -319,17 +340,15 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
     const int count = s_count;
     if (wave != 0) return;
 
-    // (c) the top K
+    // (d) the top K
     best = 0;
-    if (nq <= kMaxQual && count <= kSelCap) {
+    if (count <= kSelCap) {
         for (int base = 0; base < count; base += kWave)
             best = wave_offer(best, (base + lane < count) ? sel[base + lane] : 0, K, lane);
     } else {
-        for (int w = 0; w < W; ++w) {
-            const uint64_t m = wm[w];
-            if (m == 0 || m < thr) continue;
+        for (int q = 0; q < nq; ++q)
             for (int j0 = 0; j0 < kDocsPerWave; j0 += kWave) {
-                const int64_t doc = int64_t(w) * kDocsPerWave + j0 + lane;
+                const int64_t doc = int64_t(qual[q]) * kDocsPerWave + j0 + lane;
                 uint64_t key = 0;
                 if (doc < n_docs) {
                     const uint32_t o = db[doc];
@@ -337,7 +356,6 @@ __global__ __launch_bounds__(kFinalWaves * 64) void topk_final_kernel(
                 }
                 best = wave_offer(best, key, K, lane);
             }
-        }
     }
     if (lane < K) {
         ids[b * K + lane] = int32_t(0xFFFFFFFFu - uint32_t(best));
@@ -406,7 +424,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
                        0, st, c, a.N, a.chunk_off, a.n_docs, wpb, dkey, wmax, a.out_doc);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalWaves * 64), 0, st, dkey,
+    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalThreads), 0, st, dkey,
                        a.n_docs, wmax, wpb, a.top_k, a.out_ids, a.out_scores);
     return hipGetLastError();
 }
