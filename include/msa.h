@@ -194,11 +194,13 @@ msa_status msa_encode_pool_bwd(msa_ctx* ctx, msa_dtype dt,
  *                  the workspace).
  *   out_doc        device float[B][n_docs] receives D, or NULL.
  *   workspace      device, >= msa_route_workspace_size(...) bytes.
- * bf16 routing at d = 128 with B*Tq > 4 and (Tq == 1 or Tq a multiple of
- * 128) contracts on the matrix cores, with the head-group sum of the unit
- * query vectors rounded to bf16 (relative error <= 2^-9 per element, so a
- * score moves by at most 2^-9); other cases accumulate in fp32 on the
- * vector units.
+ * bf16 routing at d = 128 with B*Tq > 4 contracts on the matrix cores (a
+ * query of any length is padded to whole row tiles whose padding is left out
+ * of the token max), with the head-group sum of the unit query vectors
+ * rounded to bf16 (relative error <= 2^-9 per element, so a score moves by at
+ * most 2^-9); a query of at least 1,024 tokens, or a multiple of 256, takes
+ * one GEMM that also rounds the unit keys to bf16 (at most 2^-8).  Other
+ * cases accumulate in fp32 on the vector units.
  */
 size_t msa_route_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv,
                                 int64_t N, int64_t n_docs, int top_k);

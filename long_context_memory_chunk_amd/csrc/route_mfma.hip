@@ -1,7 +1,13 @@
 // Stage 2a on the matrix cores: routing scores as a dense contraction, for
-// batched decode (B*Tq > 4) and multi-token query prefill.  Two kernels:
-// route_mfma_kernel (below) for decode batches and short query blocks, and the
-// one-GEMM path (route_gemm_kernel, further down) for Tq a multiple of 256.
+// batched decode (B*Tq > 4) and multi-token query prefill of any length.  Two
+// kernels: route_mfma_kernel (below) for decode batches and short query
+// blocks, and the one-GEMM path (route_gemm_kernel, further down) for long
+// queries (Tq a multiple of 256, or at least 1,024 tokens).
+//
+// A multi-token query is padded to a whole number of row tiles: query b's
+// token t sits at row b * Tq_pad + t, rows t >= Tq hold zeros and are left
+// out of the token max (a tile never holds two queries, and the last tile of
+// a query holds at least one real token).
 //
 // Source: news.neo-ai.one MSA article, 全体設計 › アーキテクチャ (Fig. 2):
 // cosine similarity of Qr with K̄r, averaged over heads, maximised over
@@ -20,9 +26,9 @@
 // that accumulator to the running total.  K̄r enters the MFMA exactly; U is
 // rounded once to bf16 (relative error <= 2^-9 per element), which moves a
 // score by at most (1/Hq) sum_g 2^-9 |U_g| <= 2^-9, since |U_g| <= G.
-// Epilogue: Tq = 1 -> each row is its own query, scores are written; Tq a
-// multiple of BM -> the tile's column maxima over its BM tokens are written
-// to a partial array and route_mfma_tokmax takes the max over a query's tiles.
+// Epilogue: Tq = 1 -> each row is its own query, scores are written; else ->
+// the tile's column maxima over its real tokens are written to a partial
+// array and route_mfma_tokmax takes the max over a query's tiles.
 #include <type_traits>
 
 #include "lds_dma.hpp"
@@ -37,11 +43,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kStride = 128 + 8;   // LDS row stride in bf16 (16-byte pad: 4-bank skew per row)
 constexpr float kEps = 1e-8f;
 
-__global__ __launch_bounds__(256) void u_to_bf16_kernel(const float* __restrict__ U, int64_t n_real,
-                                                        int64_t n_pad, uint16_t* __restrict__ Ub) {
+// U rows in the padded layout: padded row p is query p / Tq_pad's token
+// p % Tq_pad, real when that token is < Tq (and the query < B).
+__host__ __device__ inline int64_t u_src_row(int64_t p, int64_t B, int Tq, int Tq_pad) {
+    const int64_t b = p / Tq_pad;
+    const int t = int(p % Tq_pad);
+    return (b < B && t < Tq) ? b * Tq + t : -1;
+}
+
+__global__ __launch_bounds__(256) void u_to_bf16_kernel(const float* __restrict__ U, int64_t B, int Tq, int Tq_pad,
+                                                        int row_elems, int64_t n_pad, uint16_t* __restrict__ Ub) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (i >= n_pad) return;
-    Ub[i] = (i < n_real) ? f32_to_bf16(U[i]) : uint16_t(0);
+    const int64_t src = u_src_row(i / row_elems, B, Tq, Tq_pad);
+    Ub[i] = (src >= 0) ? f32_to_bf16(U[src * row_elems + i % row_elems]) : uint16_t(0);
 }
 
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear id, and
@@ -91,7 +106,7 @@ __global__ __launch_bounds__(256) void route_rnorm_kernel(const uint16_t* __rest
 template <int BM, int BN, bool PRE_RN>
 __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
     const uint16_t* __restrict__ Ub, int64_t Q, const uint16_t* __restrict__ Kr, int64_t N, int hkv,
-    int Tq, float inv_hq, float* __restrict__ cout, float* __restrict__ partial, TileOrder ord,
+    int Tq, int Tq_pad, float inv_hq, float* __restrict__ cout, float* __restrict__ partial, TileOrder ord,
     const float* __restrict__ rn_pre) {
     constexpr int WM = (BM >= 64) ? 2 : 1;        // waves along queries
     constexpr int WN = 4 / WM;                    // waves along chunks
@@ -225,13 +240,20 @@ __global__ __launch_bounds__(256, 2) void route_mfma_kernel(
                 }
         return;
     }
+    // rows of this tile that are real tokens of its query (the padding of a
+    // query's last tile is left out of the max)
+    const int64_t t_in = q0 % Tq_pad;
+    const int real = (Tq - t_in < BM) ? int(Tq - t_in) : BM;
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
         float m = -INFINITY;
 #pragma unroll
         for (int a = 0; a < MI; ++a)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, tot[a][b][i]);
+            for (int i = 0; i < 16; ++i) {
+                const int r = wm * TM + a * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+                m = (r < real) ? fmaxf(m, tot[a][b][i]) : m;
+            }
         m = fmaxf(m, __shfl_xor(m, 32));
         if (lane < 32) sMax[wm][wn * TN + b * 32 + lane] = m;
     }
@@ -258,7 +280,7 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
 
 // ---------------------------------------------------------------- prefill: one GEMM
 //
-// For a prefill query (Tq a multiple of 256) the scores are computed as one
+// For a long prefill query (padded to a multiple of 256) the scores are computed as one
 // bf16 GEMM over the full Hkv*128-wide contraction,
 //     s[q][n] = (1/Hq) U[q] . K̂[n],   K̂[n][g] = K̄r[n][g] / max(|K̄r[n][g]|, eps),
 // with K̂ rounded once to bf16 by route_khat_pack (a second rounding next to
@@ -288,17 +310,19 @@ constexpr int kStages = 4;       // stages in LDS: three copies in flight behind
 // ((r >> 1) ^ (r >> 3)) & 3 gave 160M and a 9% slower kernel.)
 __host__ __device__ inline int swz(int r) { return (r ^ (r >> 2)) & 3; }
 
-// U (fp32 [Q][K]) -> packed bf16 tiles; rows >= Q are zero.  One thread per unit.
-__global__ __launch_bounds__(256) void route_u_pack(const float* __restrict__ U, int64_t Q, int64_t q_pad, int K,
-                                                    u32x4* __restrict__ Up) {
+// U (fp32 [B*Tq][K]) -> packed bf16 tiles in the padded row layout; padding
+// rows are zero.  One thread per unit.
+__global__ __launch_bounds__(256) void route_u_pack(const float* __restrict__ U, int64_t B, int Tq, int Tq_pad,
+                                                    int64_t q_pad, int K, u32x4* __restrict__ Up) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;        // unit index in row-major order
     const int units_per_row = K / 8;
     if (i >= q_pad * units_per_row) return;
     const int64_t q = i / units_per_row;
     const int ku = int(i % units_per_row);                             // unit along the contraction
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (q < Q) {
-        const float* src = U + q * K + ku * 8;
+    const int64_t sq = u_src_row(q, B, Tq, Tq_pad);
+    if (sq >= 0) {
+        const float* src = U + sq * K + ku * 8;
         w = u32x4{pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]), pack_bf16x2(src[4], src[5]),
                   pack_bf16x2(src[6], src[7])};
     }
@@ -337,7 +361,7 @@ __global__ __launch_bounds__(256) void route_khat_pack(const uint16_t* __restric
 }
 
 __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restrict__ Up, const u32x4* __restrict__ Kp,
-                                                            int64_t N, int S, float inv_hq,
+                                                            int64_t N, int S, int Tq, int Tq_pad, float inv_hq,
                                                             float* __restrict__ partial, TileOrder ord) {
     __shared__ __attribute__((aligned(16))) u32x4 sA[kStages * kUnitsPerStage];
     __shared__ __attribute__((aligned(16))) u32x4 sB[kStages * kUnitsPerStage];
@@ -439,17 +463,29 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
         mma_half(a1, b1, 2);
     }
 
-    // ---- epilogue: column maxima over the tile's 256 tokens (one accumulator
-    // column block at a time: the scheduler barrier keeps the reads of the
-    // accumulation registers from being hoisted all at once)
+    // ---- epilogue: column maxima over the tile's real tokens (one
+    // accumulator column block at a time: the scheduler barrier keeps the
+    // reads of the accumulation registers from being hoisted all at once)
+    const int64_t t_in = (qt * GB) % Tq_pad;
+    const int real = (Tq - t_in < GB) ? int(Tq - t_in) : GB;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         __builtin_amdgcn_sched_barrier(0);
         float m = -INFINITY;
+        if (real == GB) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[a][b][i]);
+        } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = wm * 128 + a * 32 + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
+                    m = (r < real) ? fmaxf(m, acc[a][b][i]) : m;
+                }
+        }
         m = fmaxf(m, __shfl_xor(m, 32));
         if (lane < 32) sMax[wm][wn * 128 + b * 32 + lane] = m;
     }
@@ -460,21 +496,26 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
 
 struct Plan {
     bool gemm;
-    int bm, bn;
+    int bm, bn, tq_pad;
     int64_t q_pad, q_tiles, n_pad;
     size_t ub_bytes, partial_bytes, rn_bytes, kp_bytes;
 };
 
+// Tq == 1: rows are queries (32-row tiles for up to 32 queries, else 128).
+// Tq a multiple of 256, or >= 1,024: the GEMM, each query padded to a multiple
+// of 256 tokens (at most 20% padding).  Otherwise 128-row tiles for Tq > 32
+// and 32-row tiles below, each query padded to a multiple of the tile.
 Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
     Plan p;
     const int64_t Q = B * Tq;
-    p.gemm = (Tq % GB == 0);
+    p.gemm = Tq > 1 && (Tq % GB == 0 || Tq >= 1024);
     if (p.gemm) {
         p.bm = p.bn = GB;
-        p.q_pad = Q;
-        p.q_tiles = Q / GB;
+        p.tq_pad = int(ceil_div(int64_t(Tq), int64_t(GB)) * GB);
+        p.q_pad = B * p.tq_pad;
+        p.q_tiles = p.q_pad / GB;
         p.n_pad = ceil_div(N, int64_t(GB)) * GB;
-        p.ub_bytes = align256(size_t(Q) * Hkv * 128 * 2);
+        p.ub_bytes = align256(size_t(p.q_pad) * Hkv * 128 * 2);
         p.kp_bytes = align256(size_t(p.n_pad) * Hkv * 128 * 2);
         p.partial_bytes = align256(size_t(p.q_tiles) * N * 4);
         p.rn_bytes = 0;
@@ -482,9 +523,15 @@ Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
     }
     p.kp_bytes = 0;
     p.n_pad = N;
-    p.bm = (Tq == 1 && Q <= 32) ? 32 : 128;
+    p.bm = (Tq == 1) ? (Q <= 32 ? 32 : 128) : (Tq > 32 ? 128 : 32);
     p.bn = 128;
-    p.q_pad = ceil_div(Q, p.bm) * p.bm;
+    if (Tq == 1) {
+        p.tq_pad = 1;
+        p.q_pad = ceil_div(Q, p.bm) * p.bm;
+    } else {
+        p.tq_pad = int(ceil_div(int64_t(Tq), int64_t(p.bm)) * p.bm);
+        p.q_pad = B * p.tq_pad;
+    }
     p.q_tiles = p.q_pad / p.bm;
     p.ub_bytes = align256(size_t(p.q_pad) * Hkv * 128 * 2);
     p.partial_bytes = (Tq == 1) ? 0 : align256(size_t(p.q_tiles) * N * 4);
@@ -496,8 +543,7 @@ Plan plan_for(int64_t B, int Tq, int Hkv, int64_t N) {
 
 bool route_mfma_applicable(msa_dtype dt, int64_t B, int Tq, int Hkv, int D) {
     if (dt != MSA_BF16 || D != 128 || Hkv < 1) return false;
-    if (B * Tq <= 4) return false;                 // the streaming scan handles decode
-    return Tq == 1 || Tq % 128 == 0;
+    return B * Tq > 4;                             // the streaming scan handles decode
 }
 
 size_t route_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int) {
@@ -516,26 +562,27 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
         u32x4* Up = static_cast<u32x4*>(ws);
         float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
         u32x4* Kp = reinterpret_cast<u32x4*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
-        hipLaunchKernelGGL(route_u_pack, dim3(unsigned(ceil_div(Q * (K / 8), 256))), dim3(256), 0, st, U, Q, Q, K, Up);
+        hipLaunchKernelGGL(route_u_pack, dim3(unsigned(ceil_div(p.q_pad * (K / 8), 256))), dim3(256), 0, st, U, a.B,
+                           a.Tq, p.tq_pad, p.q_pad, K, Up);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(route_khat_pack, dim3(unsigned(ceil_div(p.n_pad * a.Hkv * 16, 256))), dim3(256), 0, st,
                            static_cast<const uint16_t*>(a.Krbar), a.N, p.n_pad, a.Hkv, Kp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const TileOrder ord = tile_order(p.q_tiles, p.n_pad / GB, 4, 8);
         err = launch_timed(route_gemm_kernel, dim3(unsigned(ord.blocks)), dim3(256), st, a.prof_start, a.prof_stop,
-                           static_cast<const u32x4*>(Up), static_cast<const u32x4*>(Kp), a.N, S,
+                           static_cast<const u32x4*>(Up), static_cast<const u32x4*>(Kp), a.N, S, a.Tq, p.tq_pad,
                            1.f / float(a.Hq), partial, ord);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
-                           a.N, int(a.Tq / GB), a.B, c);
+                           a.N, int(p.tq_pad / GB), a.B, c);
         return hipGetLastError();
     }
     uint16_t* Ub = static_cast<uint16_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
     float* rn = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
-    const int64_t n_real = Q * a.Hkv * 128, n_pad = p.q_pad * a.Hkv * 128;
-    hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, n_real,
-                       n_pad, Ub);
+    const int64_t n_pad = p.q_pad * a.Hkv * 128;
+    hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, a.B, a.Tq,
+                       p.tq_pad, a.Hkv * 128, n_pad, Ub);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const TileOrder ord = tile_order(p.q_tiles, ceil_div(a.N, p.bn));
@@ -552,18 +599,18 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
     const float* rnc = rn;
     if (p.bm == 32)
         err = p.rn_bytes ? launch_timed(route_mfma_kernel<32, 128, true>, grid, dim3(256), st, a.prof_start, a.prof_stop,
-                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc)
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, p.tq_pad, inv_hq, c, partial, ord, rnc)
                          : launch_timed(route_mfma_kernel<32, 128, false>, grid, dim3(256), st, a.prof_start, a.prof_stop,
-                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc);
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, p.tq_pad, inv_hq, c, partial, ord, rnc);
     else
         err = p.rn_bytes ? launch_timed(route_mfma_kernel<128, 128, true>, grid, dim3(256), st, a.prof_start, a.prof_stop,
-                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc)
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, p.tq_pad, inv_hq, c, partial, ord, rnc)
                          : launch_timed(route_mfma_kernel<128, 128, false>, grid, dim3(256), st, a.prof_start, a.prof_stop,
-                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, inv_hq, c, partial, ord, rnc);
+                                        Ubc, Q, Kr, a.N, a.Hkv, a.Tq, p.tq_pad, inv_hq, c, partial, ord, rnc);
     if (err != hipSuccess) return err;
     if (a.Tq > 1) {
         hipLaunchKernelGGL(route_mfma_tokmax, dim3(unsigned(ceil_div(a.B * a.N, 256))), dim3(256), 0, st, partial,
-                           a.N, int(a.Tq / p.bm), a.B, c);
+                           a.N, int(p.tq_pad / p.bm), a.B, c);
         err = hipGetLastError();
     }
     return err;

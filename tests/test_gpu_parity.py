@@ -9,11 +9,12 @@ Tolerances (stated where used):
                    a 128-term fp32 dot product errs by at most 128 * 2^-24 *
                    |U_g|, so the sum over Hkv groups / Hq errs by <= 8e-6;
                    rsqrt and the unit-query error add ~1e-6
-                   3e-3 absolute on the matrix-core path, which rounds U to
-                   bf16 (relative 2^-9 per element): |delta s| <= 2^-9
+                   3e-3 absolute on the matrix-core path (bf16, d 128,
+                   B*Tq > 4), which rounds U to bf16 (relative 2^-9 per
+                   element): |delta s| <= 2^-9
                    5e-3 absolute on the prefill GEMM path (Tq a multiple of
-                   256), which also rounds the unit keys to bf16:
-                   |delta s| <= 2^-9 + 2^-9 = 2^-8
+                   256 or at least 1,024), which also rounds the unit keys to
+                   bf16: |delta s| <= 2^-9 + 2^-9 = 2^-8
   top-k            document id sets bit-exact on planted-margin inputs; on
                    unplanted inputs every selected id is a valid top-k under
                    the score tolerance and the order is (score desc, id asc)
@@ -35,16 +36,17 @@ SCORE_TOL = 1e-4
 # Matrix-core routing rounds the query group sums U to bf16 (relative 2^-9 per
 # element); by Cauchy-Schwarz |delta s| <= (1/Hq) sum_g 2^-9 |U_g| <= 2^-9.
 MFMA_SCORE_TOL = 3e-3
-# The prefill GEMM path (Tq a multiple of 256) also rounds the unit keys
-# K̄r/|K̄r| to bf16: |delta s| <= 2^-9 + 2^-9 = 2^-8 ~ 3.9e-3.
+# The prefill GEMM path (Tq a multiple of 256, or at least 1,024 tokens) also
+# rounds the unit keys K̄r/|K̄r| to bf16: |delta s| <= 2^-9 + 2^-9 = 2^-8 ~ 3.9e-3.
 GEMM_SCORE_TOL = 5e-3
 
 
 def _score_tol(dtype, d, B, Tq):
-    if dtype == "bf16" and d == 128 and B * Tq > 4 and Tq % 256 == 0:
+    if dtype != "bf16" or d != 128 or B * Tq <= 4:
+        return SCORE_TOL                        # vector units
+    if Tq > 1 and (Tq % 256 == 0 or Tq >= 1024):
         return GEMM_SCORE_TOL
-    mfma = dtype == "bf16" and d == 128 and B * Tq > 4 and (Tq == 1 or Tq % 128 == 0)
-    return MFMA_SCORE_TOL if mfma else SCORE_TOL
+    return MFMA_SCORE_TOL
 
 
 @pytest.fixture(scope="module")
@@ -223,6 +225,15 @@ ROUTE_CASES = [
     ("bf16", 128, 16, 4, 2, 128, 100, 12, 5),    # matrix cores: 4 KV heads, 2 queries
     ("bf16", 128, 16, 16, 6, 1, 90, 4, 7),       # matrix cores: 16 KV heads
     ("bf16", 128, 16, 4, 2, 512, 300, 6, 12),    # one GEMM: two 512-token queries, 4 KV heads
+    # query lengths that are no multiple of a tile: padded rows left out of the token max
+    ("bf16", 128, 32, 8, 1, 5, 200, 8, 16),      # 32-row tiles, 27 padded rows
+    ("bf16", 128, 32, 8, 4, 2, 100, 4, 8),       # 32-row tiles, four 2-token queries
+    ("bf16", 128, 16, 4, 3, 33, 100, 5, 9),      # 128-row tiles, 95 padded rows per query
+    ("bf16", 128, 32, 8, 2, 100, 150, 6, 8),     # 128-row tiles, two queries
+    ("bf16", 128, 32, 8, 1, 300, 200, 6, 16),    # three 128-row tiles, the last mostly padding
+    ("bf16", 128, 32, 8, 2, 1100, 80, 5, 10),    # GEMM: two queries of five 256-row tiles each
+    ("bf16", 128, 32, 8, 1, 1500, 80, 5, 10),    # GEMM, 36 padded rows
+    ("bf16", 128, 32, 8, 1, 8000, 60, 5, 16),    # GEMM: an 8,000-token prompt
 ]
 
 
@@ -280,7 +291,33 @@ def test_route_parity_random_shapes(torch_mod, msa, ctx64, ctx128, dtype, d, Hq,
     test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, n_docs, maxc, k)
 
 
-@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16), (32, 1), (1, 256)])
+@pytest.mark.parametrize("Tq", [5, 33, 100, 1100])
+def test_route_padded_rows_stay_out_of_the_token_max(torch_mod, msa, ctx128, Tq):
+    """Every real score is about -0.9 (keys point against the queries), so a
+    padded query row -- zeros, score 0 -- that reached the token max would
+    show as 0.  Tq 5 and 33 pad 32- and 128-row tiles, 100 a 128-row tile,
+    1,100 the GEMM's 256-row tiles."""
+    torch = torch_mod
+    Hq, Hkv, d, k = 32, 8, 128, 8
+    rng = np.random.default_rng(77)
+    v = rng.standard_normal(d)
+    Qr = v[None, None, None, :] + 0.1 * rng.standard_normal((1, Tq, Hq, d))
+    counts = rng.integers(1, 5, size=60)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = -v[None, None, :] + 0.1 * rng.standard_normal((N, Hkv, d))
+    Qr_b, Kb_b = oracle.f64_to_bf16_bits(Qr), oracle.f64_to_bf16_bits(Kb)
+    ids, sc, ch, dc = _run_route(torch_mod, msa, ctx128, Qr_b, Kb_b, coff, k, "bf16")
+    c_ref = oracle.chunk_scores(W.widen(Qr_b, "bf16"), W.widen(Kb_b, "bf16"))
+    assert c_ref.max() < -0.5
+    tol = _score_tol("bf16", d, 1, Tq)
+    assert np.max(np.abs(ch - c_ref)) <= tol
+    D_ref = oracle.doc_scores(c_ref, coff)
+    assert np.max(np.abs(dc - D_ref)) <= tol
+    _check_valid_topk(ids[0], sc[0], D_ref[0], tol)
+
+
+@pytest.mark.parametrize("B,Tq", [(1, 1), (2, 1), (1, 16), (32, 1), (1, 256), (1, 200), (2, 77)])
 def test_route_planted_exact_set(torch_mod, msa, ctx128, B, Tq):
     Hq, Hkv, d, k = 32, 8, 128, 16
     n_docs = max(500, 20 * B * k)
