@@ -208,7 +208,7 @@ class Runner:
                                                                         args.local))
         self.ids_host = torch.empty((L, 1, k), dtype=torch.int32, pin_memory=True)
         self.ids_dev = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
-        self.ws_gather = msa.workspace(msa.msa_gather_device_workspace_size(1, k))
+        self.ws_gather = msa.workspace(msa.msa_gather_device_workspace_size(1, k, self.cap))
         self.ids_np = [self.ids_host[l].numpy() for l in range(L)]
         self.KVmem = torch.empty((L, self.cap, 2, Hkv, D), dtype=torch.bfloat16, device=dev)
         self.mo_host = torch.zeros((L, 2), dtype=torch.int64, pin_memory=True)
@@ -458,7 +458,7 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
     max_rows = int(np.sort(np.diff(coff))[-k:].sum())
     KVmem = torch.empty((cap, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
     mo = torch.zeros((Lr, B + 1), dtype=torch.int64, device="cuda")
-    ws_g = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    ws_g = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
     ws_a = msa.workspace(msa.msa_sparse_attn_workspace_size(1, B, 1, Hq, Hkv, max_rows, L))
     O = torch.empty((Lr, B, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
     host = [PinnedHost(N * ROW_KV) for _ in range(Lr)]

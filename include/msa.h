@@ -316,13 +316,15 @@ msa_status msa_gather(const void* host_KVbar, size_t row_bytes, int64_t n_rows_h
  *   doc_chunk_off  device int64[n_docs+1].
  *   ids            device int32[B][top_k] (e.g. msa_route's out_ids).
  *   mem_off        device int64[B+1] output.
- *   workspace      device, >= msa_gather_device_workspace_size(B, top_k).
+ *   workspace      device, >= msa_gather_device_workspace_size(B, top_k,
+ *                  cap_rows): the copy plan and one source-row index per
+ *                  destination row.
  * B in [1, 1024].  Device-side data are not validated synchronously: an id
  * outside [0, n_docs), or a document whose rows fall outside the host
  * store, contributes no rows; rows beyond cap_rows are dropped (mem_off is
  * clamped to cap_rows).  Every access stays in bounds.
  */
-size_t msa_gather_device_workspace_size(int64_t B, int top_k);
+size_t msa_gather_device_workspace_size(int64_t B, int top_k, int64_t cap_rows);
 
 msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_bytes,
                              int64_t n_rows_host, const int64_t* doc_chunk_off, int64_t n_docs,

@@ -61,7 +61,7 @@ _SIGS = {
     "msa_route_bwd_workspace_size": (SZ, [I64, I32, I32, I32, I64, I64]),
     "msa_route_bwd": (I32, [P, I32, P, I64, I32, I32, P, I64, I32, P, I64, P, P, P, P, P, SZ, P]),
     "msa_gather": (I32, [P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, P, P]),
-    "msa_gather_device_workspace_size": (SZ, [I64, I32]),
+    "msa_gather_device_workspace_size": (SZ, [I64, I32, I64]),
     "msa_gather_device": (I32, [P, P, SZ, I64, P, I64, P, I64, I32, P, I64, P, P, SZ, P]),
     "msa_sparse_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32, P,
@@ -264,8 +264,8 @@ def msa_gather(host_KVbar, row_bytes, n_rows_host, doc_chunk_off_host, ids_host,
                             _ptr(mem_off_dev), _stream(side), done))
 
 
-def msa_gather_device_workspace_size(B, top_k):
-    return lib().msa_gather_device_workspace_size(B, top_k)
+def msa_gather_device_workspace_size(B, top_k, cap_rows):
+    return lib().msa_gather_device_workspace_size(B, top_k, cap_rows)
 
 
 def msa_gather_device(ctx, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, ids, dst_KVmem, cap_rows,

@@ -497,9 +497,9 @@ msa_status msa_gather(const void* host_KVbar, size_t row_bytes, int64_t n_rows_h
     return ok();
 }
 
-size_t msa_gather_device_workspace_size(int64_t B, int top_k) {
-    if (B < 1 || top_k < 1) return 0;
-    return msa::gather_device_workspace(B);
+size_t msa_gather_device_workspace_size(int64_t B, int top_k, int64_t cap_rows) {
+    if (B < 1 || top_k < 1 || cap_rows < 0) return 0;
+    return msa::gather_device_workspace(B, cap_rows);
 }
 
 msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_bytes, int64_t n_rows_host,
@@ -525,7 +525,7 @@ msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_by
         (void)hipGetLastError();
         return fail(MSA_ERR_INVALID_ARG, "%s: host store is not pinned host memory (use hipHostMalloc)", fn);
     }
-    const size_t need = msa::gather_device_workspace(B);
+    const size_t need = msa::gather_device_workspace(B, cap_rows);
     if (!workspace || !aligned256(workspace) || ws_bytes < need)
         return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
                     ws_bytes);

@@ -9,10 +9,14 @@
 //
 // The layout is the one msa_gather produces (ids of a query in ascending
 // order, rows back to back, mem_off prefix sums), but nothing goes through
-// the host: gather_plan turns the device-resident ids into (source row,
-// destination row, rows) triples, and gather_copy reads the host rows over
-// PCIe with 16-byte loads (pinned host memory is mapped into the GPU's
-// address space) and writes them to HBM.  For a single query, gather_one
+// the host: gather_plan turns the device-resident ids into mem_off and a
+// table holding, for every destination row, its source row in the host
+// store; gather_copy then reads the host rows over PCIe with 16-byte loads
+// (pinned host memory is mapped into the GPU's address space) and writes them
+// to HBM.  gather_copy runs on a fixed grid of kCopyWgs workgroups, each with
+// kCopyRows rows (32 KB) in flight, which keeps PCIe busy (about 2 MB in
+// flight in all) while most CUs stay free for other work, e.g. attention over
+// rows gathered earlier, on another stream.  For a single query, gather_one
 // does both in one launch: every workgroup sorts the query's K ids and scans
 // their row counts itself (a few hundred bytes) and then copies its share.
 // No host synchronisation is needed between routing and attention.
@@ -37,7 +41,8 @@ __device__ __forceinline__ int64_t wave_excl_scan(int64_t v, int lane) {
 
 __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
     const int32_t* __restrict__ ids, int B, int K, const int64_t* __restrict__ off, int64_t n_docs,
-    int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off, int64_t* __restrict__ plan) {
+    int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off, int64_t* __restrict__ plan,
+    int64_t* __restrict__ src_of_row) {
     __shared__ int64_t totals[kMaxGatherB + 1];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     // phase 1: per query, sorted ids, row counts, local prefix
@@ -84,33 +89,57 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
         mem_off[B] = acc < cap ? acc : cap;
     }
     __syncthreads();
-    // phase 3: absolute destination rows, clamped to the buffer
+    // phase 3: absolute destination rows, clamped to the buffer, and the
+    // source row of every destination row
     for (int b = wave; b < B; b += kPlanWaves) {
         int64_t* pb = plan + (int64_t(b) * 64 + lane) * 3;
+        const int64_t src = pb[0];
         int64_t dst = pb[1] + totals[b];
         int64_t rows = pb[2];
         if (dst >= cap) rows = 0;
         else if (dst + rows > cap) rows = cap - dst;
         pb[1] = dst;
         pb[2] = rows;
+        for (int e = 0; e < K; ++e) {
+            const int64_t s_e = __shfl(src, e), d_e = __shfl(dst, e), n_e = __shfl(rows, e);
+            for (int64_t r = lane; r < n_e; r += kWave) src_of_row[d_e + r] = s_e + r;
+        }
     }
 }
 
-// grid (B * 64 plan entries, kCopySplit); workgroup y copies rows y, y + kCopySplit, ...
-constexpr int kCopySplit = 8;
+// Destination rows are dealt to the kCopyWgs workgroups kCopyRows at a
+// time (rows w * kCopyRows + j, then + kCopyWgs * kCopyRows, ...); a thread
+// copies one 16-byte unit of each of its workgroup's kCopyRows rows, all
+// loads issued before the stores.
+constexpr int kCopyWgs = 64;
+constexpr int kCopyRows = 8;
 
 __global__ __launch_bounds__(256) void gather_copy_kernel(const u32x4* __restrict__ host, int64_t row_vecs,
-                                                          const int64_t* __restrict__ plan, int K,
+                                                          const int64_t* __restrict__ src_of_row,
+                                                          const int64_t* __restrict__ mem_off, int B,
                                                           u32x4* __restrict__ dst) {
-    const int64_t e = blockIdx.x;
-    if (int(e % 64) >= K) return;
-    const int64_t src_row = plan[e * 3], dst_row = plan[e * 3 + 1], rows = plan[e * 3 + 2];
-    for (int64_t r = blockIdx.y; r < rows; r += kCopySplit) {
-        const u32x4* s = host + (src_row + r) * row_vecs;
-        u32x4* d = dst + (dst_row + r) * row_vecs;
-        for (int64_t v = threadIdx.x; v < row_vecs; v += 256) d[v] = s[v];
+    const int64_t total = mem_off[B];
+    for (int64_t r0 = int64_t(blockIdx.x) * kCopyRows; r0 < total; r0 += int64_t(kCopyWgs) * kCopyRows) {
+        int64_t src[kCopyRows];
+#pragma unroll
+        for (int j = 0; j < kCopyRows; ++j) src[j] = (r0 + j < total) ? src_of_row[r0 + j] : -1;
+        for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
+            const int64_t v = v0 + threadIdx.x;
+            if (v >= row_vecs) break;
+            u32x4 x[kCopyRows];
+#pragma unroll
+            for (int j = 0; j < kCopyRows; ++j)
+                if (src[j] >= 0) x[j] = host[src[j] * row_vecs + v];
+#pragma unroll
+            for (int j = 0; j < kCopyRows; ++j)
+                if (src[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
+        }
     }
 }
+
+// grid (K plan entries, kCopySplit) of gather_one: workgroup y copies rows
+// y, y + kCopySplit, ... of its entry
+constexpr int kCopySplit = 8;
 
 // One query: workgroup (e, y) copies rows y, y + kCopySplit, ... of the
 // document in sorted position e; every wave of it derives (source row,
@@ -163,7 +192,9 @@ __global__ __launch_bounds__(256) void gather_one_kernel(const u32x4* __restrict
 
 }  // namespace
 
-size_t gather_device_workspace(int64_t B) { return align256(size_t(B) * 64 * 3 * sizeof(int64_t)); }
+size_t gather_device_workspace(int64_t B, int64_t cap_rows) {
+    return align256(size_t(B) * 64 * 3 * sizeof(int64_t)) + align256(size_t(cap_rows) * sizeof(int64_t));
+}
 
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
                                 int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
@@ -175,13 +206,13 @@ hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_ro
         return hipGetLastError();
     }
     int64_t* plan = static_cast<int64_t*>(ws);
+    int64_t* src_of_row = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + align256(size_t(B) * 64 * 3 * 8));
     hipLaunchKernelGGL(gather_plan_kernel, dim3(1), dim3(kPlanWaves * 64), 0, st, ids, int(B), K, off, n_docs,
-                       n_rows_host, cap_rows, mem_off, plan);
+                       n_rows_host, cap_rows, mem_off, plan, src_of_row);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(gather_copy_kernel, dim3(unsigned(B * 64), kCopySplit), dim3(256), 0, st,
-                       static_cast<const u32x4*>(host), int64_t(row_bytes / 16), plan, K,
-                       static_cast<u32x4*>(dst));
+    hipLaunchKernelGGL(gather_copy_kernel, dim3(kCopyWgs), dim3(256), 0, st, static_cast<const u32x4*>(host),
+                       int64_t(row_bytes / 16), src_of_row, mem_off, int(B), static_cast<u32x4*>(dst));
     return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ size_t attn_bwd_workspace(int64_t B, int Tq, int Hq, int Hkv, int64_t max_rows, 
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
 constexpr int kMaxGatherB = 1024;
-size_t gather_device_workspace(int64_t B);
+size_t gather_device_workspace(int64_t B, int64_t cap_rows);
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
                                 int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
                                 int64_t cap_rows, int64_t* mem_off, void* ws, hipStream_t st);

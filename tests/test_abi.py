@@ -139,5 +139,5 @@ def test_library_loads_next_to_torchs_hip_runtime():
 def test_gather_device_validates_before_launch():
     L = msa.lib()
     assert L.msa_gather_device(None, 1, 64, 4, 1, 2, 1, 1, 1, 1, 8, 1, 1, 256, None) == 1   # ctx NULL
-    assert msa.msa_gather_device_workspace_size(0, 4) == 0
-    assert msa.msa_gather_device_workspace_size(3, 16) >= 3 * 64 * 3 * 8
+    assert msa.msa_gather_device_workspace_size(0, 4, 100) == 0
+    assert msa.msa_gather_device_workspace_size(3, 16, 1000) >= 3 * 64 * 3 * 8 + 1000 * 8

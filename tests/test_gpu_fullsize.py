@@ -170,7 +170,7 @@ def test_chunk_level_topk_100m_layer(env):
     torch.cuda.current_stream().wait_stream(side)
     dst2 = torch.empty_like(dst)
     mo2 = torch.zeros(2, dtype=torch.int64, device="cuda")
-    wsg = msa.workspace(msa.msa_gather_device_workspace_size(1, k))
+    wsg = msa.workspace(msa.msa_gather_device_workspace_size(1, k, k))
     msa.msa_gather_device(ctx, host, 2 * Hkv * D * 2, N, coff_d, ids, dst2, k, mo2, wsg)
     torch.cuda.synchronize()
     rows = np.concatenate([msa_synth.counter_bf16(seed, W.kvbar_stream(0), int(r) * 2 * Hkv * D, 2 * Hkv * D)
@@ -226,7 +226,7 @@ def test_batch32_10m_layer_full_oracle(env):
     cap = B * max_rows
     dst = torch.empty((cap, 2, Hkv, D), dtype=torch.bfloat16, device="cuda")
     mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
-    wsg = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    wsg = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
     msa.msa_gather_device(ctx, host, 2 * Hkv * D * 2, N, coff_dev, ids, dst, cap, mo, wsg)
     Qh = msa_synth.normal_bf16(seed, 900, (B, 1, Hq, D))
     Kl = torch.empty((B, L, Hkv, D), dtype=torch.bfloat16, device="cuda")

@@ -752,7 +752,7 @@ def test_gather_device_matches_oracle_and_host_gather(torch_mod, msa, ctx128):
     coff_dev = torch.from_numpy(coff).cuda()
     dst = torch.zeros((cap, 2, Hkv, d), dtype=torch.bfloat16, device="cuda")
     mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
-    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
     msa.msa_gather_device(ctx128, host, row_bytes, N, coff_dev, torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
     # the host-side gather of the same ids gives the same bytes and offsets
     dst2 = torch.zeros_like(dst)
@@ -805,7 +805,7 @@ def test_gather_random_layouts(torch_mod, msa, ctx128, row_elems, n_docs, maxc, 
     row_bytes = row_elems * 2
     dst = torch.zeros((cap, row_elems), dtype=torch.bfloat16, device="cuda")
     mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
-    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k))
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
     msa.msa_gather_device(ctx128, host, row_bytes, N, torch.from_numpy(coff).cuda(),
                           torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
     dst2 = torch.zeros_like(dst)
@@ -835,7 +835,7 @@ def test_gather_device_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, 
     cap = 8
     dst = torch.zeros((cap, 64), dtype=torch.bfloat16, device="cuda")
     mo = torch.zeros(3, dtype=torch.int64, device="cuda")
-    ws = msa.workspace(msa.msa_gather_device_workspace_size(2, 3))
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(2, 3, cap))
     msa.msa_gather_device(ctx128, host, 128, 10, torch.from_numpy(coff).cuda(), ids, dst, cap, mo, ws)
     torch.cuda.synchronize()
     # query 0: docs 0 (3 rows) and 2 (4 rows) -> 7 rows; query 1: docs 1, 3 -> clamped to 1 row
