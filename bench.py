@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -269,6 +270,25 @@ class Runner:
                                 wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
 
 
+def host_cpu_model():
+    """The host CPU's model name as lscpu reports it (or /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True,
+                             timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, wl, W, msa_synth):
     """The oracle, untuned, on a bounded sample of the same workload: the
     routing of the first few routing layers over their chunk rows
@@ -313,7 +333,8 @@ def cpu_baseline(args, wl, W, msa_synth):
         t_attn += time.perf_counter() - t0
     t_step = wl["L"] / n_layers * (t_route * N / S + t_attn)
     gb = wl["L"] * N * ROW_KR / 1e9
-    return {"value": gb / t_step, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": gb / t_step, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": host_cpu_model(),
+            "host_cpus": os.cpu_count(),
             "sample": f"routing of layers 0..{n_layers - 1} over {S} of {N} chunk rows ({n_docs_s} documents) "
                       f"+ their attention ({mem_rows} memory rows + {args.local} local), "
                       f"scaled x{N / S:.2f} (rows) and x{wl['L'] / n_layers:.1f} (layers); "
