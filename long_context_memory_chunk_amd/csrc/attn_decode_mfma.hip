@@ -166,6 +166,15 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
         return (M > kb) ? (M - kb + 3) / 4 : int64_t(0);
     };
     auto load_k = [&](int64_t k0) {
+        // the RoPE seed first: an address it needs may have to come back from
+        // scratch, and that wait then does not cover this block's K loads
+        if (k0 + 31 >= M) {                        // the block holds local keys
+            int64_t pos = int64_t(q_offset) + k0 + slot + 4 * first_local(k0) - M;
+            pos = pos < 0 ? 0 : (pos < max_pos ? pos : max_pos - 1);
+            const float2* cs = rope_cs + pos * (DH / 2) + 4 * c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) seed[j] = cs[j];
+        }
         if (k0 + 31 < M || (k0 >= M && k0 + 31 < total)) {
             const bool mem = k0 + 31 < M;
             const int64_t stride = mem ? mem_stride : loc_stride;
@@ -184,13 +193,6 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
                 kw[it][0] = *reinterpret_cast<const u32x2*>(rb);
                 kw[it][1] = *reinterpret_cast<const u32x2*>(rb + DH);
             }
-        }
-        if (k0 + 31 >= M) {                        // the block holds local keys
-            int64_t pos = int64_t(q_offset) + k0 + slot + 4 * first_local(k0) - M;
-            pos = pos < 0 ? 0 : (pos < max_pos ? pos : max_pos - 1);
-            const float2* cs = rope_cs + pos * (DH / 2) + 4 * c;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) seed[j] = cs[j];
         }
     };
     // V rows 2 slot + 8 m + q (it = 2m + q): lane c holds dimensions 8c .. 8c+7

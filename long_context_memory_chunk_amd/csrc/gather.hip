@@ -45,8 +45,12 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
     int64_t* __restrict__ src_of_row) {
     __shared__ int64_t totals[kMaxGatherB + 1];
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    // a wave's first kRegIters queries keep their plan entries in registers
+    // between the phases; later ones (B > 64) go through the plan array
+    constexpr int kRegIters = 4;
+    int64_t r_src[kRegIters], r_local[kRegIters], r_rows[kRegIters];
     // phase 1: per query, sorted ids, row counts, local prefix
-    for (int b = wave; b < B; b += kPlanWaves) {
+    for (int it = 0, b = wave; b < B; ++it, b += kPlanWaves) {
         int32_t id = (lane < K) ? ids[int64_t(b) * K + lane] : 0x7FFFFFFF;
         if (id < 0 || id >= n_docs) id = 0x7FFFFFFF;          // invalid ids copy nothing
         // bitonic sort, ascending across lanes
@@ -69,10 +73,16 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
             else src = 0;
         }
         const int64_t local = wave_excl_scan(rows, lane);
-        int64_t* pb = plan + (int64_t(b) * 64 + lane) * 3;
-        pb[0] = src;
-        pb[1] = local;
-        pb[2] = rows;
+        if (it < kRegIters) {
+#pragma unroll
+            for (int u = 0; u < kRegIters; ++u)
+                if (u == it) { r_src[u] = src; r_local[u] = local; r_rows[u] = rows; }
+        } else {
+            int64_t* pb = plan + (int64_t(b) * 64 + lane) * 3;
+            pb[0] = src;
+            pb[1] = local;
+            pb[2] = rows;
+        }
         const int64_t tot = __shfl(local + rows, 63);
         if (lane == 0) totals[b] = tot;
     }
@@ -91,15 +101,21 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
     __syncthreads();
     // phase 3: absolute destination rows, clamped to the buffer, and the
     // source row of every destination row
-    for (int b = wave; b < B; b += kPlanWaves) {
-        int64_t* pb = plan + (int64_t(b) * 64 + lane) * 3;
-        const int64_t src = pb[0];
-        int64_t dst = pb[1] + totals[b];
-        int64_t rows = pb[2];
+    for (int it = 0, b = wave; b < B; ++it, b += kPlanWaves) {
+        int64_t src = 0, local = 0, rows = 0;
+        if (it < kRegIters) {
+#pragma unroll
+            for (int u = 0; u < kRegIters; ++u)
+                if (u == it) { src = r_src[u]; local = r_local[u]; rows = r_rows[u]; }
+        } else {
+            const int64_t* pb = plan + (int64_t(b) * 64 + lane) * 3;
+            src = pb[0];
+            local = pb[1];
+            rows = pb[2];
+        }
+        const int64_t dst = local + totals[b];
         if (dst >= cap) rows = 0;
         else if (dst + rows > cap) rows = cap - dst;
-        pb[1] = dst;
-        pb[2] = rows;
         for (int e = 0; e < K; ++e) {
             const int64_t s_e = __shfl(src, e), d_e = __shfl(dst, e), n_e = __shfl(rows, e);
             for (int64_t r = lane; r < n_e; r += kWave) src_of_row[d_e + r] = s_e + r;
