@@ -28,6 +28,14 @@ namespace {
 
 constexpr int kPlanWaves = 16;
 
+// Lane `src` of a 64-bit value, for a wave-uniform lane index (two scalar
+// reads instead of two LDS permutes).
+__device__ __forceinline__ int64_t lane64(int64_t v, int src) {
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), src));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v) >> 32)), src));
+    return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t wave_excl_scan(int64_t v, int lane) {
     // inclusive Hillis-Steele scan over 64 lanes, then shift to exclusive
     int64_t x = v;
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
             pb[1] = local;
             pb[2] = rows;
         }
-        const int64_t tot = __shfl(local + rows, 63);
+        const int64_t tot = lane64(local + rows, 63);
         if (lane == 0) totals[b] = tot;
     }
     __syncthreads();
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
         if (dst >= cap) rows = 0;
         else if (dst + rows > cap) rows = cap - dst;
         for (int e = 0; e < K; ++e) {
-            const int64_t s_e = __shfl(src, e), d_e = __shfl(dst, e), n_e = __shfl(rows, e);
+            const int64_t s_e = lane64(src, e), d_e = lane64(dst, e), n_e = lane64(rows, e);
             for (int64_t r = lane; r < n_e; r += kWave) src_of_row[d_e + r] = s_e + r;
         }
     }
@@ -153,21 +161,21 @@ __global__ __launch_bounds__(256) void gather_copy_kernel(const u32x4* __restric
     }
 }
 
-// grid (K plan entries, kCopySplit) of gather_one: workgroup y copies rows
-// y, y + kCopySplit, ... of its entry
-constexpr int kCopySplit = 8;
+// gather_one: workgroup w copies destination rows w * kOneRows .. + kOneRows
+// - 1 (all of them in flight together), so every selected row is requested at
+// once whatever the document sizes.  Each wave derives the plan on its own
+// (wave-uniform results, no barrier): the K ids sorted, their row counts and
+// prefix sums; a destination row's entry is the last one starting at or
+// before it (a ballot).  Workgroup 0 also writes mem_off.
+constexpr int kOneRows = 2;
+constexpr int64_t kOneMaxRows = 8192;   // larger capacities take the plan + bounded copy path
 
-// One query: workgroup (e, y) copies rows y, y + kCopySplit, ... of the
-// document in sorted position e; every wave of it derives (source row,
-// destination row, rows) from the ids on its own (wave-uniform results), so
-// the workgroup needs no barrier; workgroup (0, 0) also writes mem_off.
 __global__ __launch_bounds__(256) void gather_one_kernel(const u32x4* __restrict__ host, int64_t row_vecs,
                                                          const int32_t* __restrict__ ids, int K,
                                                          const int64_t* __restrict__ off, int64_t n_docs,
                                                          int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
                                                          u32x4* __restrict__ dst) {
     const int lane = threadIdx.x % kWave;
-    const int e = blockIdx.x;
     int32_t id = (lane < K) ? ids[lane] : 0x7FFFFFFF;
     if (id < 0 || id >= n_docs) id = 0x7FFFFFFF;          // invalid ids copy nothing
 #pragma unroll
@@ -189,20 +197,35 @@ __global__ __launch_bounds__(256) void gather_one_kernel(const u32x4* __restrict
         else src = 0;
     }
     const int64_t dst0 = wave_excl_scan(rows, lane);
-    const int64_t total = __shfl(dst0 + rows, 63);
-    if (e == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int64_t total = lane64(dst0 + rows, 63);
+    total = total < cap ? total : cap;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         mem_off[0] = 0;
-        mem_off[1] = total < cap ? total : cap;
+        mem_off[1] = total;
     }
-    // this workgroup's entry, clamped to the buffer
-    const int64_t my_src = __shfl(src, e), my_dst = __shfl(dst0, e);
-    int64_t my_rows = __shfl(rows, e);
-    if (my_dst >= cap) my_rows = 0;
-    else if (my_dst + my_rows > cap) my_rows = cap - my_dst;
-    for (int64_t r = blockIdx.y; r < my_rows; r += kCopySplit) {
-        const u32x4* sp = host + (my_src + r) * row_vecs;
-        u32x4* dp = dst + (my_dst + r) * row_vecs;
-        for (int64_t v = threadIdx.x; v < row_vecs; v += 256) dp[v] = sp[v];
+    const int64_t r0 = int64_t(blockIdx.x) * kOneRows;
+    int64_t sr[kOneRows];
+#pragma unroll
+    for (int j = 0; j < kOneRows; ++j) {
+        const int64_t r = r0 + j;
+        sr[j] = -1;
+        if (r < total) {
+            // the entry holding destination row r: the last lane with rows and dst0 <= r
+            const uint64_t m = __ballot(rows > 0 && dst0 <= r);
+            const int e = 63 - __builtin_clzll(m);
+            sr[j] = lane64(src, e) + (r - lane64(dst0, e));
+        }
+    }
+    for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
+        const int64_t v = v0 + threadIdx.x;
+        if (v >= row_vecs) break;
+        u32x4 x[kOneRows];
+#pragma unroll
+        for (int j = 0; j < kOneRows; ++j)
+            if (sr[j] >= 0) x[j] = host[sr[j] * row_vecs + v];
+#pragma unroll
+        for (int j = 0; j < kOneRows; ++j)
+            if (sr[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
     }
 }
 
@@ -215,8 +238,9 @@ size_t gather_device_workspace(int64_t B, int64_t cap_rows) {
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
                                 int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
                                 int64_t cap_rows, int64_t* mem_off, void* ws, hipStream_t st) {
-    if (B == 1) {
-        hipLaunchKernelGGL(gather_one_kernel, dim3(unsigned(K), kCopySplit), dim3(256), 0, st,
+    if (B == 1 && cap_rows <= kOneMaxRows) {
+        const int64_t wgs = ceil_div(cap_rows, int64_t(kOneRows));
+        hipLaunchKernelGGL(gather_one_kernel, dim3(unsigned(wgs > 0 ? wgs : 1)), dim3(256), 0, st,
                            static_cast<const u32x4*>(host), int64_t(row_bytes / 16), ids, K, off, n_docs,
                            n_rows_host, cap_rows, mem_off, static_cast<u32x4*>(dst));
         return hipGetLastError();

@@ -123,7 +123,7 @@ __device__ __forceinline__ float unorder32(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Wave w of query b owns documents [256 w, 256 w + 256).  It stages their
+// Wave w of query b owns documents [128 w, 128 w + 128).  It stages their
 // chunk offsets in LDS, streams the chunk scores of their span with
 // coalesced loads, finds each chunk's document and takes an LDS atomic max on
 // the order-preserving bits (max is exact and order-independent, so the result
@@ -135,7 +135,7 @@ __device__ __forceinline__ float unorder32(uint32_t o) {
 // lane mask, plus the marks of earlier windows) minus one.  A wave whose span
 // exceeds the bit array, or that holds an empty document (two documents would
 // share one mark), finds documents by binary search in the offsets instead.
-constexpr int kDocsPerWave = 256;
+constexpr int kDocsPerWave = 128;
 constexpr int kBitWords = 1024;                  // marks for spans of up to 32768 chunks per wave
 
 __global__ __launch_bounds__(256) void topk_partial_kernel(
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const int nq = s_nq < MSA_MAX_TOPK ? s_nq : MSA_MAX_TOPK;
 
     // (c) their document keys, one batch of loads per thread: entry e of the
-    // nq * 256 documents is thread e % 1024's load e / 1024
+    // nq * 128 documents is thread e % 1024's load e / 1024
     {
         uint32_t o[kDocsPerThread];
 #pragma unroll
