@@ -225,15 +225,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_prefill_kernel(
     const u32x4* kg = Kc + bg * (KP / BK) * kTileUnits;
     const u32x4* vg = Vt + bg * (KP / BK) * kTileUnits;
     const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t voff = uint32_t(lane) * 16u;
     auto dma = [&](int t) {
         const uint32_t slot = uint32_t(t % kStages) * kTileUnits;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int piece = (i * kWaves + wave) * kWave;
-            lds_copy16(kg + int64_t(t) * kTileUnits + piece + lane,
-                       __builtin_amdgcn_readfirstlane(ldsK + (slot + piece) * 16));
-            lds_copy16(vg + int64_t(t) * kTileUnits + piece + lane,
-                       __builtin_amdgcn_readfirstlane(ldsV + (slot + piece) * 16));
+            const int piece = (i * kWaves + wave_u) * kWave;
+            lds_copy16_s(kg + int64_t(t) * kTileUnits + piece, voff, ldsK + (slot + piece) * 16);
+            lds_copy16_s(vg + int64_t(t) * kTileUnits + piece, voff, ldsV + (slot + piece) * 16);
         }
     };
     constexpr int kCopies = 4;                       // copies per wave per tile

@@ -23,6 +23,15 @@ __device__ __forceinline__ void lds_copy16(const u32x4* src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 
+// The same copy addressed as a wave-uniform base plus a per-lane 32-bit byte
+// offset: lane i reads base + voff_i.  The base and the LDS address are scalar,
+// so a loop of copies needs no vector address arithmetic between the
+// matrix-core instructions it is interleaved with.
+__device__ __forceinline__ void lds_copy16_s(const u32x4* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
 }  // namespace msa
 
 // s_waitcnt with only the vector-memory count limited (expcnt and lgkmcnt left

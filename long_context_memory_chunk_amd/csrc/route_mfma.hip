@@ -383,17 +383,20 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
     const u32x4* Bg = Kp + ct * int64_t(S) * kUnitsPerStage;
     const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
 
-    // one stage = 2 x 16 KB; a wave copies 4 + 4 contiguous 1 KB pieces (8 copies)
+    // one stage = 2 x 16 KB; a wave copies 4 + 4 contiguous 1 KB pieces (8 copies),
+    // addressed as scalar bases plus the lane's 16-byte offset
     constexpr int kCopies = 8;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t voff = uint32_t(lane) * 16u;
     auto dma = [&](int st) {
         const u32x4* a = Ag + int64_t(st) * kUnitsPerStage;
         const u32x4* b = Bg + int64_t(st) * kUnitsPerStage;
         const uint32_t buf = uint32_t(st % kStages) * kUnitsPerStage;
 #pragma unroll
         for (int i = 0; i < kCopies / 2; ++i) {
-            const int piece = (i * 4 + wave) * kWave;
-            lds_copy16(a + piece + lane, __builtin_amdgcn_readfirstlane(ldsA + (buf + piece) * 16));
-            lds_copy16(b + piece + lane, __builtin_amdgcn_readfirstlane(ldsB + (buf + piece) * 16));
+            const int piece = (i * 4 + wave_u) * kWave;
+            lds_copy16_s(a + piece, voff, ldsA + (buf + piece) * 16);
+            lds_copy16_s(b + piece, voff, ldsB + (buf + piece) * 16);
         }
     };
 
@@ -417,51 +420,81 @@ __global__ __launch_bounds__(256, 1) void route_gemm_kernel(const u32x4* __restr
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    // Software pipeline over the 16-deep k-steps (two per stage), operands of
-    // one k-step ahead in registers (F0 / F1).  Stage st:
-    //   k-step (st, 0) from F0, while (st, 1) is read into F1 (buffer st);
+    // Software pipeline, one stage (two 16-deep k-steps) of operands ahead in
+    // registers.  Stage st:
     //   wait for stage st + 1's copies (only stage st + 2's may remain in
     //   flight), barrier;
-    //   k-step (st, 1) from F1, while (st + 1, 0) is read into F0 and stage
-    //   st + 3 is copied into the buffer of stage st - 1, last read during
-    //   k-step (st - 1, 0), before the previous barrier.
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
-    auto read_ks = [&](int st, int ks, bf16x8* xa, bf16x8* xb) {
-        const u32x4* cA = sA + (st % kStages) * kUnitsPerStage;
-        const u32x4* cB = sB + (st % kStages) * kUnitsPerStage;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            xa[a] = __builtin_bit_cast(bf16x8, cA[offA[a] + ((2 * ks) ^ sw[a])]);
-            xb[a] = __builtin_bit_cast(bf16x8, cB[offB[a] + ((2 * ks) ^ sw[4 + a])]);
-        }
+    //   copy stage st + 3 into the buffer of stage st - 1, whose operands every
+    //   wave read into registers during stage st - 2 and consumed in stage
+    //   st - 1, before this barrier;
+    //   read stage st + 1's operands into the other register set while the
+    //   matrix cores run stage st's 32 products, so a read has a whole stage
+    //   to complete.
+    // Operand sets P and Q alternate between stages: [k-step][32-row tile].
+    bf16x8 pa[2][4], pb[2][4], qa[2][4], qb[2][4];
+    constexpr int kReadFrom[9] = {0, 3, 6, 9, 12, 14, 16, 16, 16};
+    // copy j (0..7) of stage st: piece j / 2 of operand A (j even) or B (j odd)
+    auto dma_one = [&](int st, int j) {
+        const int piece = ((j >> 1) * 4 + wave_u) * kWave;
+        const uint32_t buf = uint32_t(st % kStages) * kUnitsPerStage;
+        if (j & 1) lds_copy16_s(Bg + int64_t(st) * kUnitsPerStage + piece, voff, ldsB + (buf + piece) * 16);
+        else lds_copy16_s(Ag + int64_t(st) * kUnitsPerStage + piece, voff, ldsA + (buf + piece) * 16);
     };
-    auto mma_half = [&](const bf16x8* xa, const bf16x8* xb, int a0_) {
-#pragma unroll
-        for (int a = a0_; a < a0_ + 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[a], xb[b], acc[a][b], 0, 0, 0);
-    };
-
-    for (int st = 0; st < kStages - 1 && st < S; ++st) dma(st);
-    if (S > 2) MSA_WAIT_VMCNT(2 * kCopies); else if (S > 1) MSA_WAIT_VMCNT(kCopies); else MSA_WAIT_VMCNT(0);
-    __syncthreads();
-    read_ks(0, 0, a0, b0);
-
-    for (int st = 0; st < S; ++st) {
-        const bool more = st + 1 < S;
-        mma_half(a0, b0, 0);
-        read_ks(st, 1, a1, b1);
-        mma_half(a0, b0, 2);
-        if (more) {
-            if (st + 2 < S) MSA_WAIT_VMCNT(kCopies); else MSA_WAIT_VMCNT(0);
-            __syncthreads();
-        }
-        mma_half(a1, b1, 0);
-        if (more) read_ks(st + 1, 0, a0, b0);
-        if (st + kStages - 1 < S) dma(st + kStages - 1);
-        mma_half(a1, b1, 2);
+// Read r (0..15) of stage st's operands: k-step r / 8, tile (r / 2) % 4, A or B.
+#define MSA_GEMM_READ_ONE(st_, r_, RA, RB)                                                 \
+    {                                                                                      \
+        const int ks_ = (r_) / 8, t_ = ((r_) / 2) % 4;                                     \
+        if ((r_) & 1)                                                                      \
+            RB[ks_][t_] = __builtin_bit_cast(bf16x8, sB[((st_) % kStages) * kUnitsPerStage + offB[t_] + ((2 * ks_) ^ sw[4 + t_])]); \
+        else                                                                               \
+            RA[ks_][t_] = __builtin_bit_cast(bf16x8, sA[((st_) % kStages) * kUnitsPerStage + offA[t_] + ((2 * ks_) ^ sw[t_])]);     \
     }
+// One stage: wait until at most WAITN copies are in flight (stage s + 1
+// resident), barrier; then eight groups of four of stage s's products from
+// (CA, CB), each followed by one copy of stage s + 3 (DO_DMA) and some of the
+// 16 operand reads of stage s + 1 into (NA, NB) (DO_READ: 3, 3, 3, 3, 2, 2 in
+// the first six groups, so the last reads have two groups of products to land
+// before the next barrier waits for them).  Spreading the copies and
+// reads over the stage keeps every wave's in-order issue moving: issued all at
+// once after the barrier, the four waves' 32 copies queue at the CU's address
+// unit and hold back the products behind them.  The scheduling barriers keep
+// that order.
+#define MSA_GEMM_STEP(st_, CA, CB, NA, NB, WAITN, DO_DMA, DO_READ)                          \
+    {                                                                                      \
+        const int s_ = (st_);                                                              \
+        if (DO_READ) {                                                                     \
+            MSA_WAIT_VMCNT(WAITN);                                                         \
+            __syncthreads();                                                               \
+        }                                                                                  \
+        _Pragma("unroll") for (int g = 0; g < 8; ++g) {                                    \
+            _Pragma("unroll") for (int m = 4 * g; m < 4 * g + 4; ++m)                      \
+                acc[(m / 4) % 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(          \
+                    CA[m / 16][(m / 4) % 4], CB[m / 16][m % 4], acc[(m / 4) % 4][m % 4], 0, 0, 0); \
+            if (DO_DMA) dma_one(s_ + kStages - 1, g);                                      \
+            if (DO_READ)                                                                   \
+                _Pragma("unroll") for (int r = kReadFrom[g]; r < kReadFrom[g + 1]; ++r)    \
+                    MSA_GEMM_READ_ONE(s_ + 1, r, NA, NB)                                   \
+            __builtin_amdgcn_sched_barrier(0);                                             \
+        }                                                                                  \
+    }
+
+    // S = Hkv * 4 stages, a multiple of 4: stages 0 .. S - 5 in pairs with every
+    // step whole, then the last four peeled (the copies run out three stages
+    // before the products do).
+    for (int st = 0; st < kStages - 1; ++st) dma(st);
+    MSA_WAIT_VMCNT(2 * kCopies);
+    __syncthreads();
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) MSA_GEMM_READ_ONE(0, r, pa, pb)
+    for (int st = 0; st + 4 < S; st += 2) {
+        MSA_GEMM_STEP(st, pa, pb, qa, qb, kCopies, true, true)
+        MSA_GEMM_STEP(st + 1, qa, qb, pa, pb, kCopies, true, true)
+    }
+    MSA_GEMM_STEP(S - 4, pa, pb, qa, qb, kCopies, true, true)
+    MSA_GEMM_STEP(S - 3, qa, qb, pa, pb, kCopies, false, true)
+    MSA_GEMM_STEP(S - 2, pa, pb, qa, qb, 0, false, true)
+    MSA_GEMM_STEP(S - 1, qa, qb, pa, pb, 0, false, false)
+#undef MSA_GEMM_STEP
+#undef MSA_GEMM_READ_ONE
 
     // ---- epilogue: column maxima over the tile's real tokens (one
     // accumulator column block at a time: the scheduler barrier keeps the

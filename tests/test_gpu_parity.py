@@ -291,6 +291,16 @@ def test_route_parity_random_shapes(torch_mod, msa, ctx64, ctx128, dtype, d, Hq,
     test_route_parity_random(torch_mod, msa, ctx64, ctx128, dtype, d, Hq, Hkv, B, Tq, n_docs, maxc, k)
 
 
+@pytest.mark.parametrize("Hkv,G,Tq", [(1, 4, 256), (2, 2, 512)])
+def test_route_gemm_more_tiles_than_cus(torch_mod, msa, ctx128, Hkv, G, Tq):
+    """The long-query GEMM over about 300 chunk tiles of 256 per query tile,
+    more workgroups than the chip has CUs, so tiles of one XCD's super-tile
+    run in several rounds; one KV head gives the shortest contraction (four
+    32-wide stages: the copy pipeline's prologue and its last four stages
+    with nothing in between)."""
+    test_route_parity_random(torch_mod, msa, None, ctx128, "bf16", 128, G * Hkv, Hkv, 1, Tq, 6000, 25, 16)
+
+
 @pytest.mark.parametrize("Tq", [5, 33, 100, 1100])
 def test_route_padded_rows_stay_out_of_the_token_max(torch_mod, msa, ctx128, Tq):
     """Every real score is about -0.9 (keys point against the queries), so a
