@@ -6,8 +6,8 @@ Workload (the 100M-token memory): documents with log-normal lengths
 summing to 100M tokens, pooled with chunk 64 into N = 1,562,500 rows per
 layer; 18 routing layers of K̄r [N][8][128] bf16 (57.6 GB) resident in HBM;
 pooled K̄/V̄ [N][2][8][128] bf16 of the routing layers (115.2 GB) in pinned
-host memory; 16 planted documents (the same in every layer, planted against
-each layer's own query); top-k 16; a 1-token decode query with 2,048 local
+host memory; 16 planted documents per layer (a different set in every layer,
+planted against that layer's own query); top-k 16; a 1-token decode query with 2,048 local
 tokens.  One step = for each of the 18 layers: route (scan K̄r, document
 max, top-16) -> ids to the host -> gather the 16 documents' K̄/V̄ rows from
 the host store (hipMemcpyAsync on a side stream) -> sparse GQA attention
@@ -143,11 +143,13 @@ def build_workload(args, torch, msa, msa_synth, device_fill, W, chunk_level=Fals
     Krbar = torch.empty((L, N, Hkv, D), dtype=torch.bfloat16, device=dev)
     for l in range(L):
         device_fill.fill_counter_bf16(Krbar[l], seed, W.krbar_stream(l), 0)
-    planted = msa_synth.pick_planted(seed, 60 if chunk_level else 50, n_docs, k)
+    # a different planted set in every layer, so layers that share a block of
+    # the host store (l and l + its block count) still gather different rows
+    planted = [msa_synth.pick_planted(seed, (60 if chunk_level else 50) + 1000 * l, n_docs, k) for l in range(L)]
     Qr_h = [msa_synth.normal_bf16(seed, 100 + l, (1, 1, Hq, D)) for l in range(L)]
     for l in range(L):
         q = msa_synth.bf16_bits_to_f32(Qr_h[l])[0, 0]
-        for j, d in enumerate(planted):
+        for j, d in enumerate(planted[l]):
             rows = W.planted_pooled(seed, l, q, Hkv, int(coff[d + 1] - coff[d]), tag=j)
             Krbar[l, coff[d]:coff[d + 1]].copy_(W.dev_bf16(rows))
     torch.cuda.synchronize()
@@ -311,7 +313,7 @@ def cpu_baseline(args, wl, W, msa_synth):
     for l in range(n_layers):
         Kb = W.counter_bf16_threads(seed, W.krbar_stream(l), 0, S * Hkv * D).reshape(S, Hkv, D)
         q = msa_synth.bf16_bits_to_f32(wl["Qr_h"][l])[0, 0]
-        for j, d in enumerate(wl["planted"]):
+        for j, d in enumerate(wl["planted"][l]):
             if coff[d + 1] <= S:
                 Kb[coff[d]:coff[d + 1]] = W.planted_pooled(seed, l, q, Hkv, int(coff[d + 1] - coff[d]), tag=j)
         Qr64, Kb64 = W.widen(wl["Qr_h"][l], "bf16"), W.widen(Kb, "bf16")
@@ -321,7 +323,7 @@ def cpu_baseline(args, wl, W, msa_synth):
         t_route += time.perf_counter() - t0
         del Kb64
         # attention of the layer over the planted documents' pooled rows + local context
-        sel = sorted(int(d) for d in wl["planted"])
+        sel = sorted(int(d) for d in wl["planted"][l])
         rows = [msa_synth.counter_bf16(seed, W.kvbar_stream(l % wl["HL"]), int(coff[d]) * 2 * Hkv * D,
                                        int(coff[d + 1] - coff[d]) * 2 * Hkv * D).reshape(-1, 2, Hkv, D)
                 for d in sel]
@@ -889,7 +891,7 @@ def run_reuse100m(args, torch, msa, msa_synth, device_fill, W):
         t_gen.append(t2 - t1)
         t_eager.append(t3 - t2)
     asm, gen, gen_eager = float(np.mean(t_asm)), float(np.mean(t_gen)), float(np.mean(t_eager))
-    recovered = all(sorted(ids_np[l][0].tolist()) == sorted(int(d) for d in wl["planted"]) for l in range(L))
+    recovered = all(sorted(ids_np[l][0].tolist()) == sorted(int(d) for d in wl["planted"][l]) for l in range(L))
     rows = mo_h[:, 1].numpy()
     # HBM bytes of one generated token: every layer reads its gathered rows and its local keys and values
     tok_bytes = int(sum(int(r) + L0 + T // 2 for r in rows)) * ROW_KV
@@ -948,7 +950,8 @@ def main():
     wl = build_workload(args, torch, msa, msa_synth, device_fill, W, chunk_level)
     run = Runner(args, torch, msa, wl)
     build_host_store(args, torch, device_fill, W, wl)
-    N, L, planted = wl["N"], wl["L"], sorted(int(d) for d in wl["planted"])
+    N, L = wl["N"], wl["L"]
+    planted = [sorted(int(d) for d in wl["planted"][l]) for l in range(L)]
 
     def timed(step_fn):
         for _ in range(args.warmup):
@@ -969,7 +972,7 @@ def main():
     log(f"timing {args.steps} steps (device gather)")
     step_s, scan_avg_s = timed(run.step_device_gather)
     ids_dev = run.ids_dev.cpu().numpy()
-    recovered = all(sorted(ids_dev[l, 0].tolist()) == planted for l in range(L))
+    recovered = all(sorted(ids_dev[l, 0].tolist()) == planted[l] for l in range(L))
     rows = run.mo_dev[:, 1].cpu().numpy()
     O_dev = run.O.clone()
 
@@ -978,7 +981,7 @@ def main():
     log(f"timing {args.steps} steps (hipMemcpyAsync gather)")
     mc_step_s, mc_scan_s = timed(run.step)
     attn_ms = [a.elapsed_time(b) for a, b in run.attn_timers]
-    mc_recovered = all(sorted(run.ids_np[l][0].tolist()) == planted for l in range(L))
+    mc_recovered = all(sorted(run.ids_np[l][0].tolist()) == planted[l] for l in range(L))
     same_out = bool(torch.equal(O_dev, run.O))
 
     kr_bytes_step = L * N * ROW_KR

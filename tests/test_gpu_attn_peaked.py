@@ -62,6 +62,24 @@ def test_peaked_decode(env, seed, B, Tq, Hq, Hkv, L, rows, qoff):
     P.assert_attn_close(got, ref, 2e-2, f"decode B={B} Tq={Tq} G={Hq // Hkv} L={L} rows={rows}")
 
 
+@pytest.mark.parametrize("seed,B,Tq,Hq,Hkv,L,rows,qoff", P.DECODE_CASES)
+def test_peaked_decode_closest_to_its_own_offset(env, seed, B, Tq, Hq, Hkv, L, rows, qoff):
+    """Negative control on the GPU output itself: it sits closer to the oracle
+    at the global RoPE offset k it was called with than to the oracle at k - 1
+    or k + 1, or with every query's memory range read one row late."""
+    torch, msa, ctx = env
+    w = P.peaked_inputs(seed, B, Tq, Hq, Hkv, D, L, rows, qoff, P.THETA, tokens=list(range(Tq)))
+    got = _run(torch, msa, ctx, w)
+    dist = lambda ref: float(np.max(np.abs(got - ref)))
+    own = dist(P.oracle_out(w))
+    wrong = {"k+1": P.oracle_out(w, qoff=qoff + 1), "late": P.oracle_out(w, mem_late=True)}
+    if qoff > 0:
+        wrong["k-1"] = P.oracle_out(w, qoff=qoff - 1)
+    for name, ref in wrong.items():
+        print(f"[attn] distance to the oracle at k {own:.3e}, to {name} {dist(ref):.3e}", flush=True)
+        assert own < dist(ref), name
+
+
 def test_peaked_decode_fp32(env):
     """The same planted decode in fp32 (the vector-unit kernel), bar 1e-3."""
     torch, msa, ctx = env
