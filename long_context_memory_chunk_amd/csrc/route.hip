@@ -123,7 +123,8 @@ __device__ __forceinline__ float unorder32(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Wave w of query b owns documents [128 w, 128 w + 128).  It stages their
+// Wave w of query b owns documents [S w, S w + S), S = kDocsPerWave (128, or
+// 512 for banks of many documents, see topk_docs_per_wave).  It stages their
 // chunk offsets in LDS, streams the chunk scores of their span with
 // coalesced loads, finds each chunk's document and takes an LDS atomic max on
 // the order-preserving bits (max is exact and order-independent, so the result
@@ -135,9 +136,9 @@ __device__ __forceinline__ float unorder32(uint32_t o) {
 // lane mask, plus the marks of earlier windows) minus one.  A wave whose span
 // exceeds the bit array, or that holds an empty document (two documents would
 // share one mark), finds documents by binary search in the offsets instead.
-constexpr int kDocsPerWave = 128;
 constexpr int kBitWords = 1024;                  // marks for spans of up to 32768 chunks per wave
 
+template <int kDocsPerWave>
 __global__ __launch_bounds__(256) void topk_partial_kernel(
     const float* __restrict__ c, int64_t N, const int64_t* __restrict__ off, int64_t n_docs,
     int waves_per_b, uint32_t* __restrict__ dkey, uint64_t* __restrict__ wmax, float* __restrict__ out_doc) {
@@ -258,8 +259,8 @@ constexpr int kFinalWaves = 16;
 constexpr int kFinalThreads = kFinalWaves * 64;
 constexpr int kSelCap = 4096;
 constexpr int kWmaxLds = 4096;                   // wave maxima kept in LDS (larger banks re-read them)
-constexpr int kDocsPerThread = MSA_MAX_TOPK * kDocsPerWave / kFinalThreads;
 
+template <int kDocsPerWave>
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const uint32_t* __restrict__ dkey, int64_t n_docs, const uint64_t* __restrict__ wmax, int W, int K,
     int32_t* __restrict__ ids, float* __restrict__ scores) {
@@ -276,6 +277,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const uint64_t* wm = wmax + b * W;
     const uint32_t* db = dkey + b * n_docs;
     const bool wm_lds = W <= kWmaxLds;
+    constexpr int kDocsPerThread = MSA_MAX_TOPK * kDocsPerWave / kFinalThreads;
 
     // (a) thr = the K-th largest wave maximum
     const int per = ((W + kFinalWaves - 1) / kFinalWaves + kWave - 1) / kWave * kWave;
@@ -363,8 +365,16 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     }
 }
 
-int topk_waves(int64_t n_docs) {
-    const int64_t w = ceil_div(n_docs, kDocsPerWave);
+// Documents per wave of topk_partial: 128 (the measured best on the 100M-token
+// bank's 199,922 documents: 21.5 us for the two kernels, against 24.4 with
+// 256 and 23.7 with 64), or 512 when 128 would give topk_final more wave
+// maxima than it keeps in LDS (chunk-level selection: 1,562,500 candidates).
+int topk_docs_per_wave(int64_t n_docs) {
+    return ceil_div(n_docs, int64_t(128)) <= kWmaxLds ? 128 : 512;
+}
+
+int topk_waves(int64_t n_docs, int dpw) {
+    const int64_t w = ceil_div(n_docs, int64_t(dpw));
     return int(w < 1 ? 1 : w);
 }
 
@@ -380,7 +390,7 @@ RouteWs route_ws_layout(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
     w.u_off = o;   o += align256(size_t(nq) * Hkv * D * sizeof(float));
     w.c_off = o;   o += align256(size_t(B) * N * sizeof(float));
     w.dkey_off = o; o += align256(size_t(B) * n_docs * sizeof(uint32_t));
-    w.wmax_off = o; o += align256(size_t(B) * topk_waves(n_docs) * sizeof(uint64_t));
+    w.wmax_off = o; o += align256(size_t(B) * topk_waves(n_docs, topk_docs_per_wave(n_docs)) * sizeof(uint64_t));
     w.mfma_off = o; o += align256(route_mfma_workspace(dt, B, Tq, Hq, Hkv, D, N, num_cus));
     w.total = o;
     return w;
@@ -420,12 +430,20 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     }
 
     // 3. document max + top-k
-    const int wpb = topk_waves(a.n_docs);
-    hipLaunchKernelGGL(topk_partial_kernel, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256),
-                       0, st, c, a.N, a.chunk_off, a.n_docs, wpb, dkey, wmax, a.out_doc);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_final_kernel, dim3(unsigned(a.B)), dim3(kFinalThreads), 0, st, dkey,
+    const int dpw = topk_docs_per_wave(a.n_docs);
+    const int wpb = topk_waves(a.n_docs, dpw);
+#define MSA_TOPK(S)                                                                                           \
+    hipLaunchKernelGGL(topk_partial_kernel<S>, dim3(unsigned(ceil_div(wpb, 4)), unsigned(a.B)), dim3(256), 0, \
+                       st, c, a.N, a.chunk_off, a.n_docs, wpb, dkey, wmax, a.out_doc);                      \
+    if ((err = hipGetLastError()) != hipSuccess) return err;                                                 \
+    hipLaunchKernelGGL(topk_final_kernel<S>, dim3(unsigned(a.B)), dim3(kFinalThreads), 0, st, dkey,         \
                        a.n_docs, wmax, wpb, a.top_k, a.out_ids, a.out_scores);
+    if (dpw == 128) {
+        MSA_TOPK(128)
+    } else {
+        MSA_TOPK(512)
+    }
+#undef MSA_TOPK
     return hipGetLastError();
 }
 
