@@ -853,3 +853,52 @@ def test_gather_device_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, 
     got = W.host_bits(dst)
     assert np.array_equal(got[:3], bank[0:3]) and np.array_equal(got[3:7], bank[5:9])
     assert np.array_equal(got[7:8], bank[3:4])
+
+
+def test_gather_device_one_query_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, ctx128):
+    """The single-query gather (one launch) follows the same rules as the
+    batched one: ids outside [0, n_docs) are skipped, the selected documents
+    are laid out in ascending id order, and rows past cap_rows are dropped."""
+    torch = torch_mod
+    coff = np.array([0, 3, 5, 9, 10], dtype=np.int64)
+    bank = msa_synth.counter_bf16(5, 9, 0, 10 * 64).reshape(10, 64)
+    host = torch.empty((10, 64), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    for ids_row, cap, want_rows, want in [
+        ([2, -5, 0, 99], 8, 7, [bank[0:3], bank[5:9]]),          # invalid ids skipped
+        ([3, 1, 2], 5, 5, [bank[3:5], bank[5:8]]),                # doc 2's last row and doc 3 past the cap
+    ]:
+        ids = torch.tensor([ids_row], dtype=torch.int32, device="cuda")
+        dst = torch.zeros((cap, 64), dtype=torch.bfloat16, device="cuda")
+        mo = torch.zeros(2, dtype=torch.int64, device="cuda")
+        ws = msa.workspace(msa.msa_gather_device_workspace_size(1, len(ids_row), cap))
+        msa.msa_gather_device(ctx128, host, 128, 10, torch.from_numpy(coff).cuda(), ids, dst, cap, mo, ws)
+        torch.cuda.synchronize()
+        assert mo.cpu().tolist() == [0, want_rows]
+        assert np.array_equal(W.host_bits(dst)[:want_rows], np.concatenate(want))
+
+
+def test_gather_device_one_query_past_the_single_launch_size(torch_mod, msa, ctx128):
+    """One query whose selected documents fill more than 8,192 destination
+    rows takes the plan + copy kernels instead of the single launch; the bytes
+    and offsets must match the oracle's indexing either way."""
+    torch = torch_mod
+    rng = np.random.default_rng(71)
+    n_docs, k, row_elems = 200, 60, 64
+    coff = msa_synth.prefix_offsets(rng.integers(120, 200, size=n_docs))
+    N = int(coff[-1])
+    bank = msa_synth.counter_bf16(71, 3, 0, N * row_elems).reshape(N, row_elems)
+    host = torch.empty((N, row_elems), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = rng.permutation(n_docs)[:k].astype(np.int32)[None]
+    cap = int(np.diff(coff)[ids[0]].sum())
+    assert cap > 8192
+    dst = torch.zeros((cap, row_elems), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(1, k, cap))
+    msa.msa_gather_device(ctx128, host, row_elems * 2, N, torch.from_numpy(coff).cuda(),
+                          torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
+    torch.cuda.synchronize()
+    ref, m = oracle.gather_rows(bank, coff, ids[0])
+    assert mo.cpu().tolist() == [0, m] and m == cap
+    assert np.array_equal(W.host_bits(dst), ref)
