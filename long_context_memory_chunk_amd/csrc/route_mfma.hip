@@ -293,10 +293,11 @@ __global__ __launch_bounds__(256) void route_mfma_tokmax(const float* __restrict
 // copies in flight behind the stage in use, and the XOR swizzle makes the rows
 // of a matrix-core operand read hit distinct LDS banks.  A workgroup (4 waves,
 // 2 x 2) owns 256 queries x 256 chunks; a wave owns 128 x 128, 16 accumulator
-// tiles of v_mfma_f32_32x32x16_bf16.  Each stage is two k-steps of 16; the
-// operands of the next k-step are read from LDS while the matrix cores work on
-// the current one.  The epilogue writes the tile's column maxima over its 256
-// tokens.
+// tiles of v_mfma_f32_32x32x16_bf16.  Each stage is two k-steps of 16, 32
+// products per wave; the next stage's operands are read into a second register
+// set, and the copies of the stage three ahead issued, a few at a time between
+// groups of products (see the pipeline below).  The epilogue writes the tile's
+// column maxima over its 256 tokens.
 
 constexpr int GB = 256;          // GEMM tile rows (queries and chunks)
 constexpr int GK = 32;           // contraction width of one stage
