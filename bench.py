@@ -272,6 +272,26 @@ class Runner:
                                 wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
 
 
+def read_probe_gbps(torch, device_fill, buf, reps=5):
+    """What this HBM delivers to a plain streaming read: msa_synth's probe
+    (non-temporal 16-byte loads, 16 KB in flight per wave, 8 waves per CU)
+    over every byte of `buf`, median of `reps` timed runs, in GB/s."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    nbytes = buf.numel() * buf.element_size()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for i in range(reps + 2):
+        e0.record()
+        device_fill.read_probe(buf, sink, blocks)
+        e1.record()
+        e1.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1) / 1e3)
+    return nbytes / float(np.median(ts)) / 1e9
+
+
 def host_cpu_model():
     """The host CPU's model name as lscpu reports it (or /proc/cpuinfo)."""
     try:
@@ -752,11 +772,12 @@ def run_hbmcopy(args, torch, msa, msa_synth, device_fill, W):
 
 def run_probes(args, torch, msa, msa_synth, device_fill, W):
     """Measured ceilings beside the spec figures (8 TB/s HBM, about 64 GB/s
-    PCIe per direction): a streaming read of a 4 GiB device tensor (a bf16
-    matrix-vector product over it, [2^20 x 2048] times a vector, which reads the
-    matrix once: the best reader among torch's reductions and BLAS calls here),
-    a 4 GiB device-to-device copy, and 1 GiB copies between pinned host memory
-    and the device in each direction."""
+    PCIe per direction): streaming reads of a 4 GiB device tensor, by
+    msa_synth's hand-written probe (non-temporal 16-byte loads, 8 waves per
+    CU) and by a bf16 matrix-vector product over it ([2^20 x 2048] times a
+    vector, which reads the matrix once: the best reader among torch's
+    reductions and BLAS calls here), a 4 GiB device-to-device copy, and 1 GiB
+    copies between pinned host memory and the device in each direction."""
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -774,6 +795,7 @@ def run_probes(args, torch, msa, msa_synth, device_fill, W):
     A = x.view(1 << 20, 2048)
     vec = torch.ones(2048, dtype=torch.bfloat16, device="cuda")
     read_s = timed(lambda: torch.mv(A, vec), 10)
+    probe = read_probe_gbps(torch, device_fill, x, reps=10)
     copy_s = timed(lambda: y.copy_(x), 10)
     same = bool(torch.equal(x[:1 << 20], y[:1 << 20]))
     del y
@@ -785,9 +807,10 @@ def run_probes(args, torch, msa, msa_synth, device_fill, W):
     d2h_s = timed(lambda: host.copy_(dev, non_blocking=True), 5)
     same = same and bool(torch.equal(dev[:1 << 20], x.view(torch.uint8)[:1 << 20]))
     return {"metric": "bandwidth probes (streaming read, device copy, pinned host <-> device)",
-            "value": round(2 * n / read_s / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 1,
+            "value": round(probe, 1), "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 2,
             "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "4 GiB device tensor read and copied, 1 GiB pinned host copies"},
+            "read_probe_GBps": round(probe, 1), "read_probe_frac_of_8TBps": round(probe / 8e3, 4),
             "read_GBps": round(2 * n / read_s / 1e9, 1), "read_frac_of_8TBps": round(2 * n / read_s / 8e12, 4),
             "device_copy_GBps": round(4 * n / copy_s / 1e9, 1),
             "h2d_GBps": round(m / h2d_s / 1e9, 1), "d2h_GBps": round(m / d2h_s / 1e9, 1),
@@ -992,6 +1015,7 @@ def main():
     roof_s = step_bytes / (HBM_PEAK_GBPS * 1e9)
     achieved = scan_bytes / scan_avg_s / 1e9
     traffic = counter_traffic(SCAN_COUNTERS, SCAN_SOURCES)
+    probe = read_probe_gbps(torch, device_fill, wl["Krbar"][0])
     out = {
         "metric": METRIC,
         "value": round(kr_bytes_step / step_s / 1e9, 2),
@@ -1034,6 +1058,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "route_scan_bf16_d128", "bytes_per_launch": scan_bytes,
                      "traffic_over_algorithmic": None if traffic is None else round(traffic / scan_bytes, 5)},
+        "read_probe": {"GBps": round(probe, 1), "frac_of_peak": round(probe / HBM_PEAK_GBPS, 4),
+                       "scan_over_probe": round(achieved / probe, 4),
+                       "kind": "plain streaming read of layer 0's K̄r (non-temporal 16-byte loads, 8 waves per CU)"},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
