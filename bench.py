@@ -212,6 +212,8 @@ class Runner:
         self.ids_host = torch.empty((L, 1, k), dtype=torch.int32, pin_memory=True)
         self.ids_dev = torch.empty((L, 1, k), dtype=torch.int32, device=dev)
         self.ws_gather = msa.workspace(msa.msa_gather_device_workspace_size(1, k, self.cap))
+        self.ws_ga = msa.workspace(msa.msa_gather_attn_workspace_size(1, 1, 1, Hq, Hkv, k, self.cap, self.cap,
+                                                                      args.local))
         self.ids_np = [self.ids_host[l].numpy() for l in range(L)]
         self.KVmem = torch.empty((L, self.cap, 2, Hkv, D), dtype=torch.bfloat16, device=dev)
         self.mo_host = torch.zeros((L, 2), dtype=torch.int64, pin_memory=True)
@@ -270,6 +272,22 @@ class Runner:
                                   self.ids_dev[l], self.KVmem[l], self.cap, self.mo_dev[l], self.ws_gather)
             msa.msa_sparse_attn(self.ctx, wl["Q"][l], self.KVmem[l], self.mo_dev[l], self.cap, wl["Kl"][l],
                                 wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
+
+    def step_gather_attn(self):
+        """The device-gather step with the gather and the attention in one
+        call (msa_gather_attn): the PCIe copy of the selected rows runs beside
+        the attention over the local keys, then the memory rows' attention
+        and the merge."""
+        msa, wl, k = self.msa, self.wl, self.k
+        for l in range(wl["L"]):
+            if self.timing:
+                msa.msa_route_time_next(self.ctx, *self.timers[self.t_i])
+                self.t_i += 1
+            msa.msa_route(self.ctx, wl["Qr"][l], wl["Krbar"][l], self.coff_dev, k, self.ids_dev[l],
+                          self.ws_route)
+            msa.msa_gather_attn(self.ctx, wl["host_layer"][l % wl["HL"]], ROW_KV, wl["N"], self.coff_dev,
+                                self.ids_dev[l], self.KVmem[l], self.cap, self.mo_dev[l], wl["Q"][l], self.cap,
+                                wl["Kl"][l], wl["Vl"][l], k, self.scale, self.O[l], self.ws_ga)
 
 
 def read_probe_gbps(torch, device_fill, buf, reps=5):
@@ -503,6 +521,7 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
     mo = torch.zeros((Lr, B + 1), dtype=torch.int64, device="cuda")
     ws_g = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
     ws_a = msa.workspace(msa.msa_sparse_attn_workspace_size(1, B, 1, Hq, Hkv, max_rows, L))
+    ws_ga = msa.workspace(msa.msa_gather_attn_workspace_size(1, B, 1, Hq, Hkv, k, cap, max_rows, L))
     O = torch.empty((Lr, B, 1, Hq, D), dtype=torch.bfloat16, device="cuda")
     host = [PinnedHost(N * ROW_KV) for _ in range(Lr)]
     for l in range(Lr):
@@ -513,22 +532,33 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
         a.record()
         b_.record()
 
-    def step(ti=None):
+    def step(ti=None, two_calls=False):
         for l in range(Lr):
             if ti is not None:
                 msa.msa_route_time_next(ctx, *timers[ti + l])
             msa.msa_route(ctx, Qr[l], Krbar[l], coff_dev, k, ids[l], ws_r)
-            msa.msa_gather_device(ctx, host[l].addr, ROW_KV, N, coff_dev, ids[l], KVmem, cap, mo[l], ws_g)
-            msa.msa_sparse_attn(ctx, Q[l], KVmem, mo[l], max_rows, Kl[l], Vl[l], k, 1.0 / math.sqrt(D), O[l], ws_a)
+            if two_calls:
+                msa.msa_gather_device(ctx, host[l].addr, ROW_KV, N, coff_dev, ids[l], KVmem, cap, mo[l], ws_g)
+                msa.msa_sparse_attn(ctx, Q[l], KVmem, mo[l], max_rows, Kl[l], Vl[l], k, 1.0 / math.sqrt(D), O[l],
+                                    ws_a)
+            else:   # the gather's PCIe copy runs beside the attention over the local keys
+                msa.msa_gather_attn(ctx, host[l].addr, ROW_KV, N, coff_dev, ids[l], KVmem, cap, mo[l], Q[l],
+                                    max_rows, Kl[l], Vl[l], k, 1.0 / math.sqrt(D), O[l], ws_ga)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s_ in range(args.steps):
-        step(s_ * Lr)
-    torch.cuda.synchronize()
-    st = (time.perf_counter() - t0) / args.steps
+    def timed(two_calls, with_timers):
+        for _ in range(args.warmup):
+            step(two_calls=two_calls)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            step(s_ * Lr if with_timers else None, two_calls=two_calls)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    st = timed(False, True)
+    O_one = O.clone()
+    st_two = timed(True, False)
+    o_diff = float((O_one.float() - O.float()).abs().max())
     scan = float(np.mean([a.elapsed_time(b_) for a, b_ in timers])) / 1e3
     got = ids.cpu().numpy()
     recovered = all(sorted(got[l, b].tolist()) == sorted(int(d) for d in planted[b]) for l in range(Lr) for b in range(B))
@@ -542,10 +572,13 @@ def run_batch32(args, torch, msa, msa_synth, device_fill, W):
         "warmup": args.warmup, "ms_per_step": round(st * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "32 single-token queries, 18 routing layers of 156,250 pooled chunks (10M tokens), "
-                               "top-16 each, device gather, 2,048 local tokens", "n_docs": n_docs,
+                               "top-16 each, device gather beside the local-key attention (msa_gather_attn), "
+                               "2,048 local tokens", "n_docs": n_docs,
                    "chunk_rows": N, "batch": B, "layers": Lr, "top_k": k, "local": L},
         "decode_tokens_per_s": round(B / st, 1),
         "route_ms": round(scan * 1e3, 4),
+        "two_calls_ms_per_step": round(st_two * 1e3, 4),
+        "two_calls_max_abs_diff": o_diff,
         "planted_recovered_all": recovered,
         "roofline": {"bound": "hbm", "achieved": round(scan_bytes / scan / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(scan_bytes / scan / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -999,6 +1032,13 @@ def main():
     rows = run.mo_dev[:, 1].cpu().numpy()
     O_dev = run.O.clone()
 
+    # the same step with the gather and the attention in one call
+    log(f"timing {args.steps} steps (gather + attention in one call)")
+    ga_step_s, ga_scan_s = timed(run.step_gather_attn)
+    ids_ga = run.ids_dev.cpu().numpy()
+    ga_recovered = all(sorted(ids_ga[l, 0].tolist()) == planted[l] for l in range(L))
+    ga_diff = float((run.O.float() - O_dev.float()).abs().max())
+
     # the same step with msa_gather: ids to the host, one hipMemcpyAsync per
     # run of selected rows on a side stream
     log(f"timing {args.steps} steps (hipMemcpyAsync gather)")
@@ -1045,6 +1085,12 @@ def main():
                             "frac": round(roof_s / step_s, 4)},
         "scan_kernel_ms": round(scan_avg_s * 1e3, 4),
         "planted_recovered_all_layers": recovered,
+        "gather_attn": {"ms_per_step": round(ga_step_s * 1e3, 4),
+                        "decode_tokens_per_s": round(1.0 / ga_step_s, 3),
+                        "decode_roofline_frac": round(roof_s / ga_step_s, 4),
+                        "scan_kernel_ms": round(ga_scan_s * 1e3, 4),
+                        "planted_recovered_all_layers": ga_recovered,
+                        "max_abs_diff_vs_two_calls": ga_diff},
         "memcpy_gather": {"ms_per_step": round(mc_step_s * 1e3, 4),
                           "decode_tokens_per_s": round(1.0 / mc_step_s, 3),
                           "Krbar_GBps": round(kr_bytes_step / mc_step_s / 1e9, 2),
@@ -1069,7 +1115,7 @@ def main():
     torch.cuda.synchronize()
     for h in wl["host"]:
         h.free()
-    if not (recovered and mc_recovered and same_out):
+    if not (recovered and mc_recovered and same_out and ga_recovered):
         sys.exit(1)
 
 

@@ -451,6 +451,40 @@ msa_status msa_sparse_attn_bwd(msa_ctx* ctx, msa_dtype dt,
                                void* dQ, void* dKVmem, void* dK_local, void* dV_local,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * msa_gather_attn -- stages 2b and 3 in one call: msa_gather_device of the
+ * selected documents' K̄/V̄ rows into dst_KVmem, then msa_sparse_attn over
+ * [those rows ; local K/V].  ([neo] 推論パイプライン, Fig. 3: the selected
+ * K̄/V̄ are loaded from host memory and concatenated with the local context
+ * for the attention; [blog] Memory Parallel: K̄/V̄ live in CPU memory and are
+ * fetched when selected.)
+ * The local keys need none of the gathered rows, so for decode rows (bf16,
+ * d 128, Hq/Hkv in {1, 2, 4, 8}, Tq < 64) their attention runs in the same
+ * launch as the PCIe copy, and the memory rows' attention and the merge of
+ * both follow it; other shapes run the gather and then the attention.
+ * Arguments: those of msa_gather_device (host_KVbar .. mem_off, with
+ * B = the queries) followed by those of msa_sparse_attn (Q .. O; KVmem is
+ * dst_KVmem and mem_rows_cap is cap_rows), with the same meaning, layout,
+ * validation and results: dst_KVmem and mem_off exactly as msa_gather_device
+ * writes them, O as msa_sparse_attn computes it (the partial softmaxes are
+ * merged in another order, so the bits can differ within rounding).
+ * row_bytes must be 2 * Hkv * d * sizeof(dt) (a K̄ row and a V̄ row).
+ *   workspace      device, >= msa_gather_attn_workspace_size(...) bytes,
+ *                  256-byte aligned; nothing in it needs to start at zero.
+ */
+size_t msa_gather_attn_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int top_k,
+                                      int64_t cap_rows, int64_t max_rows_per_query, int L);
+
+msa_status msa_gather_attn(msa_ctx* ctx, msa_dtype dt,
+                           const void* host_KVbar, size_t row_bytes, int64_t n_rows_host,
+                           const int64_t* doc_chunk_off, int64_t n_docs,
+                           const int32_t* ids, int top_k,
+                           void* dst_KVmem, int64_t cap_rows, int64_t* mem_off,
+                           const void* Q, int64_t B, int Tq, int Hq, int64_t max_rows_per_query,
+                           const void* K_local, const void* V_local, int L, int Hkv,
+                           int q_offset, float scale, void* O,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ EXPORTS = [
     "msa_gather", "msa_gather_device_workspace_size", "msa_gather_device",
     "msa_sparse_attn_workspace_size", "msa_sparse_attn", "msa_sparse_attn_noalloc",
     "msa_sparse_attn_lse", "msa_sparse_attn_bwd_workspace_size", "msa_sparse_attn_bwd",
+    "msa_gather_attn_workspace_size", "msa_gather_attn",
 ]
 
 
@@ -73,6 +74,9 @@ _SIGS = {
     "msa_sparse_attn_bwd_workspace_size": (SZ, [I32, I64, I32, I32, I32, I64, I32]),
     "msa_sparse_attn_bwd": (I32, [P, I32, P, I64, I32, I32, P, P, I64, I64, P, P, I32, I32, I32, F32,
                                   P, P, P, P, P, P, P, P, SZ, P]),
+    "msa_gather_attn_workspace_size": (SZ, [I32, I64, I32, I32, I32, I32, I64, I64, I32]),
+    "msa_gather_attn": (I32, [P, I32, P, SZ, I64, P, I64, P, I32, P, I64, P, P, I64, I32, I32, I64, P, P,
+                              I32, I32, I32, F32, P, P, SZ, P]),
 }
 
 
@@ -347,3 +351,26 @@ def workspace(nbytes, device="cuda"):
     """A device byte buffer (torch allocations are 512-byte aligned)."""
     import torch
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- stages 2b + 3
+
+def msa_gather_attn_workspace_size(dtype, B, Tq, Hq, Hkv, top_k, cap_rows, max_rows_per_query, L):
+    return lib().msa_gather_attn_workspace_size(dtype, B, Tq, Hq, Hkv, top_k, cap_rows, max_rows_per_query, L)
+
+
+def msa_gather_attn(ctx, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, ids, dst_KVmem, cap_rows, mem_off,
+                    Q, max_rows_per_query, K_local, V_local, q_offset, scale, O, workspace, stream=None):
+    """msa_gather_device then msa_sparse_attn over the gathered rows, in one
+    call: host_KVbar pinned host tensor or address; doc_chunk_off int64 device
+    [n_docs+1]; ids int32 device [B, top_k]; dst_KVmem [cap_rows, 2, Hkv, d];
+    mem_off int64 device [B+1]; Q [B, Tq, Hq, d]; K_local/V_local
+    [B, L, Hkv, d]; O [B, Tq, Hq, d]."""
+    B, top_k = ids.shape
+    _, Tq, Hq, _ = Q.shape
+    _, L, Hkv, _ = K_local.shape
+    _check(lib().msa_gather_attn(ctx.handle, _dtype(Q), _ptr(host_KVbar), row_bytes, n_rows_host,
+                                 _ptr(doc_chunk_off), doc_chunk_off.numel() - 1, _ptr(ids), top_k, _ptr(dst_KVmem),
+                                 cap_rows, _ptr(mem_off), _ptr(Q), B, Tq, Hq, max_rows_per_query, _ptr(K_local),
+                                 _ptr(V_local), L, Hkv, q_offset, float(scale), _ptr(O), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))

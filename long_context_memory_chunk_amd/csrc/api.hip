@@ -113,6 +113,32 @@ msa_status check_doc_len(const char* fn, const msa_ctx* ctx, int64_t n_docs, int
     return MSA_OK;
 }
 
+// Checks of the device gather's arguments (msa_gather_device, msa_gather_attn).
+msa_status check_gather_device(const char* fn, const msa_ctx* ctx, const void* host_KVbar, size_t row_bytes,
+                               int64_t n_rows_host, const int64_t* doc_chunk_off, int64_t n_docs,
+                               const int32_t* ids, int64_t B, int top_k, const void* dst_KVmem, int64_t cap_rows,
+                               const int64_t* mem_off) {
+    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+    if (!host_KVbar || !doc_chunk_off || !ids || !dst_KVmem || !mem_off)
+        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (row_bytes == 0 || row_bytes % 16 || n_rows_host < 0 || n_docs < 1 || cap_rows < 0)
+        return fail(MSA_ERR_INVALID_ARG, "%s: bad size (row_bytes must be a multiple of 16)", fn);
+    if (B < 1 || B > msa::kMaxGatherB)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: B must be in [1, %d]", fn, msa::kMaxGatherB);
+    if (top_k < 1 || top_k > MSA_MAX_TOPK || top_k > n_docs)
+        return fail(MSA_ERR_INVALID_ARG, "%s: top_k %d outside [1, min(n_docs, %d)]", fn, top_k, MSA_MAX_TOPK);
+    if (!aligned16(host_KVbar) || !aligned16(dst_KVmem))
+        return fail(MSA_ERR_INVALID_ARG, "%s: host store and destination must be 16-byte aligned", fn);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    const hipError_t e = hipPointerGetAttributes(&attr, host_KVbar);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(MSA_ERR_INVALID_ARG, "%s: host store is not pinned host memory (use hipHostMalloc)", fn);
+    }
+    return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -507,31 +533,16 @@ msa_status msa_gather_device(msa_ctx* ctx, const void* host_KVbar, size_t row_by
                              int top_k, void* dst_KVmem, int64_t cap_rows, int64_t* mem_off,
                              void* workspace, size_t ws_bytes, hipStream_t stream) {
     const char* fn = "msa_gather_device";
-    if (!ctx) return fail(MSA_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
-    if (!host_KVbar || !doc_chunk_off || !ids || !dst_KVmem || !mem_off)
-        return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-    if (row_bytes == 0 || row_bytes % 16 || n_rows_host < 0 || n_docs < 1 || cap_rows < 0)
-        return fail(MSA_ERR_INVALID_ARG, "%s: bad size (row_bytes must be a multiple of 16)", fn);
-    if (B < 1 || B > msa::kMaxGatherB)
-        return fail(MSA_ERR_UNSUPPORTED, "%s: B must be in [1, %d]", fn, msa::kMaxGatherB);
-    if (top_k < 1 || top_k > MSA_MAX_TOPK || top_k > n_docs)
-        return fail(MSA_ERR_INVALID_ARG, "%s: top_k %d outside [1, min(n_docs, %d)]", fn, top_k, MSA_MAX_TOPK);
-    if (!aligned16(host_KVbar) || !aligned16(dst_KVmem))
-        return fail(MSA_ERR_INVALID_ARG, "%s: host store and destination must be 16-byte aligned", fn);
-    hipPointerAttribute_t attr;
-    std::memset(&attr, 0, sizeof(attr));
-    hipError_t e = hipPointerGetAttributes(&attr, host_KVbar);
-    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
-        (void)hipGetLastError();
-        return fail(MSA_ERR_INVALID_ARG, "%s: host store is not pinned host memory (use hipHostMalloc)", fn);
-    }
+    msa_status s = check_gather_device(fn, ctx, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, B,
+                                       top_k, dst_KVmem, cap_rows, mem_off);
+    if (s != MSA_OK) return s;
     const size_t need = msa::gather_device_workspace(B, cap_rows);
     if (!workspace || !aligned256(workspace) || ws_bytes < need)
         return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
                     ws_bytes);
     DeviceGuard dg(ctx->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_gather_device: hipSetDevice");
-    e = msa::launch_gather_device(host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, B, top_k,
+    const hipError_t e = msa::launch_gather_device(host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, B, top_k,
                                   dst_KVmem, cap_rows, mem_off, workspace, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_gather_device: launch");
     return ok();
@@ -691,6 +702,53 @@ msa_status msa_sparse_attn_bwd(msa_ctx* ctx, msa_dtype dt, const void* Q, int64_
     if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_sparse_attn_bwd: hipSetDevice");
     hipError_t e = msa::launch_attn_bwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_bwd: launch");
+    return ok();
+}
+
+size_t msa_gather_attn_workspace_size(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int top_k,
+                                      int64_t cap_rows, int64_t max_rows_per_query, int L) {
+    if (!dtype_ok(dt) || B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || top_k < 1 || cap_rows < 0 ||
+        max_rows_per_query < 0 || L < 1)
+        return 0;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+    }
+    msa::AttnArgs a{dt, nullptr, B, Tq, Hq, Hkv, 128, L, nullptr, nullptr, cap_rows, max_rows_per_query,
+                    nullptr, nullptr, 0, 1.f, nullptr, nullptr, 0, nullptr, 0, cus, nullptr};
+    return msa::gather_attn_workspace(a, cap_rows);
+}
+
+msa_status msa_gather_attn(msa_ctx* ctx, msa_dtype dt, const void* host_KVbar, size_t row_bytes,
+                           int64_t n_rows_host, const int64_t* doc_chunk_off, int64_t n_docs, const int32_t* ids,
+                           int top_k, void* dst_KVmem, int64_t cap_rows, int64_t* mem_off, const void* Q, int64_t B,
+                           int Tq, int Hq, int64_t max_rows_per_query, const void* K_local, const void* V_local,
+                           int L, int Hkv, int q_offset, float scale, void* O, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    const char* fn = "msa_gather_attn";
+    msa_status s = check_gather_device(fn, ctx, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, B,
+                                       top_k, dst_KVmem, cap_rows, mem_off);
+    if (s != MSA_OK) return s;
+    s = check_attn(fn, ctx, dt, Q, B, Tq, Hq, dst_KVmem, mem_off, cap_rows, max_rows_per_query, K_local, V_local,
+                   L, Hkv, q_offset, scale);
+    if (s != MSA_OK) return s;
+    if (row_bytes != size_t(2) * Hkv * ctx->head_dim * dtype_bytes(dt))
+        return fail(MSA_ERR_INVALID_ARG, "%s: row_bytes %zu is not one K̄ and one V̄ row (2 x %d x %d x %zu)", fn,
+                    row_bytes, Hkv, ctx->head_dim, dtype_bytes(dt));
+    if (!O || !aligned16(O)) return fail(MSA_ERR_INVALID_ARG, "%s: O must be a 16-byte aligned pointer", fn);
+    msa::GatherAttnArgs ga{msa::AttnArgs{dt, Q, B, Tq, Hq, Hkv, ctx->head_dim, L, dst_KVmem, mem_off, cap_rows,
+                                         max_rows_per_query, K_local, V_local, q_offset, scale, O, workspace,
+                                         ws_bytes, ctx->rope_cs, ctx->max_pos, ctx->num_cus, nullptr},
+                           host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, top_k, cap_rows};
+    const size_t need = msa::gather_attn_workspace(ga.a, cap_rows);
+    if (!workspace || !aligned256(workspace) || ws_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,
+                    ws_bytes);
+    DeviceGuard dg(ctx->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "msa_gather_attn: hipSetDevice");
+    const hipError_t e = msa::launch_gather_attn(ga, stream);
+    if (e != hipSuccess) return hip_fail(e, "msa_gather_attn: launch");
     return ok();
 }
 

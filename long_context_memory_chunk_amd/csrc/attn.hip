@@ -33,6 +33,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "attn_mfma.hpp"
+#include "gather_body.hpp"
 
 namespace msa {
 
@@ -370,6 +371,90 @@ size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, i
     size_t split = align256(rows * D * sizeof(float)) + align256(rows * sizeof(float2));
     size_t mf = attn_mfma_workspace(dt, B, Tq, Hq, Hkv, D, max_rows, L);
     return split > mf ? split : mf;
+}
+
+// ---------------------------------------------------------------- gather + attention
+//
+// Decode rows on the matrix-core path: the device gather's copy and the
+// attention over the local keys run in one launch (the local keys need none
+// of the gathered rows), then the attention over the gathered memory rows,
+// then one combine over both sets of partials.  Other shapes run the gather
+// and then the attention, one after the other.
+
+namespace {
+
+struct GatherAttnPlan {
+    bool fused, one;
+    DecodePlan loc, mem;     // mem.P == 0: no memory rows
+    int P_total;
+};
+
+GatherAttnPlan gather_attn_plan(const AttnArgs& a, int64_t cap_rows) {
+    GatherAttnPlan g{false, false, {0, 0}, {0, 0}, 0};
+    if (!decode_applicable(a.dt, a.D, a.Hq, a.Hkv, a.max_rows, a.L) || attn_mfma_applicable(a)) return g;
+    g.loc = decode_plan(a.B, a.Tq, a.Hkv, 0, a.L, a.num_cus);
+    if (a.max_rows > 0) g.mem = decode_plan(a.B, a.Tq, a.Hkv, a.max_rows, 0, a.num_cus);
+    g.P_total = g.loc.P + g.mem.P;
+    if (g.P_total > kMaxParts) return g;                     // the combine's bound
+    g.fused = true;
+    g.one = a.B == 1 && cap_rows <= kOneMaxRows;
+    return g;
+}
+
+size_t partial_bytes(int64_t rows, int D) {
+    return align256(size_t(rows) * D * sizeof(float)) + align256(size_t(rows) * sizeof(float2));
+}
+
+}  // namespace
+
+size_t gather_attn_workspace(const AttnArgs& a, int64_t cap_rows) {
+    const size_t gws = align256(gather_device_workspace(a.B, cap_rows));
+    const GatherAttnPlan g = gather_attn_plan(a, cap_rows);
+    if (g.fused) return gws + partial_bytes(a.B * a.Tq * a.Hq * g.P_total, a.D);
+    return gws + attn_workspace(a.dt, a.B, a.Tq, a.Hq, a.Hkv, a.D, a.max_rows, a.L, a.num_cus);
+}
+
+hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
+    const AttnArgs& a0 = ga.a;
+    if (a0.B == 0) return hipSuccess;
+    const size_t gws = align256(gather_device_workspace(a0.B, ga.cap_rows));
+    AttnArgs a = a0;
+    a.ws = static_cast<char*>(a0.ws) + gws;
+    a.ws_bytes = a0.ws_bytes - gws;
+    const GatherAttnPlan g = gather_attn_plan(a, ga.cap_rows);
+    hipError_t err;
+    if (!g.fused) {
+        err = launch_gather_device(ga.host, ga.row_bytes, ga.n_rows_host, ga.off, ga.n_docs, ga.ids, a.B, ga.K,
+                                   const_cast<void*>(a.KVmem), ga.cap_rows, const_cast<int64_t*>(a.mem_off), a0.ws, st);
+        if (err != hipSuccess) return err;
+        return launch_attn(a, st);
+    }
+    GatherCopyArgs gc{static_cast<const u32x4*>(ga.host), int64_t(ga.row_bytes / 16), nullptr, int(a.B), ga.ids, ga.K,
+                      ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, const_cast<int64_t*>(a.mem_off),
+                      static_cast<u32x4*>(const_cast<void*>(a.KVmem))};
+    int n_copy = kCopyWgs;
+    if (g.one) {
+        const int64_t w = ceil_div(ga.cap_rows, int64_t(kOneRows));
+        n_copy = int(w > 0 ? w : 1);
+    } else {
+        int64_t* src_of_row = nullptr;
+        err = launch_gather_plan(ga.ids, a.B, ga.K, ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows,
+                                 const_cast<int64_t*>(a.mem_off), a0.ws, &src_of_row, st);
+        if (err != hipSuccess) return err;
+        gc.src_of_row = src_of_row;
+    }
+    const size_t rows = size_t(a.B) * a.Tq * a.Hq * g.P_total;
+    float* part_o = static_cast<float*>(a.ws);
+    float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align256(rows * a.D * sizeof(float)));
+    err = launch_gather_local_attn(gc, g.one, n_copy, a, part_o, part_ml, g.loc.P, g.loc.nc, g.P_total, st);
+    if (err != hipSuccess) return err;
+    if (g.mem.P > 0) {
+        err = launch_decode_mfma_mem(a, part_o, part_ml, g.mem.P, g.mem.nc, g.loc.P, g.P_total, st);
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
+                       part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse);
+    return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {

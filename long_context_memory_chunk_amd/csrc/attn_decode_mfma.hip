@@ -39,6 +39,7 @@
 // rows once this block's P . V is done.
 #include "common.hpp"
 #include "attn_mfma.hpp"
+#include "gather_body.hpp"
 
 namespace msa {
 
@@ -78,12 +79,44 @@ __device__ __forceinline__ void rotate_pack(u32x4 x1, u32x4 x2, const float2* __
                 pack_bf16x2(y2[6], y2[7])};
 }
 
-template <int G>
-__global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
+// The arguments of one launch.  Partials of row r and partition p of this
+// launch go to index r * P_total + p_base + p of part_o / part_ml, so two
+// launches over disjoint key ranges of the same rows fill one partial set.
+struct DecodeArgs {
+    const uint16_t* Q;
+    int Tq, Hq, hkv;
+    const uint16_t* KVmem;
+    const int64_t* mem_off;
+    int64_t cap, max_rows;
+    const uint16_t* Kl;
+    const uint16_t* Vl;
+    int L, q_offset;
+    float qscale;
+    const float2* rope_cs;
+    int max_pos;
+    int NC, p_base, P_total;
+    int use_mem, use_local;   // 1/1 all keys, 0/1 local keys only, 1/0 memory rows only (launch
+                              // arguments: every range runs the one compiled body)
+    float* part_o;
+    float2* part_ml;
+};
+
+// Key ranges: every key of the row, only its local keys (memory rows taken as
+// absent: KVmem is not read, and mem_off is read but not used), or only its
+// memory rows.  The query keeps its position in every case.
+enum DecodeKeys : int { kKeysAll = 0, kKeysLocal = 1, kKeysMem = 2 };
+
+// One workgroup: partition p (chunks p * NC ..) of (query token bt, KV head g);
+// P is the partials' row stride and p_base + p this partial's index.  (The
+// pointers are parameters so that their no-alias promise survives inlining.)
+template <int G, bool kRanged>
+__device__ __forceinline__ void decode_wg(
     const uint16_t* __restrict__ Q, int Tq, int Hq, int hkv, const uint16_t* __restrict__ KVmem,
     const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows, const uint16_t* __restrict__ Kl,
     const uint16_t* __restrict__ Vl, int L, int q_offset, float qscale, const float2* __restrict__ rope_cs,
-    int max_pos, int P, int NC, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    int max_pos, int NC, int p_base, int P, int use_mem, int use_local, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, int p, int g, int64_t bt) {
+    const int pp = p_base + p;
     constexpr int GH = G < 4 ? G : 4;             // heads per 32-lane half of the score layout
     __shared__ u32x4 s_k[4][32 * 16];             // each wave's 32 (rotated) key rows, 16-byte units swizzled
     __shared__ uint32_t s_pp[4][16][G];           // P of each wave's block: pair p = keys 2p, 2p + 1
@@ -94,14 +127,13 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int slot = lane / 16, c = lane % 16;    // row layouts: 4 rows per instruction
     const int col = lane % 32;                    // score layout: key (B operand column), head (A operand row)
-    const int p = blockIdx.x, g = blockIdx.y;
-    const int64_t bt = blockIdx.z;
     const int64_t b = bt / Tq;
     const int i = int(bt % Tq);
 
     int64_t r0, M;
     mem_range(mem_off, b, cap, max_rows, r0, M);
-    const int64_t total = M + int64_t(L - Tq) + i + 1;
+    if (kRanged) M *= use_mem;                    // (the all-keys kernel is compiled without the range)
+    const int64_t total = M + (kRanged ? use_local : 1) * (int64_t(L - Tq) + i + 1);
     const int64_t row_elems = int64_t(hkv) * DH;
     const int64_t hrow = bt * Hq + int64_t(g) * G;   // first query head row of this group
     const int64_t n_chunks = (total + kDecodeChunk - 1) / kDecodeChunk;
@@ -109,8 +141,8 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
     const int64_t ce = (cb + NC < n_chunks) ? cb + NC : n_chunks;
 
     if (cb >= ce) {                               // no keys here: an empty partial
-        for (int idx = tid; idx < G * DH; idx += 256) part_o[((hrow + idx / DH) * P + p) * DH + idx % DH] = 0.f;
-        if (tid < G) part_ml[(hrow + tid) * P + p] = make_float2(-INFINITY, 0.f);
+        for (int idx = tid; idx < G * DH; idx += 256) part_o[((hrow + idx / DH) * P + pp) * DH + idx % DH] = 0.f;
+        if (tid < G) part_ml[(hrow + tid) * P + pp] = make_float2(-INFINITY, 0.f);
         return;
     }
 
@@ -418,7 +450,7 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
             const float f = (s_m[w][hh] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][hh] - mw);
             acc += f * red[w][hh][dd];
         }
-        part_o[((hrow + hh) * P + p) * DH + dd] = acc;
+        part_o[((hrow + hh) * P + pp) * DH + dd] = acc;
     }
     if (tid < G) {
         const float mw = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
@@ -427,8 +459,84 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
         for (int w = 0; w < 4; ++w)
             lsum += (s_m[w][tid] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][tid] - mw) * s_l[w][tid];
         // the combine takes m in natural-log units
-        part_ml[(hrow + tid) * P + p] = make_float2(mw == -INFINITY ? -INFINITY : mw * kLn2D, lsum);
+        part_ml[(hrow + tid) * P + pp] = make_float2(mw == -INFINITY ? -INFINITY : mw * kLn2D, lsum);
     }
+}
+
+template <int G>
+__device__ __forceinline__ void decode_ranged(const DecodeArgs& da, int p, int g, int64_t bt) {
+    decode_wg<G, true>(da.Q, da.Tq, da.Hq, da.hkv, da.KVmem, da.mem_off, da.cap, da.max_rows, da.Kl, da.Vl, da.L,
+                       da.q_offset, da.qscale, da.rope_cs, da.max_pos, da.NC, da.p_base, da.P_total, da.use_mem,
+                       da.use_local, da.part_o, da.part_ml, p, g, bt);
+}
+
+// Every key of each row (the arguments one by one, as the launch passes them).
+template <int G>
+__global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_mfma_kernel(
+    const uint16_t* __restrict__ Q, int Tq, int Hq, int hkv, const uint16_t* __restrict__ KVmem,
+    const int64_t* __restrict__ mem_off, int64_t cap, int64_t max_rows, const uint16_t* __restrict__ Kl,
+    const uint16_t* __restrict__ Vl, int L, int q_offset, float qscale, const float2* __restrict__ rope_cs,
+    int max_pos, int P, int NC, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    decode_wg<G, false>(Q, Tq, Hq, hkv, KVmem, mem_off, cap, max_rows, Kl, Vl, L, q_offset, qscale, rope_cs, max_pos,
+                        NC, 0, P, 1, 1, part_o, part_ml, int(blockIdx.x), int(blockIdx.y), int64_t(blockIdx.z));
+}
+
+// A key range of each row (memory rows only), partials at an offset.
+template <int G>
+__global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_range_kernel(DecodeArgs da) {
+    decode_ranged<G>(da, int(blockIdx.x), int(blockIdx.y), int64_t(blockIdx.z));
+}
+
+// The device gather and the attention over the local keys in one launch: the
+// copy waits on PCIe and leaves most CUs idle, and the local keys (most of a
+// decode row's keys) need none of the gathered rows, so their partials are
+// formed meanwhile.  Workgroups [copy_first, copy_first + n_copy) copy, the
+// others are the local-key attention grid (P x hkv x B*Tq, partition
+// fastest).  The bounded copy goes first, since it is the longer; the
+// one-query copy (one workgroup per kOneRows rows) after the attention, so
+// that a large capacity cannot hold every slot before the attention starts.
+template <int G, bool kOne>
+__global__ __launch_bounds__(256, G < 8 ? 2 : 1) void gather_local_attn_kernel(GatherCopyArgs gc, DecodeArgs da,
+                                                                              int P, int copy_first, int n_copy) {
+    const int bx = int(blockIdx.x);
+    if (bx >= copy_first && bx < copy_first + n_copy) {
+        const int wg = bx - copy_first;
+        if (kOne)
+            gather_one_wg(gc.host, gc.row_vecs, gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off,
+                          gc.dst, wg);
+        else
+            gather_copy_wg(gc.host, gc.row_vecs, gc.src_of_row, gc.mem_off, gc.B, gc.dst, wg, n_copy);
+        return;
+    }
+    // 32-bit, wave-uniform index arithmetic (the grid has fewer than 2^31 workgroups)
+    const uint32_t w = uint32_t(__builtin_amdgcn_readfirstlane(bx < copy_first ? bx : bx - n_copy));
+    // (the divisions run on the vector units: readfirstlane puts their results
+    // back in scalar registers, so the addresses built from them stay scalar)
+    const uint32_t wp = uint32_t(__builtin_amdgcn_readfirstlane(int(w / uint32_t(P))));
+    const int p = __builtin_amdgcn_readfirstlane(int(w - wp * uint32_t(P)));
+    const int g = __builtin_amdgcn_readfirstlane(int(wp % uint32_t(da.hkv)));
+    const int bt = __builtin_amdgcn_readfirstlane(int(wp / uint32_t(da.hkv)));
+    decode_ranged<G>(da, p, g, int64_t(bt));
+}
+
+DecodeArgs decode_args(const AttnArgs& a, int keys, float* part_o, float2* part_ml, int nc, int p_base,
+                       int P_total) {
+    return DecodeArgs{static_cast<const uint16_t*>(a.Q), a.Tq, a.Hq, a.Hkv, static_cast<const uint16_t*>(a.KVmem),
+                      a.mem_off, a.mem_rows_cap, a.max_rows, static_cast<const uint16_t*>(a.K_local),
+                      static_cast<const uint16_t*>(a.V_local), a.L, a.q_offset, a.scale * kLog2eD, a.rope_cs,
+                      a.max_pos, nc, p_base, P_total, keys != kKeysLocal, keys != kKeysMem, part_o, part_ml};
+}
+
+hipError_t launch_range(const AttnArgs& a, const DecodeArgs& da, int P, hipStream_t st) {
+    const dim3 grid(unsigned(P), unsigned(a.Hkv), unsigned(a.B * a.Tq));
+    switch (a.Hq / a.Hkv) {
+        case 1: hipLaunchKernelGGL((attn_decode_range_kernel<1>), grid, dim3(256), 0, st, da); break;
+        case 2: hipLaunchKernelGGL((attn_decode_range_kernel<2>), grid, dim3(256), 0, st, da); break;
+        case 4: hipLaunchKernelGGL((attn_decode_range_kernel<4>), grid, dim3(256), 0, st, da); break;
+        case 8: hipLaunchKernelGGL((attn_decode_range_kernel<8>), grid, dim3(256), 0, st, da); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -448,6 +556,37 @@ hipError_t launch_decode_mfma(const AttnArgs& a, float* part_o, float2* part_ml,
         default: return hipErrorInvalidValue;
     }
 #undef MSA_DM
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_mem(const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, int p_base,
+                                  int P_total, hipStream_t st) {
+    return launch_range(a, decode_args(a, kKeysMem, part_o, part_ml, nc, p_base, P_total), P, st);
+}
+
+hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int n_copy, const AttnArgs& a,
+                                    float* part_o, float2* part_ml, int P, int nc, int P_total, hipStream_t st) {
+    const DecodeArgs da = decode_args(a, kKeysLocal, part_o, part_ml, nc, 0, P_total);
+    const int64_t n_attn = int64_t(P) * a.Hkv * a.B * a.Tq;
+    const unsigned grid = unsigned(n_attn + n_copy);
+    const int copy_first = one ? int(n_attn) : 0;
+#define MSA_GLA(GG)                                                                                              \
+    do {                                                                                                         \
+        if (one)                                                                                                 \
+            hipLaunchKernelGGL((gather_local_attn_kernel<GG, true>), dim3(grid), dim3(256), 0, st, gc, da, P,   \
+                               copy_first, n_copy);                                                             \
+        else                                                                                                     \
+            hipLaunchKernelGGL((gather_local_attn_kernel<GG, false>), dim3(grid), dim3(256), 0, st, gc, da, P,  \
+                               copy_first, n_copy);                                                             \
+    } while (0)
+    switch (a.Hq / a.Hkv) {
+        case 1: MSA_GLA(1); break;
+        case 2: MSA_GLA(2); break;
+        case 4: MSA_GLA(4); break;
+        case 8: MSA_GLA(8); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef MSA_GLA
     return hipGetLastError();
 }
 

@@ -15,5 +15,15 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 // of nc chunks each, writing the partial (m, l, o) of every row and partition.
 constexpr int kDecodeChunk = 128;
 hipError_t launch_decode_mfma(const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, hipStream_t st);
+// The same over the memory rows only, its P partitions written as partials
+// p_base .. p_base + P - 1 of P_total per row.
+hipError_t launch_decode_mfma_mem(const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, int p_base,
+                                  int P_total, hipStream_t st);
+// One launch: the device gather's copy (n_copy workgroups; the one-query copy
+// if `one`) beside the attention over the local keys only, whose P partitions
+// are written as partials 0 .. P - 1 of P_total per row.  a.KVmem and
+// a.mem_off are not read.
+hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int n_copy, const AttnArgs& a,
+                                    float* part_o, float2* part_ml, int P, int nc, int P_total, hipStream_t st);
 
 }  // namespace msa

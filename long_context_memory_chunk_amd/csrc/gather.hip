@@ -21,31 +21,13 @@
 // their row counts itself (a few hundred bytes) and then copies its share.
 // No host synchronisation is needed between routing and attention.
 #include "common.hpp"
+#include "gather_body.hpp"
 #include "launch.hpp"
 
 namespace msa {
 namespace {
 
 constexpr int kPlanWaves = 16;
-
-// Lane `src` of a 64-bit value, for a wave-uniform lane index (two scalar
-// reads instead of two LDS permutes).
-__device__ __forceinline__ int64_t lane64(int64_t v, int src) {
-    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), src));
-    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(uint64_t(v) >> 32)), src));
-    return int64_t((uint64_t(hi) << 32) | lo);
-}
-
-__device__ __forceinline__ int64_t wave_excl_scan(int64_t v, int lane) {
-    // inclusive Hillis-Steele scan over 64 lanes, then shift to exclusive
-    int64_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    return x - v;
-}
 
 __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
     const int32_t* __restrict__ ids, int B, int K, const int64_t* __restrict__ off, int64_t n_docs,
@@ -131,108 +113,37 @@ __global__ __launch_bounds__(kPlanWaves * 64) void gather_plan_kernel(
     }
 }
 
-// Destination rows are dealt to the kCopyWgs workgroups kCopyRows at a
-// time (rows w * kCopyRows + j, then + kCopyWgs * kCopyRows, ...); a thread
-// copies one 16-byte unit of each of its workgroup's kCopyRows rows, all
-// loads issued before the stores.
-constexpr int kCopyWgs = 64;
-constexpr int kCopyRows = 8;
-
 __global__ __launch_bounds__(256) void gather_copy_kernel(const u32x4* __restrict__ host, int64_t row_vecs,
                                                           const int64_t* __restrict__ src_of_row,
                                                           const int64_t* __restrict__ mem_off, int B,
                                                           u32x4* __restrict__ dst) {
-    const int64_t total = mem_off[B];
-    for (int64_t r0 = int64_t(blockIdx.x) * kCopyRows; r0 < total; r0 += int64_t(kCopyWgs) * kCopyRows) {
-        int64_t src[kCopyRows];
-#pragma unroll
-        for (int j = 0; j < kCopyRows; ++j) src[j] = (r0 + j < total) ? src_of_row[r0 + j] : -1;
-        for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
-            const int64_t v = v0 + threadIdx.x;
-            if (v >= row_vecs) break;
-            u32x4 x[kCopyRows];
-#pragma unroll
-            for (int j = 0; j < kCopyRows; ++j)
-                if (src[j] >= 0) x[j] = host[src[j] * row_vecs + v];
-#pragma unroll
-            for (int j = 0; j < kCopyRows; ++j)
-                if (src[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
-        }
-    }
+    gather_copy_wg(host, row_vecs, src_of_row, mem_off, B, dst, int(blockIdx.x), kCopyWgs);
 }
 
-// gather_one: workgroup w copies destination rows w * kOneRows .. + kOneRows
-// - 1 (all of them in flight together), so every selected row is requested at
-// once whatever the document sizes.  Each wave derives the plan on its own
-// (wave-uniform results, no barrier): the K ids sorted, their row counts and
-// prefix sums; a destination row's entry is the last one starting at or
-// before it (a ballot).  Workgroup 0 also writes mem_off.
-constexpr int kOneRows = 2;
-constexpr int64_t kOneMaxRows = 8192;   // larger capacities take the plan + bounded copy path
-
+// gather_one: every selected row is requested at once, whatever the
+// document sizes (kOneRows rows per workgroup, all in flight together).
 __global__ __launch_bounds__(256) void gather_one_kernel(const u32x4* __restrict__ host, int64_t row_vecs,
                                                          const int32_t* __restrict__ ids, int K,
                                                          const int64_t* __restrict__ off, int64_t n_docs,
                                                          int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
                                                          u32x4* __restrict__ dst) {
-    const int lane = threadIdx.x % kWave;
-    int32_t id = (lane < K) ? ids[lane] : 0x7FFFFFFF;
-    if (id < 0 || id >= n_docs) id = 0x7FFFFFFF;          // invalid ids copy nothing
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const int32_t y = __shfl_xor(id, j);
-            const bool asc_block = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            const int32_t mn = id < y ? id : y, mx = id < y ? y : id;
-            id = (lower == asc_block) ? mn : mx;
-        }
-    }
-    int64_t src = 0, rows = 0;
-    if (id != 0x7FFFFFFF) {
-        src = off[id];
-        const int64_t end = off[id + 1];
-        if (src >= 0 && end >= src && end <= n_rows_host) rows = end - src;
-        else src = 0;
-    }
-    const int64_t dst0 = wave_excl_scan(rows, lane);
-    int64_t total = lane64(dst0 + rows, 63);
-    total = total < cap ? total : cap;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        mem_off[0] = 0;
-        mem_off[1] = total;
-    }
-    const int64_t r0 = int64_t(blockIdx.x) * kOneRows;
-    int64_t sr[kOneRows];
-#pragma unroll
-    for (int j = 0; j < kOneRows; ++j) {
-        const int64_t r = r0 + j;
-        sr[j] = -1;
-        if (r < total) {
-            // the entry holding destination row r: the last lane with rows and dst0 <= r
-            const uint64_t m = __ballot(rows > 0 && dst0 <= r);
-            const int e = 63 - __builtin_clzll(m);
-            sr[j] = lane64(src, e) + (r - lane64(dst0, e));
-        }
-    }
-    for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
-        const int64_t v = v0 + threadIdx.x;
-        if (v >= row_vecs) break;
-        u32x4 x[kOneRows];
-#pragma unroll
-        for (int j = 0; j < kOneRows; ++j)
-            if (sr[j] >= 0) x[j] = host[sr[j] * row_vecs + v];
-#pragma unroll
-        for (int j = 0; j < kOneRows; ++j)
-            if (sr[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
-    }
+    gather_one_wg(host, row_vecs, ids, K, off, n_docs, n_rows_host, cap, mem_off, dst, int(blockIdx.x));
 }
 
 }  // namespace
 
 size_t gather_device_workspace(int64_t B, int64_t cap_rows) {
     return align256(size_t(B) * 64 * 3 * sizeof(int64_t)) + align256(size_t(cap_rows) * sizeof(int64_t));
+}
+
+hipError_t launch_gather_plan(const int32_t* ids, int64_t B, int K, const int64_t* off, int64_t n_docs,
+                              int64_t n_rows_host, int64_t cap_rows, int64_t* mem_off, void* ws,
+                              int64_t** src_of_row, hipStream_t st) {
+    int64_t* plan = static_cast<int64_t*>(ws);
+    *src_of_row = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + align256(size_t(B) * 64 * 3 * 8));
+    hipLaunchKernelGGL(gather_plan_kernel, dim3(1), dim3(kPlanWaves * 64), 0, st, ids, int(B), K, off, n_docs,
+                       n_rows_host, cap_rows, mem_off, plan, *src_of_row);
+    return hipGetLastError();
 }
 
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
@@ -245,11 +156,8 @@ hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_ro
                            n_rows_host, cap_rows, mem_off, static_cast<u32x4*>(dst));
         return hipGetLastError();
     }
-    int64_t* plan = static_cast<int64_t*>(ws);
-    int64_t* src_of_row = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + align256(size_t(B) * 64 * 3 * 8));
-    hipLaunchKernelGGL(gather_plan_kernel, dim3(1), dim3(kPlanWaves * 64), 0, st, ids, int(B), K, off, n_docs,
-                       n_rows_host, cap_rows, mem_off, plan, src_of_row);
-    hipError_t err = hipGetLastError();
+    int64_t* src_of_row = nullptr;
+    hipError_t err = launch_gather_plan(ids, B, K, off, n_docs, n_rows_host, cap_rows, mem_off, ws, &src_of_row, st);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(gather_copy_kernel, dim3(kCopyWgs), dim3(256), 0, st, static_cast<const u32x4*>(host),
                        int64_t(row_bytes / 16), src_of_row, mem_off, int(B), static_cast<u32x4*>(dst));

@@ -115,6 +115,27 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
 
 constexpr int kMaxGatherB = 1024;
 size_t gather_device_workspace(int64_t B, int64_t cap_rows);
+// The copy plan of the device gather (one workgroup): mem_off and, in the
+// workspace, the source row of every destination row (*src_of_row).
+hipError_t launch_gather_plan(const int32_t* ids, int64_t B, int K, const int64_t* off, int64_t n_docs,
+                              int64_t n_rows_host, int64_t cap_rows, int64_t* mem_off, void* ws,
+                              int64_t** src_of_row, hipStream_t st);
+
+// The device gather's copy as the gather + local-attention launch runs it:
+// the one-query copy (it plans itself from ids and off, and writes mem_off)
+// or the bounded copy of a plan (src_of_row; mem_off[B] rows in all).
+struct GatherCopyArgs {
+    const u32x4* host;
+    int64_t row_vecs;
+    const int64_t* src_of_row;
+    int B;
+    const int32_t* ids;
+    int K;
+    const int64_t* off;
+    int64_t n_docs, n_rows_host, cap;
+    int64_t* mem_off;
+    u32x4* dst;
+};
 hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_rows_host, const int64_t* off,
                                 int64_t n_docs, const int32_t* ids, int64_t B, int K, void* dst,
                                 int64_t cap_rows, int64_t* mem_off, void* ws, hipStream_t st);
@@ -122,5 +143,22 @@ hipError_t launch_gather_device(const void* host, size_t row_bytes, int64_t n_ro
 size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
                       int64_t max_rows, int L, int num_cus);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+// The device gather followed by the attention over its rows (a.KVmem is the
+// gather's destination of cap_rows rows, a.mem_off its output, a.ws the
+// workspace of gather_attn_workspace bytes).
+struct GatherAttnArgs {
+    AttnArgs a;
+    const void* host;
+    size_t row_bytes;
+    int64_t n_rows_host;
+    const int64_t* off;
+    int64_t n_docs;
+    const int32_t* ids;
+    int K;
+    int64_t cap_rows;
+};
+size_t gather_attn_workspace(const AttnArgs& a, int64_t cap_rows);
+hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st);
 
 }  // namespace msa
