@@ -31,16 +31,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "long_context_memory_chunk_amd", "csrc")
 
 # HBM counter calibration: for a plain 4 GiB device-to-device copy (bench.py
-# --workload hbmcopy under rocprofv3 --pmc), FETCH_SIZE reads 2,097,168.3 KiB per
+# --workload hbmcopy under rocprofv3 --pmc), FETCH_SIZE reads 2,097,166.5 KiB per
 # dispatch (mean of the 11 full-size copies) for the 4,194,304 KiB read,
 # WRITE_SIZE reads 4,194,304 KiB for the 4,194,304 KiB written.
-FETCH_SCALE = 4194304.0 / 2097168.3
+FETCH_SCALE = 4194304.0 / 2097166.5
 WRITE_SCALE = 1.0
 # FETCH_SIZE / WRITE_SIZE of the routing scan on the 100M-token bank (KiB per
-# dispatch, mean over 108 dispatches), taken on the sources whose digest is
+# dispatch, mean over 162 dispatches), taken on the sources whose digest is
 # given; a different digest means the kernel has changed since, and the
 # traffic is reported as unknown.
-SCAN_COUNTERS = {"digest": "b46ebaeee6a7784a", "fetch_kib": 1562594.9, "write_kib": 6103.5}
+SCAN_COUNTERS = {"digest": "f9a23ce27e6ea7c9", "fetch_kib": 1562584.2, "write_kib": 6103.5}
 SCAN_SOURCES = ("route_scan.hip", "common.hpp")     # the scan kernel, its launch and device helpers
 
 
