@@ -184,7 +184,8 @@ def test_chunk_level_topk_100m_layer(env):
 def test_batch32_10m_layer_full_oracle(env):
     """32 single-token queries against one layer of the 10M-token bank
     (156,250 chunk rows, ~20K documents), matrix-core routing: every query's
-    top-16 against the oracle over every chunk; device gather; attention."""
+    top-16 against the oracle over every chunk; device gather; attention,
+    both as two calls and as msa_gather_attn."""
     torch, msa, device, ctx = env
     seed, k, B, L = 0, 16, 32, 2048
     lens = msa_synth.lognormal_lengths(seed, 10_000_000)
@@ -239,6 +240,7 @@ def test_batch32_10m_layer_full_oracle(env):
     torch.cuda.synchronize()
     mo_np = mo.cpu().numpy()
     got_o = W.widen(W.host_bits(O), "bf16")
+    refs = {}
     for b in (0, 7, 31):
         sel = sorted(int(d) for d in ids_ref[b])
         rows = np.concatenate([msa_synth.counter_bf16(seed, W.kvbar_stream(0), int(coff[d]) * 2 * Hkv * D,
@@ -251,6 +253,24 @@ def test_batch32_10m_layer_full_oracle(env):
         ref = oracle.sparse_attn(W.widen(Qh[b:b + 1], "bf16"), kv[:, 0], kv[:, 1], [0, len(kv)], klb[None],
                                  vlb[None], k, 1 / math.sqrt(D), 1e6)
         P.assert_attn_close(got_o[b], ref[0], 2e-2, f"batch32 query {b}")
+        refs[b] = ref[0]
+
+    # the same layer through msa_gather_attn, as the batched decode step runs
+    # it (the copy beside the local keys' attention): the same rows and
+    # offsets, the same attention within rounding, and the oracle's bar
+    dst2 = torch.empty_like(dst)
+    mo2 = torch.zeros_like(mo)
+    O2 = torch.empty_like(O)
+    wsga = msa.workspace(msa.msa_gather_attn_workspace_size(1, B, 1, Hq, Hkv, k, cap, max_rows, L))
+    msa.msa_gather_attn(ctx, host, 2 * Hkv * D * 2, N, coff_dev, ids, dst2, cap, mo2, W.dev_bf16(Qh), max_rows,
+                        Kl, Vl, k, 1 / math.sqrt(D), O2, wsga)
+    torch.cuda.synchronize()
+    assert np.array_equal(mo2.cpu().numpy(), mo_np)
+    assert np.array_equal(W.host_bits(dst2[:mo_np[B]]), W.host_bits(dst[:mo_np[B]]))
+    got_o2 = W.widen(W.host_bits(O2), "bf16")
+    for b, ref in refs.items():
+        P.assert_attn_close(got_o2[b], ref, 2e-2, f"batch32 query {b}, one call")
+    assert float(np.max(np.abs(got_o2 - got_o))) <= 1e-2
 
 
 @pytest.mark.timeout(900)
