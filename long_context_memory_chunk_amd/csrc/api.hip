@@ -740,7 +740,8 @@ msa_status msa_gather_attn(msa_ctx* ctx, msa_dtype dt, const void* host_KVbar, s
     msa::GatherAttnArgs ga{msa::AttnArgs{dt, Q, B, Tq, Hq, Hkv, ctx->head_dim, L, dst_KVmem, mem_off, cap_rows,
                                          max_rows_per_query, K_local, V_local, q_offset, scale, O, workspace,
                                          ws_bytes, ctx->rope_cs, ctx->max_pos, ctx->num_cus, nullptr},
-                           host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids, top_k, cap_rows};
+                           dst_KVmem, mem_off, host_KVbar, row_bytes, n_rows_host, doc_chunk_off, n_docs, ids,
+                           top_k, cap_rows};
     const size_t need = msa::gather_attn_workspace(ga.a, cap_rows);
     if (!workspace || !aligned256(workspace) || ws_bytes < need)
         return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-aligned (got %zu)", fn, need,

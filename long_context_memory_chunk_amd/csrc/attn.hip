@@ -424,22 +424,21 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
     const GatherAttnPlan g = gather_attn_plan(a, ga.cap_rows);
     hipError_t err;
     if (!g.fused) {
-        err = launch_gather_device(ga.host, ga.row_bytes, ga.n_rows_host, ga.off, ga.n_docs, ga.ids, a.B, ga.K,
-                                   const_cast<void*>(a.KVmem), ga.cap_rows, const_cast<int64_t*>(a.mem_off), a0.ws, st);
+        err = launch_gather_device(ga.host, ga.row_bytes, ga.n_rows_host, ga.off, ga.n_docs, ga.ids, a.B, ga.K, ga.dst,
+                                   ga.cap_rows, ga.mem_off, a0.ws, st);
         if (err != hipSuccess) return err;
         return launch_attn(a, st);
     }
     GatherCopyArgs gc{static_cast<const u32x4*>(ga.host), int64_t(ga.row_bytes / 16), nullptr, int(a.B), ga.ids, ga.K,
-                      ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, const_cast<int64_t*>(a.mem_off),
-                      static_cast<u32x4*>(const_cast<void*>(a.KVmem))};
+                      ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, ga.mem_off, static_cast<u32x4*>(ga.dst)};
     int n_copy = kCopyWgs;
     if (g.one) {
         const int64_t w = ceil_div(ga.cap_rows, int64_t(kOneRows));
         n_copy = int(w > 0 ? w : 1);
     } else {
         int64_t* src_of_row = nullptr;
-        err = launch_gather_plan(ga.ids, a.B, ga.K, ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows,
-                                 const_cast<int64_t*>(a.mem_off), a0.ws, &src_of_row, st);
+        err = launch_gather_plan(ga.ids, a.B, ga.K, ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, ga.mem_off, a0.ws,
+                                 &src_of_row, st);
         if (err != hipSuccess) return err;
         gc.src_of_row = src_of_row;
     }

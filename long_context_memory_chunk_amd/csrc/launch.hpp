@@ -144,11 +144,14 @@ size_t attn_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D,
                       int64_t max_rows, int L, int num_cus);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 
-// The device gather followed by the attention over its rows (a.KVmem is the
-// gather's destination of cap_rows rows, a.mem_off its output, a.ws the
-// workspace of gather_attn_workspace bytes).
+// The device gather followed by the attention over its rows: dst (cap_rows
+// rows) and mem_off are the gather's outputs, which the attention then reads
+// (a.KVmem == dst, a.mem_off == mem_off); a.ws is the workspace of
+// gather_attn_workspace bytes.
 struct GatherAttnArgs {
     AttnArgs a;
+    void* dst;
+    int64_t* mem_off;
     const void* host;
     size_t row_bytes;
     int64_t n_rows_host;

@@ -413,8 +413,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     uint64_t* wmax = reinterpret_cast<uint64_t*>(ws + w.wmax_off);
     hipError_t err;
 
-    // 1. unit-query group sums
-    if ((err = launch_route_prep(a, U, st)) != hipSuccess) return err;
+    // 1. unit-query group sums (the matrix-core path of decode batches and
+    // short queries forms them itself, in its bf16 operand layout)
+    if (!(a.N > 0 && !route_scan_fast_applicable(a) && route_mfma_preps_itself(a)))
+        if ((err = launch_route_prep(a, U, st)) != hipSuccess) return err;
 
     // 2. chunk scores c[B][N]; the chunk-score kernel's dispatch records the
     // profiling events itself (an empty bank records them back to back)

@@ -59,6 +59,54 @@ __global__ __launch_bounds__(256) void u_to_bf16_kernel(const float* __restrict_
     Ub[i] = (src >= 0) ? f32_to_bf16(U[src * row_elems + i % row_elems]) : uint16_t(0);
 }
 
+// route_prep and the bf16 rounding in one launch, for route_mfma_kernel:
+// padded row p, group g of Ub holds U[q][g] = sum_{h in g} q_h / max(|q_h|,
+// eps) of query token q = u_src_row(p), rounded to bf16 (zeros for a padding
+// row).  bf16 rows of 128: lane l loads the 16-byte slot l % 16 of head l / 16
+// of a batch of four heads (one 1 KB wave load per batch), each head's norm is
+// a 16-lane sum, the four partial rows meet by two shuffles, and lanes 0..15
+// store the group's 128 values.  The head sum is taken in the order of
+// route_prep's 16-byte form, so Ub holds the bits u_to_bf16 would give.
+__global__ __launch_bounds__(256) void route_prep_ub_kernel(const u32x4* __restrict__ Qr, int64_t B, int Tq,
+                                                            int Tq_pad, int64_t n_items, int Hq, int hkv,
+                                                            u32x4* __restrict__ Ub) {
+    const int G = Hq / hkv;
+    const int lane = threadIdx.x % kWave, sub = lane / 16, c = lane % 16;
+    for (int64_t it = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave; it < n_items; it += int64_t(gridDim.x) * 4) {
+        const int64_t prow = it / hkv;
+        const int g = int(it % hkv);
+        const int64_t q = u_src_row(prow, B, Tq, Tq_pad);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        if (q >= 0) {
+            for (int h0 = g * G; h0 < (g + 1) * G; h0 += 4) {
+                const int h = h0 + sub;
+                u32x4 w = {0u, 0u, 0u, 0u};
+                if (h < (g + 1) * G) w = Qr[(q * Hq + h) * 16 + c];
+                float x[8];
+                x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+                x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+                float n2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) n2 += x[e] * x[e];
+                n2 = group_sum<16>(n2);
+                const float inv = 1.f / fmaxf(sqrtf(n2), kEps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += x[e] * inv;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[e] += __shfl_xor(acc[e], 16);
+            acc[e] += __shfl_xor(acc[e], 32);
+        }
+        if (sub == 0)
+            Ub[(prow * hkv + g) * 16 + c] = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    }
+}
+
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear id, and
 // each XCD has its own L2.  Consecutive workgroups of one XCD take the tiles of
 // one super-tile of SQ query tiles x SC chunk tiles, so the tiles in flight on
@@ -580,6 +628,11 @@ bool route_mfma_applicable(msa_dtype dt, int64_t B, int Tq, int Hkv, int D) {
     return B * Tq > 4;                             // the streaming scan handles decode
 }
 
+bool route_mfma_preps_itself(const RouteArgs& a) {
+    return route_mfma_applicable(a.dt, a.B, a.Tq, a.Hkv, a.D) && !plan_for(a.B, a.Tq, a.Hkv, a.N).gemm &&
+           (reinterpret_cast<uintptr_t>(a.Qr) & 15u) == 0;
+}
+
 size_t route_mfma_workspace(msa_dtype dt, int64_t B, int Tq, int Hq, int Hkv, int D, int64_t N, int) {
     (void)Hq;
     if (!route_mfma_applicable(dt, B, Tq, Hkv, D)) return 0;
@@ -615,8 +668,17 @@ hipError_t launch_route_mfma(const RouteArgs& a, const float* U, float* c, void*
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes);
     float* rn = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ub_bytes + p.partial_bytes);
     const int64_t n_pad = p.q_pad * a.Hkv * 128;
-    hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, a.B, a.Tq,
-                       p.tq_pad, a.Hkv * 128, n_pad, Ub);
+    if (route_mfma_preps_itself(a)) {             // U is formed here, straight into the padded bf16 operand
+        const int64_t items = p.q_pad * a.Hkv;
+        int64_t blocks = ceil_div(items, int64_t(4));
+        if (blocks > int64_t(a.num_cus) * 8) blocks = int64_t(a.num_cus) * 8;
+        hipLaunchKernelGGL(route_prep_ub_kernel, dim3(unsigned(blocks < 1 ? 1 : blocks)), dim3(256), 0, st,
+                           static_cast<const u32x4*>(a.Qr), a.B, a.Tq, p.tq_pad, items, a.Hq, a.Hkv,
+                           reinterpret_cast<u32x4*>(Ub));
+    } else {
+        hipLaunchKernelGGL(u_to_bf16_kernel, dim3(unsigned(ceil_div(n_pad, 256))), dim3(256), 0, st, U, a.B, a.Tq,
+                           p.tq_pad, a.Hkv * 128, n_pad, Ub);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const TileOrder ord = tile_order(p.q_tiles, ceil_div(a.N, p.bn));
