@@ -108,6 +108,9 @@ CASES = [
     (64, 2, 1, 16, 2, 257, [300, 1], 3),                # G = 8, a ragged local tail
     (65, 2, 2, 8, 4, 128, [64, 65], 4),                 # G = 2
     (66, 8, 1, 32, 8, 2048, [60, 200, 130, 90, 1, 170, 150, 77], 16),
+    (70, 1, 63, 32, 8, 300, [90], 6),                  # Tq = 63: the largest query block on the fused path
+    (71, 1, 64, 32, 8, 256, [100], 8),                 # Tq = 64: the prefill kernel, after the gather
+    (72, 2, 3, 32, 2, 200, [30, 70], 5),               # G = 16: the split kernel, after the gather
 ]
 
 
