@@ -102,8 +102,8 @@ struct DecodeArgs {
 };
 
 // Key ranges: every key of the row, only its local keys (memory rows taken as
-// absent: KVmem is not read, and mem_off is read but not used), or only its
-// memory rows.  The query keeps its position in every case.
+// absent: neither KVmem nor mem_off is read), or only its memory rows.  The
+// query keeps its position in every case.
 enum DecodeKeys : int { kKeysAll = 0, kKeysLocal = 1, kKeysMem = 2 };
 
 // One workgroup: partition p (chunks p * NC ..) of (query token bt, KV head g);
@@ -130,9 +130,10 @@ __device__ __forceinline__ void decode_wg(
     const int64_t b = bt / Tq;
     const int i = int(bt % Tq);
 
-    int64_t r0, M;
-    mem_range(mem_off, b, cap, max_rows, r0, M);
-    if (kRanged) M *= use_mem;                    // (the all-keys kernel is compiled without the range)
+    int64_t r0 = 0, M = 0;
+    // (the all-keys kernel is compiled without the range; a local-keys range
+    // does not read mem_off, which a copy in the same launch may be writing)
+    if (!kRanged || use_mem) mem_range(mem_off, b, cap, max_rows, r0, M);
     const int64_t total = M + (kRanged ? use_local : 1) * (int64_t(L - Tq) + i + 1);
     const int64_t row_elems = int64_t(hkv) * DH;
     const int64_t hrow = bt * Hq + int64_t(g) * G;   // first query head row of this group
