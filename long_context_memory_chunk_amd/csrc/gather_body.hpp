@@ -48,21 +48,35 @@ __device__ __forceinline__ void gather_copy_wg(const u32x4* __restrict__ host, i
                                                const int64_t* __restrict__ mem_off, int B,
                                                u32x4* __restrict__ dst, int wg, int n_wgs) {
     const int64_t total = mem_off[B];
-    for (int64_t r0 = int64_t(wg) * kCopyRows; r0 < total; r0 += int64_t(n_wgs) * kCopyRows) {
-        int64_t src[kCopyRows];
+    const int64_t stride = int64_t(n_wgs) * kCopyRows;
+    int64_t src[kCopyRows];
+    int64_t r0 = int64_t(wg) * kCopyRows;
 #pragma unroll
-        for (int j = 0; j < kCopyRows; ++j) src[j] = (r0 + j < total) ? src_of_row[r0 + j] : -1;
+    for (int j = 0; j < kCopyRows; ++j) src[j] = (r0 + j < total) ? src_of_row[r0 + j] : -1;
+    for (; r0 < total; r0 += stride) {
+        // the next round's source rows are read while this round's first
+        // units come over PCIe, so a round waits on no HBM read of its own
+        // (every thread takes the first pass, row_vecs >= 1; units past the
+        // row are skipped, not broken out of)
+        int64_t nxt[kCopyRows];
         for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
             const int64_t v = v0 + threadIdx.x;
-            if (v >= row_vecs) break;
+            const bool on = v < row_vecs;
             u32x4 x[kCopyRows];
 #pragma unroll
             for (int j = 0; j < kCopyRows; ++j)
-                if (src[j] >= 0) x[j] = host[src[j] * row_vecs + v];
+                if (on && src[j] >= 0) x[j] = host[src[j] * row_vecs + v];
+            if (v0 == 0) {
+#pragma unroll
+                for (int j = 0; j < kCopyRows; ++j)
+                    nxt[j] = (r0 + stride + j < total) ? src_of_row[r0 + stride + j] : -1;
+            }
 #pragma unroll
             for (int j = 0; j < kCopyRows; ++j)
-                if (src[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
+                if (on && src[j] >= 0) dst[(r0 + j) * row_vecs + v] = x[j];
         }
+#pragma unroll
+        for (int j = 0; j < kCopyRows; ++j) src[j] = nxt[j];
     }
 }
 
