@@ -835,6 +835,43 @@ def test_gather_random_layouts(torch_mod, msa, ctx128, row_elems, n_docs, maxc, 
     assert mo_np[B] == cap
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_gather_device_both_plans(torch_mod, msa, ctx128, B):
+    """64 queries take the plan with one workgroup per query, 65 the plan
+    with one workgroup for all: the same rows and offsets as the oracle's
+    indexing either way, with an invalid id and a capacity that cuts the
+    last query short."""
+    torch = torch_mod
+    rng = np.random.default_rng(300 + B)
+    n_docs, k, row_elems = 300, 12, 64
+    coff = msa_synth.prefix_offsets(rng.integers(1, 9, size=n_docs))
+    N = int(coff[-1])
+    bank = msa_synth.counter_bf16(300 + B, 3, 0, N * row_elems).reshape(N, row_elems)
+    host = torch.empty((N, row_elems), dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    ids = np.stack([rng.permutation(n_docs)[:k] for _ in range(B)]).astype(np.int32)
+    ids[3, 5] = -1                                   # an invalid id copies nothing
+    valid = [ids[b][ids[b] >= 0] for b in range(B)]
+    full = int(sum(np.diff(coff)[v].sum() for v in valid))
+    cap = full - 3                                   # the last query's rows cut short
+    dst = torch.zeros((cap, row_elems), dtype=torch.bfloat16, device="cuda")
+    mo = torch.zeros(B + 1, dtype=torch.int64, device="cuda")
+    ws = msa.workspace(msa.msa_gather_device_workspace_size(B, k, cap))
+    msa.msa_gather_device(ctx128, host, row_elems * 2, N, torch.from_numpy(coff).cuda(),
+                          torch.from_numpy(ids).cuda(), dst, cap, mo, ws)
+    torch.cuda.synchronize()
+    mo_np = mo.cpu().numpy()
+    got = W.host_bits(dst)
+    start = 0
+    for b in range(B):
+        ref, m = oracle.gather_rows(bank, coff, valid[b])
+        end = min(start + m, cap)
+        assert mo_np[b] == min(start, cap) and mo_np[b + 1] == end, b
+        assert np.array_equal(got[start:end], ref[:end - start]), b
+        start += m
+    assert mo_np[B] == cap
+
+
 def test_gather_device_skips_invalid_ids_and_clamps_to_capacity(torch_mod, msa, ctx128):
     torch = torch_mod
     coff = np.array([0, 3, 5, 9, 10], dtype=np.int64)
