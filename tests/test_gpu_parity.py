@@ -468,6 +468,46 @@ def test_route_is_deterministic(torch_mod, msa, ctx128):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("B,Tq", [(1, 1), (3, 1), (8, 1), (2, 5), (1, 256)])
+def test_route_query_not_16_byte_aligned(torch_mod, msa, ctx128, B, Tq):
+    """A query tensor that starts 2 bytes past a 16-byte boundary (a view one
+    element into a buffer): the operand prep takes its element-wise form on the
+    streaming scan (B*Tq <= 4), the matrix cores (decode batch, short blocks)
+    and the token-tile GEMM alike, with the same chunk scores and selection as
+    the oracle (neo-ai.one MSA article, 全体設計 › アーキテクチャ, Fig. 2: cosine,
+    head mean, token max, top-k)."""
+    torch = torch_mod
+    Hq, Hkv, d, k = 32, 8, 128, 12
+    counts = np.random.default_rng(B * 100 + Tq).integers(1, 11, size=180)
+    coff = msa_synth.prefix_offsets(counts)
+    N = int(coff[-1])
+    Kb = _bank("bf16", N, Hkv, d, 63)
+    Qr = msa_synth.normal_bf16(64 + B, Tq, (B, Tq, Hq, d))
+    flat = torch.empty(Qr.size + 1, dtype=torch.bfloat16, device="cuda")
+    flat[1:].copy_(W.dev_bf16(Qr.reshape(-1)))
+    Qd = flat[1:].view(B, Tq, Hq, d)
+    assert Qd.data_ptr() % 16 == 2
+    ws = msa.workspace(msa.msa_route_workspace_size(1, B, Tq, Hq, Hkv, N, len(coff) - 1, k))
+    ids = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    ch = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    dc = torch.empty((B, len(coff) - 1), dtype=torch.float32, device="cuda")
+    msa.msa_route(ctx128, Qd, W.dev_bf16(Kb), torch.from_numpy(coff).cuda(), k, ids, ws, out_scores=sc,
+                  out_chunk=ch, out_doc=dc)
+    torch.cuda.synchronize()
+    ids, sc, ch, dc = ids.cpu().numpy(), sc.cpu().numpy(), ch.cpu().numpy(), dc.cpu().numpy()
+    c_ref = oracle.chunk_scores(W.widen(Qr, "bf16"), W.widen(Kb, "bf16"))
+    D_ref = oracle.doc_scores(c_ref, coff)
+    tol = _score_tol("bf16", d, B, Tq)
+    assert np.max(np.abs(ch - c_ref)) <= tol
+    assert np.max(np.abs(dc - D_ref)) <= tol
+    for b in range(B):
+        _check_valid_topk(ids[b], sc[b], D_ref[b], tol)
+    # the aligned call on the same values: the same chunk scores within the path's tolerance
+    _, _, ch_a, _ = _run_route(torch, msa, ctx128, Qr, Kb, coff, k, "bf16")
+    assert np.max(np.abs(ch - ch_a)) <= tol
+
+
 # ---------------------------------------------------------------- stage 2b
 
 def test_gather_matches_oracle_indexing(torch_mod, msa):
