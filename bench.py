@@ -5,13 +5,19 @@ Workload (the 100M-token memory): documents with log-normal lengths
 (median 400 tokens, log-sd 0.67, clipped to [64, 8192], multiples of 64)
 summing to 100M tokens, pooled with chunk 64 into N = 1,562,500 rows per
 layer; 18 routing layers of K̄r [N][8][128] bf16 (57.6 GB) resident in HBM;
-pooled K̄/V̄ [N][2][8][128] bf16 of the routing layers (115.2 GB) in pinned
-host memory; 16 planted documents per layer (a different set in every layer,
-planted against that layer's own query); top-k 16; a 1-token decode query with 2,048 local
+pooled K̄/V̄ [N][2][8][128] bf16 in pinned host memory, one block per
+routing layer (115.2 GB), or as many blocks as the host lets the process
+page-lock, routing layer l then reading block l mod that count; 16 planted
+documents per layer (a different set in every layer, planted against that
+layer's own query); top-k 16; a 1-token decode query with 2,048 local
 tokens.  One step = for each of the 18 layers: route (scan K̄r, document
-max, top-16) -> ids to the host -> gather the 16 documents' K̄/V̄ rows from
-the host store (hipMemcpyAsync on a side stream) -> sparse GQA attention
-over [gathered rows ; local K/V].  All inputs are synthetic and seeded.
+max, top-16, the ids staying on the GPU) -> a kernel gathers the 16
+documents' K̄/V̄ rows from the pinned host store over PCIe
+(msa_gather_device) -> sparse GQA attention over [gathered rows ; local
+K/V].  The same step is also timed with the gather and the attention in one
+call (msa_gather_attn) and with the hipMemcpyAsync gather (msa_gather, the
+ids copied to the host); both are reported beside the headline.  All inputs
+are synthetic and seeded.
 
 Prints one JSON line.  `value` is K̄r bytes routed per second of whole
 routed-decode step (18 layers x N x 2 KiB per step / step time).
