@@ -137,6 +137,39 @@ def test_gather_attn_matches_oracle(env, seed, B, Tq, Hq, Hkv, L, rows, k):
     assert diff <= 1e-2 * max(1.0, float(np.max(np.abs(ref))))
 
 
+def _random_cases(n, seed):
+    """Seeded shapes over both copies (one query; the plan and bounded copy
+    for B > 1): 1-40 queries of 1-3 tokens, group sizes 1-8 over 1-8 KV
+    heads, local contexts of up to 1,500 keys, 0-300 memory rows per query in
+    1-16 documents."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = 1 if i % 3 == 0 else int(rng.integers(2, 41))
+        Tq = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(Tq, 1501))
+        rows = [int(r) if rng.random() > 0.15 else 0 for r in rng.integers(1, 301, size=B)]
+        if B == 1 and rows[0] == 0:
+            rows[0] = 1
+        cases.append((900 + i, B, Tq, G * Hkv, Hkv, L, rows, int(rng.integers(1, 17))))
+    return cases
+
+
+@pytest.mark.parametrize("seed,B,Tq,Hq,Hkv,L,rows,k", _random_cases(9, 77))
+def test_gather_attn_random_shapes(env, seed, B, Tq, Hq, Hkv, L, rows, k):
+    torch, msa, ctx = env
+    w = P.peaked_inputs(seed, B, Tq, Hq, Hkv, D, L, rows, k, P.THETA, tokens=list(range(Tq)))
+    bank, coff, ids, got_rows, mo, got = _run(torch, msa, ctx, w, k, seed)
+    want_off = np.asarray(w["mem_off"], dtype=np.int64)
+    assert np.array_equal(mo, want_off)
+    for b in range(B):
+        ref_rows, _ = oracle.gather_rows(bank, coff, ids[b])
+        assert np.array_equal(oracle.f64_to_bf16_bits(got_rows[mo[b]:mo[b + 1]]), ref_rows)
+    P.assert_attn_close(got, P.oracle_out(w), 2e-2, f"gather_attn random B={B} Tq={Tq} G={Hq // Hkv} L={L}")
+
+
 def test_gather_attn_fp32_takes_the_two_step_path(env):
     """fp32 (not on the fused path): the gather then the vector-unit attention, bar 1e-3."""
     torch, msa, ctx = env
