@@ -461,7 +461,9 @@ msa_status msa_sparse_attn_bwd(msa_ctx* ctx, msa_dtype dt,
  * The local keys need none of the gathered rows, so for decode rows (bf16,
  * d 128, Hq/Hkv in {1, 2, 4, 8}, Tq < 64) their attention runs in the same
  * launch as the PCIe copy, and the memory rows' attention and the merge of
- * both follow it; other shapes run the gather and then the attention.
+ * both follow it (for one query of one token with Hkv <= 8, the workgroups
+ * that copy the memory rows also attend over them, in fp32, so only the
+ * merge follows); other shapes run the gather and then the attention.
  * Arguments: those of msa_gather_device (host_KVbar .. mem_off, with
  * B = the queries) followed by those of msa_sparse_attn (Q .. O; KVmem is
  * dst_KVmem and mem_rows_cap is cap_rows), with the same meaning, layout,

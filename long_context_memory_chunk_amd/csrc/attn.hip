@@ -385,19 +385,33 @@ namespace {
 
 struct GatherAttnPlan {
     bool fused, one;
-    DecodePlan loc, mem;     // mem.P == 0: no memory rows
+    bool mem_in_copy;        // the one-query copy forms the memory rows' partials
+    int n_copy;              // copy workgroups
+    DecodePlan loc, mem;     // mem.P == 0: no launch over the memory rows
     int P_total;
 };
 
 GatherAttnPlan gather_attn_plan(const AttnArgs& a, int64_t cap_rows) {
-    GatherAttnPlan g{false, false, {0, 0}, {0, 0}, 0};
+    GatherAttnPlan g{false, false, false, kCopyWgs, {0, 0}, {0, 0}, 0};
     if (!decode_applicable(a.dt, a.D, a.Hq, a.Hkv, a.max_rows, a.L) || attn_mfma_applicable(a)) return g;
     g.loc = decode_plan(a.B, a.Tq, a.Hkv, 0, a.L, a.num_cus);
-    if (a.max_rows > 0) g.mem = decode_plan(a.B, a.Tq, a.Hkv, a.max_rows, 0, a.num_cus);
-    g.P_total = g.loc.P + g.mem.P;
+    g.one = a.B == 1 && cap_rows <= kOneMaxRows;
+    if (g.one) {
+        // a one-token query with at most 8 KV heads (a row of at most 256
+        // 16-byte units): the copy workgroups attend over their own rows
+        const int64_t w = ceil_div(cap_rows, int64_t(kOneAttnRows));
+        g.mem_in_copy = a.Tq == 1 && a.Hkv <= 8 && a.max_rows > 0 && g.loc.P + w <= kMaxParts;
+        const int64_t n = g.mem_in_copy ? w : ceil_div(cap_rows, int64_t(kOneRows));
+        g.n_copy = int(n > 0 ? n : 1);
+    }
+    if (g.mem_in_copy) {
+        g.P_total = g.loc.P + g.n_copy;
+    } else {
+        if (a.max_rows > 0) g.mem = decode_plan(a.B, a.Tq, a.Hkv, a.max_rows, 0, a.num_cus);
+        g.P_total = g.loc.P + g.mem.P;
+    }
     if (g.P_total > kMaxParts) return g;                     // the combine's bound
     g.fused = true;
-    g.one = a.B == 1 && cap_rows <= kOneMaxRows;
     return g;
 }
 
@@ -431,11 +445,7 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
     }
     GatherCopyArgs gc{static_cast<const u32x4*>(ga.host), int64_t(ga.row_bytes / 16), nullptr, int(a.B), ga.ids, ga.K,
                       ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, ga.mem_off, static_cast<u32x4*>(ga.dst)};
-    int n_copy = kCopyWgs;
-    if (g.one) {
-        const int64_t w = ceil_div(ga.cap_rows, int64_t(kOneRows));
-        n_copy = int(w > 0 ? w : 1);
-    } else {
+    if (!g.one) {
         int64_t* src_of_row = nullptr;
         err = launch_gather_plan(ga.ids, a.B, ga.K, ga.off, ga.n_docs, ga.n_rows_host, ga.cap_rows, ga.mem_off, a0.ws,
                                  &src_of_row, st);
@@ -445,7 +455,8 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
     const size_t rows = size_t(a.B) * a.Tq * a.Hq * g.P_total;
     float* part_o = static_cast<float*>(a.ws);
     float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align256(rows * a.D * sizeof(float)));
-    err = launch_gather_local_attn(gc, g.one, n_copy, a, part_o, part_ml, g.loc.P, g.loc.nc, g.P_total, st);
+    err = launch_gather_local_attn(gc, g.one, g.mem_in_copy, g.n_copy, a, part_o, part_ml, g.loc.P, g.loc.nc,
+                                   g.P_total, st);
     if (err != hipSuccess) return err;
     if (g.mem.P > 0) {
         err = launch_decode_mfma_mem(a, part_o, part_ml, g.mem.P, g.mem.nc, g.loc.P, g.P_total, st);

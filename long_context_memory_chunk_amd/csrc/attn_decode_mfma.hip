@@ -488,6 +488,123 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_range_kernel(D
     decode_ranged<G>(da, int(blockIdx.x), int(blockIdx.y), int64_t(blockIdx.z));
 }
 
+// The eight bf16 values of a 16-byte unit (the dwords unpacked by name).
+__device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
+    const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    f[0] = bf16_lo(w0); f[1] = bf16_hi(w0); f[2] = bf16_lo(w1); f[3] = bf16_hi(w1);
+    f[4] = bf16_lo(w2); f[5] = bf16_hi(w2); f[6] = bf16_lo(w3); f[7] = bf16_hi(w3);
+}
+
+// One-query copy of destination rows wg * R .. wg * R + R - 1 that also forms
+// the attention partial of those rows for every query head of a one-token
+// query (index pp of its row's partials), so that the memory rows need no
+// launch of their own after the copy.  A row is [K̄ ; V̄] of hkv heads, 32 hkv
+// <= 256 units of 16 bytes: thread t copies unit t of every row and keeps it.
+// Thread 16 g + c (t < 16 hkv) holds dimensions 8c .. 8c+7 of K̄ head g: it
+// rotates the G query heads of group g at those dimensions (their RoPE
+// partners 8 (c ^ 8) .. come from the same query row), forms its share of
+// each row's score and sums the 16 shares of the group (fp32 throughout),
+// and the group's lane 0 hands the probabilities to the V̄ threads through
+// LDS; thread 16 hkv + 16 g + c then accumulates dimensions 8c .. 8c+7 of
+// the G heads' outputs.  A workgroup with no rows writes an empty partial.
+template <int G>
+__device__ __forceinline__ void gather_one_attn_wg(const GatherCopyArgs& gc, const DecodeArgs& da, int wg, int pp) {
+    constexpr int R = kOneAttnRows;
+    __shared__ float s_p[8][G][R];
+    int64_t sr[R];
+    gather_one_plan<R>(gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off, wg, sr);
+    const int t = threadIdx.x;
+    const int64_t rv = gc.row_vecs;
+    const bool on = t < rv;
+    const int64_t r0 = int64_t(wg) * R;
+    u32x4 x[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        x[j] = u32x4{0u, 0u, 0u, 0u};
+        if (on && sr[j] >= 0) x[j] = gc.host[sr[j] * rv + t];
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        if (on && sr[j] >= 0) gc.dst[(r0 + j) * rv + t] = x[j];
+
+    const int P = da.P_total, kv_units = 16 * da.hkv, c = t % 16;
+    if (t < kv_units) {
+        const int g = t / 16;
+        int pos = da.q_offset + da.L - 1;          // the token's global position (Tq = 1)
+        pos = pos < da.max_pos ? pos : da.max_pos - 1;
+        const float2* cs = da.rope_cs + int64_t(pos) * (DH / 2) + 8 * (c % 8);
+        float s[R][G];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) s[j][hh] = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const uint16_t* qrow = da.Q + int64_t(g * G + hh) * DH;
+            float a[8], b[8], q[8];
+            unpack8(*reinterpret_cast<const u32x4*>(qrow + 8 * c), a);
+            unpack8(*reinterpret_cast<const u32x4*>(qrow + 8 * (c ^ 8)), b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 r = cs[e];
+                q[e] = (c < 8 ? a[e] * r.x - b[e] * r.y : a[e] * r.x + b[e] * r.y) * da.qscale;
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                float k[8];
+                unpack8(x[j], k);
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d += q[e] * k[e];
+                s[j][hh] = d;
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                s[j][hh] = group_sum<16>(s[j][hh]);
+                if (sr[j] < 0) s[j][hh] = -INFINITY;
+                m = fmaxf(m, s[j][hh]);
+            }
+            float l = 0.f, p[R];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                p[j] = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[j][hh] - m);
+                l += p[j];
+            }
+            if (c == 0) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) s_p[g][hh][j] = p[j];
+                // the combine takes m in natural-log units
+                da.part_ml[int64_t(g * G + hh) * P + pp] = make_float2(m == -INFINITY ? -INFINITY : m * kLn2D, l);
+            }
+        }
+    }
+    __syncthreads();
+    if (t >= kv_units && on) {
+        const int g = (t - kv_units) / 16;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const float pj = s_p[g][hh][j];
+                float v[8];
+                unpack8(x[j], v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] += pj * v[e];
+            }
+            float4* op = reinterpret_cast<float4*>(da.part_o + (int64_t(g * G + hh) * P + pp) * DH + 8 * c);
+            op[0] = make_float4(o[0], o[1], o[2], o[3]);
+            op[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
 // The device gather and the attention over the local keys in one launch: the
 // copy waits on PCIe and leaves most CUs idle, and the local keys (most of a
 // decode row's keys) need none of the gathered rows, so their partials are
@@ -496,13 +613,19 @@ __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void attn_decode_range_kernel(D
 // fastest).  The bounded copy goes first, since it is the longer; the
 // one-query copy (one workgroup per kOneRows rows) after the attention, so
 // that a large capacity cannot hold every slot before the attention starts.
+// With mem_in_copy (a one-token query) the one-query copy takes kOneAttnRows
+// rows per workgroup and also forms their partials (indices P + wg), so the
+// launch covers every key of the row.
 template <int G, bool kOne>
 __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void gather_local_attn_kernel(GatherCopyArgs gc, DecodeArgs da,
-                                                                              int P, int copy_first, int n_copy) {
+                                                                              int P, int copy_first, int n_copy,
+                                                                              int mem_in_copy) {
     const int bx = int(blockIdx.x);
     if (bx >= copy_first && bx < copy_first + n_copy) {
         const int wg = bx - copy_first;
-        if (kOne)
+        if (kOne && mem_in_copy)
+            gather_one_attn_wg<G>(gc, da, wg, P + wg);
+        else if (kOne)
             gather_one_wg(gc.host, gc.row_vecs, gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off,
                           gc.dst, wg);
         else
@@ -565,8 +688,9 @@ hipError_t launch_decode_mfma_mem(const AttnArgs& a, float* part_o, float2* part
     return launch_range(a, decode_args(a, kKeysMem, part_o, part_ml, nc, p_base, P_total), P, st);
 }
 
-hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int n_copy, const AttnArgs& a,
-                                    float* part_o, float2* part_ml, int P, int nc, int P_total, hipStream_t st) {
+hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, bool mem_in_copy, int n_copy,
+                                    const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, int P_total,
+                                    hipStream_t st) {
     const DecodeArgs da = decode_args(a, kKeysLocal, part_o, part_ml, nc, 0, P_total);
     const int64_t n_attn = int64_t(P) * a.Hkv * a.B * a.Tq;
     const unsigned grid = unsigned(n_attn + n_copy);
@@ -575,10 +699,10 @@ hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int n_co
     do {                                                                                                         \
         if (one)                                                                                                 \
             hipLaunchKernelGGL((gather_local_attn_kernel<GG, true>), dim3(grid), dim3(256), 0, st, gc, da, P,   \
-                               copy_first, n_copy);                                                             \
+                               copy_first, n_copy, int(mem_in_copy));                                           \
         else                                                                                                     \
             hipLaunchKernelGGL((gather_local_attn_kernel<GG, false>), dim3(grid), dim3(256), 0, st, gc, da, P,  \
-                               copy_first, n_copy);                                                             \
+                               copy_first, n_copy, 0);                                                          \
     } while (0)
     switch (a.Hq / a.Hkv) {
         case 1: MSA_GLA(1); break;

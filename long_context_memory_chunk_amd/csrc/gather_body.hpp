@@ -21,6 +21,9 @@ constexpr int kCopyRows = 8;
 // One-query copy: workgroup w copies destination rows w * kOneRows .. + kOneRows - 1.
 constexpr int kOneRows = 2;
 constexpr int64_t kOneMaxRows = 8192;   // larger capacities take the plan + bounded copy path
+// One-query copy that also attends over the rows it copies (a one-token
+// query, KV heads <= 8): destination rows per workgroup.
+constexpr int kOneAttnRows = 8;
 
 // Lane `src` of a 64-bit value, for a wave-uniform lane index (two scalar
 // reads instead of two LDS permutes).
@@ -80,15 +83,17 @@ __device__ __forceinline__ void gather_copy_wg(const u32x4* __restrict__ host, i
     }
 }
 
-// One-query copy by workgroup wg (256 threads): each wave derives the plan on
-// its own (wave-uniform results, no barrier): the K ids sorted, their row
-// counts and prefix sums; a destination row's entry is the last one starting
-// at or before it (a ballot).  Workgroup 0 also writes mem_off.
-__device__ __forceinline__ void gather_one_wg(const u32x4* __restrict__ host, int64_t row_vecs,
-                                              const int32_t* __restrict__ ids, int K,
-                                              const int64_t* __restrict__ off, int64_t n_docs,
-                                              int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
-                                              u32x4* __restrict__ dst, int wg) {
+// One-query plan for destination rows wg * R .. wg * R + R - 1 (256 threads):
+// each wave derives it on its own (wave-uniform results, no barrier): the K
+// ids sorted, their row counts and prefix sums; a destination row's entry is
+// the last one starting at or before it (a ballot).  sr[j] is the source row
+// of destination row wg * R + j, or -1 past the end.  Workgroup 0 also writes
+// mem_off.  Returns the number of destination rows.
+template <int R>
+__device__ __forceinline__ int64_t gather_one_plan(const int32_t* __restrict__ ids, int K,
+                                                   const int64_t* __restrict__ off, int64_t n_docs,
+                                                   int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
+                                                   int wg, int64_t (&sr)[R]) {
     const int lane = threadIdx.x % kWave;
     int32_t id = (lane < K) ? ids[lane] : 0x7FFFFFFF;
     if (id < 0 || id >= n_docs) id = 0x7FFFFFFF;          // invalid ids copy nothing
@@ -117,10 +122,9 @@ __device__ __forceinline__ void gather_one_wg(const u32x4* __restrict__ host, in
         mem_off[0] = 0;
         mem_off[1] = total;
     }
-    const int64_t r0 = int64_t(wg) * kOneRows;
-    int64_t sr[kOneRows];
+    const int64_t r0 = int64_t(wg) * R;
 #pragma unroll
-    for (int j = 0; j < kOneRows; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int64_t r = r0 + j;
         sr[j] = -1;
         if (r < total) {
@@ -130,6 +134,19 @@ __device__ __forceinline__ void gather_one_wg(const u32x4* __restrict__ host, in
             sr[j] = lane64(src, e) + (r - lane64(dst0, e));
         }
     }
+    return total;
+}
+
+// One-query copy by workgroup wg (256 threads): destination rows wg * kOneRows
+// .. + kOneRows - 1, planned by gather_one_plan.
+__device__ __forceinline__ void gather_one_wg(const u32x4* __restrict__ host, int64_t row_vecs,
+                                              const int32_t* __restrict__ ids, int K,
+                                              const int64_t* __restrict__ off, int64_t n_docs,
+                                              int64_t n_rows_host, int64_t cap, int64_t* __restrict__ mem_off,
+                                              u32x4* __restrict__ dst, int wg) {
+    int64_t sr[kOneRows];
+    gather_one_plan<kOneRows>(ids, K, off, n_docs, n_rows_host, cap, mem_off, wg, sr);
+    const int64_t r0 = int64_t(wg) * kOneRows;
     for (int64_t v0 = 0; v0 < row_vecs; v0 += 256) {
         const int64_t v = v0 + threadIdx.x;
         if (v >= row_vecs) break;

@@ -170,6 +170,35 @@ def test_gather_attn_random_shapes(env, seed, B, Tq, Hq, Hkv, L, rows, k):
     P.assert_attn_close(got, P.oracle_out(w), 2e-2, f"gather_attn random B={B} Tq={Tq} G={Hq // Hkv} L={L}")
 
 
+@pytest.mark.parametrize("seed,Hq,Hkv,rows,k,cap_extra", [
+    (930, 32, 8, [1], 1, 0),        # one memory row
+    (931, 32, 8, [8], 2, 0),        # exactly one copy workgroup's rows
+    (932, 32, 8, [9], 3, 0),        # a second workgroup with one row
+    (933, 8, 8, [61], 5, 0),        # G = 1
+    (934, 8, 1, [77], 4, 0),        # one KV head, G = 8 (a 32-unit row)
+    (935, 16, 4, [50], 6, 37),      # spare capacity: workgroups with no rows
+    (936, 32, 8, [100], 16, 8040),  # 1,018 copy workgroups + 6 local partials: the most the merge takes
+    (937, 32, 8, [100], 16, 8080),  # past it: the copy alone, then a launch over the rows
+])
+def test_gather_attn_one_token_memory_rows_in_the_copy(env, seed, Hq, Hkv, rows, k, cap_extra):
+    """A one-token query: the workgroups that copy the memory rows also form
+    their attention partials (the copy of kOneAttnRows rows per workgroup),
+    unless the partials would exceed what the merge takes."""
+    torch, msa, ctx = env
+    L = 700
+    w = P.peaked_inputs(seed, 1, 1, Hq, Hkv, D, L, rows, k, P.THETA)
+    bank, coff, ids, got_rows, mo, got = _run(torch, msa, ctx, w, k, seed, cap_extra=cap_extra)
+    assert np.array_equal(mo, np.asarray(w["mem_off"], dtype=np.int64))
+    ref_rows, _ = oracle.gather_rows(bank, coff, ids[0])
+    assert np.array_equal(oracle.f64_to_bf16_bits(got_rows[:mo[1]]), ref_rows)
+    ref = P.oracle_out(w)
+    P.assert_attn_close(got, ref, 2e-2, f"gather_attn one token G={Hq // Hkv} rows={rows} cap+{cap_extra}")
+    _, _, _, _, _, got2 = _run(torch, msa, ctx, w, k, seed, cap_extra=cap_extra, fused=False)
+    diff = float(np.max(np.abs(got - got2)))
+    print(f"[gather_attn] max|O - O_two_calls| = {diff:.3e}", flush=True)
+    assert diff <= 1e-2 * max(1.0, float(np.max(np.abs(ref))))
+
+
 def test_gather_attn_fp32_takes_the_two_step_path(env):
     """fp32 (not on the fused path): the gather then the vector-unit attention, bar 1e-3."""
     torch, msa, ctx = env
