@@ -199,6 +199,52 @@ def test_gather_attn_one_token_memory_rows_in_the_copy(env, seed, Hq, Hkv, rows,
     assert diff <= 1e-2 * max(1.0, float(np.max(np.abs(ref))))
 
 
+@pytest.mark.parametrize("cap_cut", [0, 30])
+def test_gather_attn_one_token_invalid_ids_and_capacity(env, cap_cut):
+    """Ids outside [0, n_docs) copy nothing and a capacity below the selected
+    rows keeps the first cap_rows of them, as in msa_gather_device; the
+    one-token call (the copy workgroups attending over their rows) then gives
+    the rows, offsets and output of the two calls on the same arguments."""
+    torch, msa, ctx = env
+    seed, Hq, Hkv, L, rows, k = 940, 32, 8, 600, [90], 8
+    w = P.peaked_inputs(seed, 1, 1, Hq, Hkv, D, L, rows, k, P.THETA)
+    bank, coff, ids = _bank(w, k, seed)
+    n_docs = len(coff) - 1
+    ids = ids.copy()
+    ids[0, 1] = n_docs + 5
+    ids[0, 4] = -1
+    valid = sorted(int(i) for i in ids[0] if 0 <= i < n_docs)
+    want = int(sum(coff[i + 1] - coff[i] for i in valid))
+    cap = want - cap_cut
+    host = torch.empty(bank.shape, dtype=torch.bfloat16, pin_memory=True)
+    host.copy_(W.dev_bf16(bank, "cpu"))
+    coff_d, ids_d = torch.from_numpy(coff).cuda(), torch.from_numpy(ids).cuda()
+    Q, Kl, Vl = W.dev_bf16(w["Q"]), W.dev_bf16(w["Kl"]), W.dev_bf16(w["Vl"])
+    outs = []
+    for fused in (True, False):
+        dst = torch.full((cap, 2, Hkv, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        mo = torch.full((2,), -7, dtype=torch.int64, device="cuda")
+        O = torch.full((1, 1, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            ws = msa.workspace(msa.msa_gather_attn_workspace_size(1, 1, 1, Hq, Hkv, k, cap, cap, L))
+            msa.msa_gather_attn(ctx, host, 2 * Hkv * D * 2, bank.shape[0], coff_d, ids_d, dst, cap, mo, Q, cap, Kl,
+                                Vl, k, w["scale"], O, ws)
+        else:
+            wsg = msa.workspace(msa.msa_gather_device_workspace_size(1, k, cap))
+            msa.msa_gather_device(ctx, host, 2 * Hkv * D * 2, bank.shape[0], coff_d, ids_d, dst, cap, mo, wsg)
+            wsa = msa.workspace(msa.msa_sparse_attn_workspace_size(1, 1, 1, Hq, Hkv, cap, L))
+            msa.msa_sparse_attn(ctx, Q, dst, mo, cap, Kl, Vl, k, w["scale"], O, wsa)
+        torch.cuda.synchronize()
+        outs.append((W.host_bits(dst), mo.cpu().numpy(), W.widen(W.host_bits(O), "bf16")))
+    (rows1, mo1, o1), (rows2, mo2, o2) = outs
+    assert mo1.tolist() == mo2.tolist() == [0, cap]
+    assert np.array_equal(rows1, rows2)
+    ref_rows = np.concatenate([bank[coff[i]:coff[i + 1]] for i in valid])[:cap]
+    assert np.array_equal(rows1, ref_rows)
+    assert np.all(np.isfinite(o1))
+    assert float(np.max(np.abs(o1 - o2))) <= 1e-2 * max(1.0, float(np.max(np.abs(o2))))
+
+
 def test_gather_attn_fp32_takes_the_two_step_path(env):
     """fp32 (not on the fused path): the gather then the vector-unit attention, bar 1e-3."""
     torch, msa, ctx = env
