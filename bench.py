@@ -232,6 +232,11 @@ class Runner:
         self.timing = False
 
     def arm_timers(self, n):
+        """n timed steps: each records the scan of one layer (layer s mod L in
+        step s) and, in the hipMemcpyAsync step, that layer's attention call.
+        Events around every layer's scan added about 6 us per layer to the
+        step (the gaps they leave before and after the dispatch), so one
+        sampled launch per step measures the kernel without slowing the step."""
         ev = lambda: self.torch.cuda.Event(enable_timing=True)
         self.timers = [(ev(), ev()) for _ in range(n)]
         self.attn_timers = [(ev(), ev()) for _ in range(n)]
@@ -239,12 +244,18 @@ class Runner:
             a.record()
             b.record()
         self.t_i = 0
+        self.step_i = 0
+
+    def timed_layer(self, l):
+        """Whether layer l's scan is the one this timed step records."""
+        return self.timing and l == self.step_i % self.wl["L"]
 
     def step(self):
         torch, msa, wl, k = self.torch, self.msa, self.wl, self.k
         main = torch.cuda.current_stream()
         for l in range(wl["L"]):
-            if self.timing:
+            timed = self.timed_layer(l)
+            if timed:
                 msa.msa_route_time_next(self.ctx, *self.timers[self.t_i])
             # the top-k ids land directly in pinned host memory
             msa.msa_route(self.ctx, wl["Qr"][l], wl["Krbar"][l], self.coff_dev, k, self.ids_host[l],
@@ -254,23 +265,25 @@ class Runner:
             msa.msa_gather(wl["host_layer"][l % wl["HL"]], ROW_KV, wl["N"], self.coff_np, self.ids_np[l], k, self.KVmem[l],
                            self.cap, self.mo_host[l], self.mo_dev[l], side=self.side)
             main.wait_stream(self.side)
-            if self.timing:
+            if timed:
                 self.attn_timers[self.t_i][0].record(main)
             msa.msa_sparse_attn(self.ctx, wl["Q"][l], self.KVmem[l], self.mo_dev[l], self.cap, wl["Kl"][l],
                                 wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
-            if self.timing:
+            if timed:
                 self.attn_timers[self.t_i][1].record(main)
                 self.t_i += 1
+        if self.timing:
+            self.step_i += 1
 
     def step_device_gather(self):
         """The step as two calls, msa_gather_device then msa_sparse_attn: ids
         stay on the GPU and a kernel reads the selected rows from the pinned
         host store, so the 18 layers are enqueued without any host
-        synchronisation.  When timing, the scan kernel's own dispatch records
-        its events (no extra packets)."""
+        synchronisation.  When timing, the sampled scan's own dispatch
+        records its events (no extra packets)."""
         msa, wl, k = self.msa, self.wl, self.k
         for l in range(wl["L"]):
-            if self.timing:
+            if self.timed_layer(l):
                 msa.msa_route_time_next(self.ctx, *self.timers[self.t_i])
                 self.t_i += 1
             msa.msa_route(self.ctx, wl["Qr"][l], wl["Krbar"][l], self.coff_dev, k, self.ids_dev[l],
@@ -279,6 +292,8 @@ class Runner:
                                   self.ids_dev[l], self.KVmem[l], self.cap, self.mo_dev[l], self.ws_gather)
             msa.msa_sparse_attn(self.ctx, wl["Q"][l], self.KVmem[l], self.mo_dev[l], self.cap, wl["Kl"][l],
                                 wl["Vl"][l], k, self.scale, self.O[l], self.ws_attn)
+        if self.timing:
+            self.step_i += 1
 
     def step_gather_attn(self):
         """The step: the device gather and the attention in one call
@@ -287,7 +302,7 @@ class Runner:
         rows they copy, then the merge."""
         msa, wl, k = self.msa, self.wl, self.k
         for l in range(wl["L"]):
-            if self.timing:
+            if self.timed_layer(l):
                 msa.msa_route_time_next(self.ctx, *self.timers[self.t_i])
                 self.t_i += 1
             msa.msa_route(self.ctx, wl["Qr"][l], wl["Krbar"][l], self.coff_dev, k, self.ids_dev[l],
@@ -295,6 +310,8 @@ class Runner:
             msa.msa_gather_attn(self.ctx, wl["host_layer"][l % wl["HL"]], ROW_KV, wl["N"], self.coff_dev,
                                 self.ids_dev[l], self.KVmem[l], self.cap, self.mo_dev[l], wl["Q"][l], self.cap,
                                 wl["Kl"][l], wl["Vl"][l], k, self.scale, self.O[l], self.ws_ga)
+        if self.timing:
+            self.step_i += 1
 
 
 def read_probe_gbps(torch, device_fill, buf, reps=5):
@@ -1019,7 +1036,7 @@ def main():
     def timed(step_fn):
         for _ in range(args.warmup):
             step_fn()
-        run.arm_timers(args.steps * L)
+        run.arm_timers(args.steps)
         torch.cuda.synchronize()             # the timers' first records stay outside the timed steps
         run.timing = True
         t0 = time.perf_counter()
