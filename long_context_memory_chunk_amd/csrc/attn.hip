@@ -241,17 +241,28 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 // several loads in flight.
 constexpr int kMaxParts = 1024;
 
+// With mem_off (the one-token gather + attention launch, one query), only the
+// partials that hold rows are read: the P_loc local ones, then one per
+// rows_per memory rows actually gathered (mem_off[1]); the copy workgroups
+// past the gathered rows write none.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                         const float2* __restrict__ part_ml, int P,
-                                                         T* __restrict__ O, float* __restrict__ lse) {
+                                                         const float2* __restrict__ part_ml, int P_stride,
+                                                         T* __restrict__ O, float* __restrict__ lse,
+                                                         const int64_t* __restrict__ mem_off = nullptr,
+                                                         int P_loc = 0, int rows_per = 1) {
     __shared__ float s_w[kMaxParts];
     __shared__ float s_red[2][D / 64];
+    int P = P_stride;
+    if (mem_off != nullptr) {
+        const int64_t used = P_loc + (mem_off[1] + rows_per - 1) / rows_per;
+        P = int(used < P_stride ? used : P_stride);
+    }
     const int64_t row = blockIdx.x;   // (b, i, h)
     const int dd = threadIdx.x;
     const int lane = dd % kWave, wave = dd / kWave;
     float m = -INFINITY;
-    for (int p = dd; p < P; p += D) m = fmaxf(m, part_ml[row * P + p].x);
+    for (int p = dd; p < P; p += D) m = fmaxf(m, part_ml[row * P_stride + p].x);
     m = wave_max(m);
     if (lane == 0) s_red[0][wave] = m;
     __syncthreads();
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     for (int w = 1; w < D / 64; ++w) m = fmaxf(m, s_red[0][w]);
     float l = 0.f;
     for (int p = dd; p < P; p += D) {
-        const float2 ml = part_ml[row * P + p];
+        const float2 ml = part_ml[row * P_stride + p];
         const float w = (ml.x == -INFINITY) ? 0.f : expf(ml.x - m);
         s_w[p] = w;
         l += w * ml.y;
@@ -274,14 +285,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     float acc = 0.f;
     int p = 0;
     for (; p + 4 <= P; p += 4) {
-        const float o0 = part_o[(row * P + p) * D + dd], o1 = part_o[(row * P + p + 1) * D + dd];
-        const float o2 = part_o[(row * P + p + 2) * D + dd], o3 = part_o[(row * P + p + 3) * D + dd];
+        const float o0 = part_o[(row * P_stride + p) * D + dd], o1 = part_o[(row * P_stride + p + 1) * D + dd];
+        const float o2 = part_o[(row * P_stride + p + 2) * D + dd], o3 = part_o[(row * P_stride + p + 3) * D + dd];
         acc += s_w[p] * o0;
         acc += s_w[p + 1] * o1;
         acc += s_w[p + 2] * o2;
         acc += s_w[p + 3] * o3;
     }
-    for (; p < P; ++p) acc += s_w[p] * part_o[(row * P + p) * D + dd];
+    for (; p < P; ++p) acc += s_w[p] * part_o[(row * P_stride + p) * D + dd];
     Elem<T>::store(O, row * D + dd, acc / l);
     if (lse != nullptr && dd == 0) lse[row] = m + logf(l);
 }
@@ -462,8 +473,13 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
         err = launch_decode_mfma_mem(a, part_o, part_ml, g.mem.P, g.mem.nc, g.loc.P, g.P_total, st);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
-                       part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse);
+    if (g.mem_in_copy)
+        hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
+                           part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse,
+                           static_cast<const int64_t*>(ga.mem_off), g.loc.P, kOneAttnRows);
+    else
+        hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
+                           part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse, nullptr, 0, 1);
     return hipGetLastError();
 }
 

@@ -506,13 +506,17 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
 // each row's score and sums the 16 shares of the group (fp32 throughout),
 // and the group's lane 0 hands the probabilities to the V̄ threads through
 // LDS; thread 16 hkv + 16 g + c then accumulates dimensions 8c .. 8c+7 of
-// the G heads' outputs.  A workgroup with no rows writes an empty partial.
+// the G heads' outputs.  A workgroup past the gathered rows writes nothing:
+// the combine reads the partials of the first ceil(mem_off[1] / R) only.
 template <int G>
 __device__ __forceinline__ void gather_one_attn_wg(const GatherCopyArgs& gc, const DecodeArgs& da, int wg, int pp) {
     constexpr int R = kOneAttnRows;
     __shared__ float s_p[8][G][R];
     int64_t sr[R];
     gather_one_plan<R>(gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off, wg, sr);
+    // past the gathered rows (the same answer in every wave): nothing to copy,
+    // and the combine reads no partial of this workgroup
+    if (sr[0] < 0) return;
     const int t = threadIdx.x;
     const int64_t rv = gc.row_vecs;
     const bool on = t < rv;
