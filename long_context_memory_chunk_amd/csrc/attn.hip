@@ -396,26 +396,35 @@ namespace {
 
 struct GatherAttnPlan {
     bool fused, one;
-    bool mem_in_copy;        // the one-query copy forms the memory rows' partials
+    int attn_rows;           // > 0: the one-query copy forms the memory rows' partials, this many rows each
     int n_copy;              // copy workgroups
     DecodePlan loc, mem;     // mem.P == 0: no launch over the memory rows
     int P_total;
 };
 
 GatherAttnPlan gather_attn_plan(const AttnArgs& a, int64_t cap_rows) {
-    GatherAttnPlan g{false, false, false, kCopyWgs, {0, 0}, {0, 0}, 0};
+    GatherAttnPlan g{false, false, 0, kCopyWgs, {0, 0}, {0, 0}, 0};
     if (!decode_applicable(a.dt, a.D, a.Hq, a.Hkv, a.max_rows, a.L) || attn_mfma_applicable(a)) return g;
     g.loc = decode_plan(a.B, a.Tq, a.Hkv, 0, a.L, a.num_cus);
     g.one = a.B == 1 && cap_rows <= kOneMaxRows;
     if (g.one) {
         // a one-token query with at most 8 KV heads (a row of at most 256
-        // 16-byte units): the copy workgroups attend over their own rows
-        const int64_t w = ceil_div(cap_rows, int64_t(kOneAttnRows));
-        g.mem_in_copy = a.Tq == 1 && a.Hkv <= 8 && a.max_rows > 0 && g.loc.P + w <= kMaxParts;
-        const int64_t n = g.mem_in_copy ? w : ceil_div(cap_rows, int64_t(kOneRows));
+        // 16-byte units): the copy workgroups attend over their own rows, 4
+        // each while their partials fit the combine, else 8
+        int64_t n = ceil_div(cap_rows, int64_t(kOneRows));
+        if (a.Tq == 1 && a.Hkv <= 8 && a.max_rows > 0) {
+            for (const int R : {kOneAttnRowsFew, kOneAttnRowsMany}) {
+                const int64_t w = ceil_div(cap_rows, int64_t(R));
+                if (g.loc.P + (w > 0 ? w : 1) <= kMaxParts) {
+                    g.attn_rows = R;
+                    n = w;
+                    break;
+                }
+            }
+        }
         g.n_copy = int(n > 0 ? n : 1);
     }
-    if (g.mem_in_copy) {
+    if (g.attn_rows > 0) {
         g.P_total = g.loc.P + g.n_copy;
     } else {
         if (a.max_rows > 0) g.mem = decode_plan(a.B, a.Tq, a.Hkv, a.max_rows, 0, a.num_cus);
@@ -466,17 +475,17 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
     const size_t rows = size_t(a.B) * a.Tq * a.Hq * g.P_total;
     float* part_o = static_cast<float*>(a.ws);
     float2* part_ml = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align256(rows * a.D * sizeof(float)));
-    err = launch_gather_local_attn(gc, g.one, g.mem_in_copy, g.n_copy, a, part_o, part_ml, g.loc.P, g.loc.nc,
+    err = launch_gather_local_attn(gc, g.one, g.attn_rows, g.n_copy, a, part_o, part_ml, g.loc.P, g.loc.nc,
                                    g.P_total, st);
     if (err != hipSuccess) return err;
     if (g.mem.P > 0) {
         err = launch_decode_mfma_mem(a, part_o, part_ml, g.mem.P, g.mem.nc, g.loc.P, g.P_total, st);
         if (err != hipSuccess) return err;
     }
-    if (g.mem_in_copy)
+    if (g.attn_rows > 0)
         hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
                            part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse,
-                           static_cast<const int64_t*>(ga.mem_off), g.loc.P, kOneAttnRows);
+                           static_cast<const int64_t*>(ga.mem_off), g.loc.P, g.attn_rows);
     else
         hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
                            part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse, nullptr, 0, 1);

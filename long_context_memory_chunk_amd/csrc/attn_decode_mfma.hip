@@ -508,9 +508,8 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
 // LDS; thread 16 hkv + 16 g + c then accumulates dimensions 8c .. 8c+7 of
 // the G heads' outputs.  A workgroup past the gathered rows writes nothing:
 // the combine reads the partials of the first ceil(mem_off[1] / R) only.
-template <int G>
+template <int G, int R>
 __device__ __forceinline__ void gather_one_attn_wg(const GatherCopyArgs& gc, const DecodeArgs& da, int wg, int pp) {
-    constexpr int R = kOneAttnRows;
     __shared__ float s_p[8][G][R];
     int64_t sr[R];
     gather_one_plan<R>(gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off, wg, sr);
@@ -617,18 +616,20 @@ __device__ __forceinline__ void gather_one_attn_wg(const GatherCopyArgs& gc, con
 // fastest).  The bounded copy goes first, since it is the longer; the
 // one-query copy (one workgroup per kOneRows rows) after the attention, so
 // that a large capacity cannot hold every slot before the attention starts.
-// With mem_in_copy (a one-token query) the one-query copy takes kOneAttnRows
-// rows per workgroup and also forms their partials (indices P + wg), so the
-// launch covers every key of the row.
+// With attn_rows (a one-token query: 4 or 8; 0 for the copy alone) the
+// one-query copy takes attn_rows rows per workgroup and also forms their
+// partials (indices P + wg), so the launch covers every key of the row.
 template <int G, bool kOne>
 __global__ __launch_bounds__(256, G < 8 ? 2 : 1) void gather_local_attn_kernel(GatherCopyArgs gc, DecodeArgs da,
                                                                               int P, int copy_first, int n_copy,
-                                                                              int mem_in_copy) {
+                                                                              int attn_rows) {
     const int bx = int(blockIdx.x);
     if (bx >= copy_first && bx < copy_first + n_copy) {
         const int wg = bx - copy_first;
-        if (kOne && mem_in_copy)
-            gather_one_attn_wg<G>(gc, da, wg, P + wg);
+        if (kOne && attn_rows == kOneAttnRowsFew)
+            gather_one_attn_wg<G, kOneAttnRowsFew>(gc, da, wg, P + wg);
+        else if (kOne && attn_rows == kOneAttnRowsMany)
+            gather_one_attn_wg<G, kOneAttnRowsMany>(gc, da, wg, P + wg);
         else if (kOne)
             gather_one_wg(gc.host, gc.row_vecs, gc.ids, gc.K, gc.off, gc.n_docs, gc.n_rows_host, gc.cap, gc.mem_off,
                           gc.dst, wg);
@@ -692,7 +693,7 @@ hipError_t launch_decode_mfma_mem(const AttnArgs& a, float* part_o, float2* part
     return launch_range(a, decode_args(a, kKeysMem, part_o, part_ml, nc, p_base, P_total), P, st);
 }
 
-hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, bool mem_in_copy, int n_copy,
+hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int attn_rows, int n_copy,
                                     const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, int P_total,
                                     hipStream_t st) {
     const DecodeArgs da = decode_args(a, kKeysLocal, part_o, part_ml, nc, 0, P_total);
@@ -703,7 +704,7 @@ hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, bool mem
     do {                                                                                                         \
         if (one)                                                                                                 \
             hipLaunchKernelGGL((gather_local_attn_kernel<GG, true>), dim3(grid), dim3(256), 0, st, gc, da, P,   \
-                               copy_first, n_copy, int(mem_in_copy));                                           \
+                               copy_first, n_copy, attn_rows);                                                 \
         else                                                                                                     \
             hipLaunchKernelGGL((gather_local_attn_kernel<GG, false>), dim3(grid), dim3(256), 0, st, gc, da, P,  \
                                copy_first, n_copy, 0);                                                          \

@@ -22,11 +22,11 @@ hipError_t launch_decode_mfma_mem(const AttnArgs& a, float* part_o, float2* part
 // One launch: the device gather's copy (n_copy workgroups; the one-query copy
 // if `one`) beside the attention over the local keys only, whose P partitions
 // are written as partials 0 .. P - 1 of P_total per row.  a.KVmem and
-// a.mem_off are not read.  With mem_in_copy (one-query copy of a one-token
-// query, hkv <= 8), copy workgroup w takes kOneAttnRows rows and writes their
-// partial as index P + w, so n_copy = P_total - P (workgroups past the
+// a.mem_off are not read.  With attn_rows (4 or 8: one-query copy of a
+// one-token query, hkv <= 8), copy workgroup w takes attn_rows rows and writes
+// their partial as index P + w, so n_copy = P_total - P (workgroups past the
 // gathered rows write none; the combine is told to read only those that do).
-hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, bool mem_in_copy, int n_copy,
+hipError_t launch_gather_local_attn(const GatherCopyArgs& gc, bool one, int attn_rows, int n_copy,
                                     const AttnArgs& a, float* part_o, float2* part_ml, int P, int nc, int P_total,
                                     hipStream_t st);
 

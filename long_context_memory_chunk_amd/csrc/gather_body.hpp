@@ -22,8 +22,10 @@ constexpr int kCopyRows = 8;
 constexpr int kOneRows = 2;
 constexpr int64_t kOneMaxRows = 8192;   // larger capacities take the plan + bounded copy path
 // One-query copy that also attends over the rows it copies (a one-token
-// query, KV heads <= 8): destination rows per workgroup.
-constexpr int kOneAttnRows = 8;
+// query, KV heads <= 8): destination rows per workgroup, 4 while the
+// partials (one per workgroup) fit the combine, else 8.
+constexpr int kOneAttnRowsFew = 4;
+constexpr int kOneAttnRowsMany = 8;
 
 // Lane `src` of a 64-bit value, for a wave-uniform lane index (two scalar
 // reads instead of two LDS permutes).

@@ -177,13 +177,15 @@ def test_gather_attn_random_shapes(env, seed, B, Tq, Hq, Hkv, L, rows, k):
     (933, 8, 8, [61], 5, 0),        # G = 1
     (934, 8, 1, [77], 4, 0),        # one KV head, G = 8 (a 32-unit row)
     (935, 16, 4, [50], 6, 37),      # spare capacity: workgroups with no rows
-    (936, 32, 8, [100], 16, 8040),  # 1,018 copy workgroups + 6 local partials: the most the merge takes
+    (938, 32, 8, [100], 16, 3972),  # 4 rows per copy workgroup: 1,018 + 6 local partials, the most that fit
+    (939, 32, 8, [100], 16, 3976),  # past it: 8 rows per copy workgroup (510 + 6 partials)
+    (936, 32, 8, [100], 16, 8040),  # 8 rows per workgroup: 1,018 copy workgroups + 6 local partials
     (937, 32, 8, [100], 16, 8080),  # past it: the copy alone, then a launch over the rows
 ])
 def test_gather_attn_one_token_memory_rows_in_the_copy(env, seed, Hq, Hkv, rows, k, cap_extra):
     """A one-token query: the workgroups that copy the memory rows also form
-    their attention partials (the copy of kOneAttnRows rows per workgroup),
-    unless the partials would exceed what the merge takes."""
+    their attention partials (4 rows per workgroup, or 8 where 4 would give
+    more partials than the merge takes), unless even 8 would."""
     torch, msa, ctx = env
     L = 700
     w = P.peaked_inputs(seed, 1, 1, Hq, Hkv, D, L, rows, k, P.THETA)
