@@ -241,23 +241,32 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 // several loads in flight.
 constexpr int kMaxParts = 1024;
 
-// With mem_off (the one-token gather + attention launch, one query), only the
-// partials that hold rows are read: the P_loc local ones, then one per
-// rows_per memory rows actually gathered (mem_off[1]); the copy workgroups
-// past the gathered rows write none.
+// Which of a row's P_stride partials the combine reads: all of them (mode
+// 0), or, for the one-token gather + attention launch (mode 1, one query),
+// the P_loc local partials and then one per rows_per memory rows actually
+// gathered (mem_off[1]): the copy workgroups past the gathered rows write
+// none.  (Trimming the empty partitions of the decode launch the same way,
+// from mem_off, was slower: the combine then waits for mem_off before its
+// first partial load.)
+struct CombineTrim {
+    int mode;
+    const int64_t* mem_off;
+    int P_loc, rows_per;
+};
+
+__device__ __forceinline__ int trim_parts(const CombineTrim& tr, int P_stride) {
+    const int64_t used = tr.P_loc + (tr.mem_off[1] + tr.rows_per - 1) / tr.rows_per;
+    return int(used < 1 ? 1 : (used < P_stride ? used : P_stride));
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml, int P_stride,
                                                          T* __restrict__ O, float* __restrict__ lse,
-                                                         const int64_t* __restrict__ mem_off = nullptr,
-                                                         int P_loc = 0, int rows_per = 1) {
+                                                         CombineTrim tr) {
     __shared__ float s_w[kMaxParts];
     __shared__ float s_red[2][D / 64];
-    int P = P_stride;
-    if (mem_off != nullptr) {
-        const int64_t used = P_loc + (mem_off[1] + rows_per - 1) / rows_per;
-        P = int(used < P_stride ? used : P_stride);
-    }
+    const int P = tr.mode == 0 ? P_stride : trim_parts(tr, P_stride);
     const int64_t row = blockIdx.x;   // (b, i, h)
     const int dd = threadIdx.x;
     const int lane = dd % kWave, wave = dd / kWave;
@@ -342,7 +351,7 @@ hipError_t launch_split_g(const AttnArgs& a, float* part_o, float2* part_ml, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((attn_combine_kernel<T, D>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(D), 0, st,
-                       part_o, part_ml, P, static_cast<T*>(a.O), a.lse);
+                       part_o, part_ml, P, static_cast<T*>(a.O), a.lse, CombineTrim{});
     return hipGetLastError();
 }
 
@@ -350,7 +359,7 @@ hipError_t launch_decode(const AttnArgs& a, float* part_o, float2* part_ml, Deco
     hipError_t err = launch_decode_mfma(a, part_o, part_ml, pl.P, pl.nc, st);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
-                       part_o, part_ml, pl.P, static_cast<bf16_t*>(a.O), a.lse);
+                       part_o, part_ml, pl.P, static_cast<bf16_t*>(a.O), a.lse, CombineTrim{});
     return hipGetLastError();
 }
 
@@ -482,13 +491,10 @@ hipError_t launch_gather_attn(const GatherAttnArgs& ga, hipStream_t st) {
         err = launch_decode_mfma_mem(a, part_o, part_ml, g.mem.P, g.mem.nc, g.loc.P, g.P_total, st);
         if (err != hipSuccess) return err;
     }
-    if (g.attn_rows > 0)
-        hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
-                           part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse,
-                           static_cast<const int64_t*>(ga.mem_off), g.loc.P, g.attn_rows);
-    else
-        hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
-                           part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse, nullptr, 0, 1);
+    const CombineTrim tr = g.attn_rows > 0 ? CombineTrim{1, ga.mem_off, g.loc.P, g.attn_rows}
+                                           : CombineTrim{0, nullptr, 0, 1};
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, 128>), dim3(unsigned(a.B * a.Tq * a.Hq)), dim3(128), 0, st,
+                       part_o, part_ml, g.P_total, static_cast<bf16_t*>(a.O), a.lse, tr);
     return hipGetLastError();
 }
 
