@@ -125,6 +125,20 @@ def test_decode_100m_layer_full_oracle_topk(env):
                              W.widen(Vlh, "bf16"), k, 1 / math.sqrt(D), 1e6)
     P.assert_attn_close(W.widen(W.host_bits(O), "bf16"), ref, 2e-2, "100M layer decode")
 
+    # the same layer through msa_gather_attn, as the routed decode step runs it
+    # (a 2,048-row capacity: most copy workgroups past the gathered rows)
+    dst2 = torch.full((cap, 2, Hkv, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mo2 = torch.full((2,), -7, dtype=torch.int64, device="cuda")
+    O2 = torch.full((1, 1, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ids_dev = torch.from_numpy(got.astype(np.int32)).cuda()
+    wsga = msa.workspace(msa.msa_gather_attn_workspace_size(1, 1, 1, Hq, Hkv, k, cap, cap, L))
+    msa.msa_gather_attn(ctx, host, 2 * Hkv * D * 2, N, torch.from_numpy(coff).cuda(), ids_dev, dst2, cap, mo2,
+                        W.dev_bf16(Qh), cap, W.dev_bf16(Klh), W.dev_bf16(Vlh), k, 1 / math.sqrt(D), O2, wsga)
+    torch.cuda.synchronize()
+    assert mo2.cpu().tolist() == [0, len(rows)]
+    assert np.array_equal(W.host_bits(dst2[:len(rows)]), rows)
+    P.assert_attn_close(W.widen(W.host_bits(O2), "bf16"), ref, 2e-2, "100M layer decode, one call")
+
 
 @pytest.mark.timeout(900)
 def test_chunk_level_topk_100m_layer(env):
