@@ -7,8 +7,8 @@
 // 方法 › 稀疏注意力机制 (top-k documents by cosine).  github-eval-reports
 // review, 核心模块 (head mean first, then token max).
 //
-// Order of the call: route_prep (U, the unit-query group sums), then the
-// chunk scores c[B][N] from one of three scans -- the VALU streaming scan or
+// Order of the call: route_prep (U, the unit-query group sums; skipped where
+// the scan forms U itself), then the chunk scores c[B][N] from one of three scans -- the VALU streaming scan or
 // the generic one (route_scan.hip), or the matrix-core path (route_mfma.hip)
 // -- then the two top-k kernels below.
 //
@@ -413,9 +413,12 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     uint64_t* wmax = reinterpret_cast<uint64_t*>(ws + w.wmax_off);
     hipError_t err;
 
-    // 1. unit-query group sums (the matrix-core path of decode batches and
-    // short queries forms them itself, in its bf16 operand layout)
-    if (!(a.N > 0 && !route_scan_fast_applicable(a) && route_mfma_preps_itself(a)))
+    // 1. unit-query group sums (the streaming scan with an aligned query, and
+    // the matrix-core path of decode batches and short queries, form them
+    // themselves; the latter in its bf16 operand layout)
+    const bool preps_itself = a.N > 0 && (route_scan_fast_applicable(a) ? route_scan_fast_preps_itself(a)
+                                                                         : route_mfma_preps_itself(a));
+    if (!preps_itself)
         if ((err = launch_route_prep(a, U, st)) != hipSuccess) return err;
 
     // 2. chunk scores c[B][N]; the chunk-score kernel's dispatch records the

@@ -20,7 +20,11 @@
 //                         coalesced loads (a 1 KiB wave load per 4 heads), dot
 //                         and norm partials per lane, DPP reduction over the
 //                         16 lanes of a head, cross-group sum by readlane.
-//                         HBM-bound (1 flop per byte at B*Tq = 1).
+//                         HBM-bound (1 flop per byte at B*Tq = 1).  With a
+//                         16-byte aligned Qr every wave forms the U slice it
+//                         needs from Qr itself (unit_group_slice, the same
+//                         operations in the same order as route_prep_bf16_d128,
+//                         so U is bit-identical) and no prep launch precedes it.
 //   route_scan_generic    any dtype/shape: one thread per (query, chunk).
 #include "common.hpp"
 #include "launch.hpp"
@@ -105,12 +109,49 @@ __global__ __launch_bounds__(256) void route_prep_bf16_d128(const u32x4* __restr
 
 // ---------------------------------------------------------------- decode scan
 
+// Elements e0 .. e0+7 of U[q][g] for bf16 rows of 128, formed by one lane from
+// Qr with the operations of route_prep_bf16_d128 in its order: the 16 lanes
+// that share g each read their 16-byte slot of head h, the head's squared norm
+// is summed over those lanes, and the unit values of heads g*G + 4t + s
+// (t = 0, 1, ..) gather in a[s] before (a0 + a1) + (a2 + a3), which is the
+// order of that kernel's two cross-slot shuffles.  Every lane of a 16-lane
+// group must call it with the same q and g (the norm sum crosses them).
+__device__ __forceinline__ void unit_group_slice(const u32x4* __restrict__ Qr, int64_t q, int g, int Hq,
+                                                 int G, int c, float out[8]) {
+    float a[4][8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[s][e] = 0.f;
+    for (int h0 = g * G; h0 < (g + 1) * G; h0 += 4) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int h = h0 + s;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (h < (g + 1) * G) w = Qr[(q * Hq + h) * 16 + c];
+            float x[8];
+            x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+            x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+            float n2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) n2 += x[e] * x[e];
+            n2 = group_sum<16>(n2);
+            const float inv = 1.f / fmaxf(sqrtf(n2), kEps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[s][e] += x[e] * inv;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (a[0][e] + a[1][e]) + (a[2][e] + a[3][e]);
+}
+
 // Row n of K̄r is hkv*128 bf16 = LPR KiB; wave load j of a row covers heads
 // 4j .. 4j+3, 16 lanes per head, 8 elements per lane.
-template <int LPR, int NQ>
+// Fused: U is formed from Qr (16-byte aligned rows of Hq heads) instead of read.
+template <int LPR, int NQ, bool Fused>
 __global__ __launch_bounds__(256) void route_scan_bf16_d128(
-    const u32x4* __restrict__ Kr, int64_t N, const float* __restrict__ U, int B, int Tq,
-    float inv_hq, float* __restrict__ cout) {
+    const u32x4* __restrict__ Kr, int64_t N, const float* __restrict__ U, const u32x4* __restrict__ Qr, int Hq,
+    int B, int Tq, float inv_hq, float* __restrict__ cout) {
     // rows in flight per wave: 8 (16 KiB) when registers allow, else 4
     constexpr int UNROLL = (LPR * NQ <= 2) ? 8 : 4;
     const int lane = threadIdx.x % kWave;
@@ -124,9 +165,14 @@ __global__ __launch_bounds__(256) void route_scan_bf16_d128(
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int j = 0; j < LPR; ++j)
+        for (int j = 0; j < LPR; ++j) {
+            if constexpr (Fused) {
+                unit_group_slice(Qr, q, j * 4 + sub, Hq, Hq / HKV, lane % 16, u[q][j]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) u[q][j][e] = U[(int64_t(q) * HKV + j * 4 + sub) * 128 + e0 + e];
+                for (int e = 0; e < 8; ++e) u[q][j][e] = U[(int64_t(q) * HKV + j * 4 + sub) * 128 + e0 + e];
+            }
+        }
 
     const int64_t n_groups = (N + 63) / 64;
     for (int64_t grp = wave_id; grp < n_groups; grp += n_waves) {
@@ -238,15 +284,22 @@ hipError_t launch_scan_generic(const RouteArgs& a, const float* U, float* c, hip
                         1.f / float(a.Hq), c);
 }
 
+bool qr_aligned16(const RouteArgs& a) { return (reinterpret_cast<uintptr_t>(a.Qr) & 15u) == 0; }
+
 template <int LPR, int NQ>
 hipError_t launch_scan_fast(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
     const int64_t groups = ceil_div(a.N, 64);
     int64_t blocks = ceil_div(groups, 4);
     const int64_t cap = int64_t(a.num_cus) * 4;   // 16 waves per CU, grid-strided over 64-row groups
     if (blocks > cap) blocks = cap;
-    return launch_timed(route_scan_bf16_d128<LPR, NQ>, dim3(unsigned(blocks)), dim3(256), st, a.prof_start,
-                        a.prof_stop, static_cast<const u32x4*>(a.Krbar), a.N, U, int(a.B), a.Tq,
-                        1.f / float(a.Hq), c);
+    const u32x4* qr = static_cast<const u32x4*>(a.Qr);
+    if (qr_aligned16(a))
+        return launch_timed(route_scan_bf16_d128<LPR, NQ, true>, dim3(unsigned(blocks)), dim3(256), st,
+                            a.prof_start, a.prof_stop, static_cast<const u32x4*>(a.Krbar), a.N, U, qr, a.Hq,
+                            int(a.B), a.Tq, 1.f / float(a.Hq), c);
+    return launch_timed(route_scan_bf16_d128<LPR, NQ, false>, dim3(unsigned(blocks)), dim3(256), st,
+                        a.prof_start, a.prof_stop, static_cast<const u32x4*>(a.Krbar), a.N, U, qr, a.Hq,
+                        int(a.B), a.Tq, 1.f / float(a.Hq), c);
 }
 
 template <int LPR>
@@ -297,6 +350,8 @@ bool route_scan_fast_applicable(const RouteArgs& a) {
     return a.dt == MSA_BF16 && a.D == 128 && a.B * a.Tq <= 4 &&
            (a.Hkv == 4 || a.Hkv == 8 || a.Hkv == 16);
 }
+
+bool route_scan_fast_preps_itself(const RouteArgs& a) { return route_scan_fast_applicable(a) && qr_aligned16(a); }
 
 hipError_t launch_route_scan_fast(const RouteArgs& a, const float* U, float* c, hipStream_t st) {
     if (a.Hkv == 4) return dispatch_nq<1>(a, U, c, st);

@@ -215,6 +215,9 @@ ROUTE_CASES = [
     ("bf16", 128, 16, 4, 3, 1, 150, 5, 5),       # decode scan, 4 KV heads
     ("bf16", 128, 16, 16, 1, 1, 64, 3, 64),      # decode scan, 16 KV heads, k = 64
     ("bf16", 128, 32, 8, 1, 3, 100, 4, 7),       # 3 tokens of one query
+    ("bf16", 128, 16, 8, 1, 1, 120, 6, 8),       # decode scan, G = 2 (half the head slots empty)
+    ("bf16", 128, 24, 8, 2, 1, 110, 5, 6),       # decode scan, G = 3
+    ("bf16", 128, 64, 8, 1, 2, 130, 7, 9),       # decode scan, G = 8 (two passes over the head slots)
     ("f32", 64, 4, 2, 1, 32, 64, 16, 4),         # tiny fp32 shape, generic scan
     ("bf16", 64, 8, 2, 2, 5, 90, 6, 10),         # generic scan
     ("bf16", 128, 32, 8, 3, 3, 120, 7, 9),       # 9 queries
